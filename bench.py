@@ -1,0 +1,289 @@
+"""Benchmark of varlen GQA attention on one MI355X: forward and forward+backward.
+
+One step = one pass of the whole path over one batch: attn_varlen_fwd (with the
+LSE) followed by attn_varlen_bwd (Delta preprocess, dK/dV, dQ), inputs resident
+in HBM. Timing follows the pages' benchmark method ("FA2 vs NATTEN on A100"
+issue, benchmark script: warm-up iterations, then timed iterations with
+device events; the LSE repro warms the GPU with 1 s of bf16 GEMMs first).
+
+Work accounting (same as the pages: forward 4 * n^2 * heads * head_dim per
+sequence, forward+backward 3.5x that; causal counts half):
+    fwd_flop = 4 * sum_b Lq_b * Lk_b * Hq * D * (1/2 if causal)
+
+Prints one JSON line. Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "varlen GQA attn TFLOP/s fwd & fwd+bwd, bf16 hd128 @16K; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def warm_gpu(seconds: float = 1.0):
+    import torch
+
+    x = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        torch.mm(x, x)
+    torch.cuda.synchronize()
+
+
+def kernel_flop(name: str, wl) -> float:
+    """Algorithmic flop of one launch of the named kernel (MFMA work it must do)."""
+    pairs = sum(a * b for a, b in zip(wl.seqlens_q, wl.seqlens_k)) * (0.5 if wl.causal else 1.0)
+    per_pair = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6}.get(name)
+    if per_pair is None:
+        return 0.0
+    return per_pair * pairs * wl.n_q_heads * wl.head_dim
+
+
+def kernel_bytes(name: str, wl) -> float:
+    """Algorithmic HBM bytes of one launch (each tensor read or written once)."""
+    tq, tk, hq, hkv, d = wl.total_q, wl.total_k, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    q = 2 * tq * hq * d
+    kv = 2 * tk * hkv * d
+    rows = 4 * tq * hq
+    return {
+        "attn_fwd": q + 2 * kv + q + rows,
+        "attn_bwd_delta": 2 * q + rows,
+        "attn_bwd_dkdv": 2 * q + 2 * kv + 2 * rows + 2 * kv,
+        "attn_bwd_dq": 2 * q + 2 * kv + 2 * rows + q,
+    }.get(name, 0.0)
+
+
+def time_steps(fn, steps: int, warmup: int):
+    """Run warmup untimed, then `steps` timed calls; returns (ms per step, per-step event ms list)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / max(1, steps)
+    per = [s.elapsed_time(e) for s, e in evs]
+    return wall, per
+
+
+def run_workload(wl, steps, warmup, profile=True):
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    inp = W.make_inputs(wl)
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    mq, mk = wl.max_seqlen_q, wl.max_seqlen_k
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+    dq = torch.empty_like(d["q"])
+    dk = torch.empty_like(d["k"])
+    dv = torch.empty_like(d["v"])
+    ws = torch.empty(max(16, A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k,
+                                                              wl.n_q_heads, wl.n_kv_heads, wl.head_dim)),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def fwd():
+        A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk, wl.softmax_scale,
+                          wl.causal, out=out, lse=lse)
+
+    def step():
+        fwd()
+        A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
+                          wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    res = {}
+    fwd_ms, fwd_per = time_steps(fwd, steps, warmup)
+    if profile:
+        A.attn_varlen_profile_enable(True)
+    step_ms, step_per = time_steps(step, steps, warmup)
+    recs = []
+    if profile:
+        A.attn_varlen_profile_enable(False)
+        recs = A.attn_varlen_profile_records()
+    fwd_flop = wl.accounted_fwd_flop()
+    res["fwd_ms"] = fwd_ms
+    res["fwd_ms_median"] = statistics.median(fwd_per)
+    res["fwd_tflops"] = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    res["step_ms"] = step_ms
+    res["step_ms_median"] = statistics.median(step_per)
+    res["fwdbwd_tflops"] = 3.5 * fwd_flop / (step_ms * 1e-3) / 1e12
+    # per-kernel averages over the timed steps (the warm-up launches are not recorded
+    # because warm-up runs before the session starts... they are: drop the first `warmup`)
+    per_kernel = {}
+    if recs:
+        n_per_step = len(recs) // (steps + warmup)
+        timed = recs[warmup * n_per_step:]
+        for name, ms in timed:
+            per_kernel.setdefault(name, []).append(ms)
+    res["kernels"] = {k: {"avg_ms": sum(v) / len(v), "launches": len(v)} for k, v in per_kernel.items()}
+    return res
+
+
+def cpu_baseline(wl, budget_s: float = 20.0):
+    """Time the float64 oracle (forward + backward) on a bounded sample of the workload.
+
+    The sample is whole sequences from the front of the batch with all heads, grown
+    until the estimated cost reaches the budget; the rate is reported in accounted
+    TFLOP/s of forward+backward, the same unit as the GPU figure."""
+    import numpy as np
+
+    import oracle.attention as O
+    import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = W.make_inputs(wl)
+    q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
+    cu = wl.cu_seqlens_q
+    # grow a sample of heads of the first sequence until it takes ~budget
+    L = wl.seqlens_q[0]
+    heads = 1
+    sample_desc = None
+    spent = 0.0
+    flop_done = 0.0
+    h_done = 0
+    seq = slice(cu[0], cu[1])
+    t_start = time.perf_counter()
+    while h_done < wl.n_q_heads and (time.perf_counter() - t_start) < budget_s:
+        r = wl.n_q_heads // wl.n_kv_heads
+        g = h_done // r
+        # one query head (with its KV head) at a time, as a one-head problem
+        qs = q[seq, h_done:h_done + 1]
+        ks = k[seq, g:g + 1]
+        vs = v[seq, g:g + 1]
+        dos = do[seq, h_done:h_done + 1]
+        t0 = time.perf_counter()
+        O.forward(qs, ks, vs, [0, L], [0, L], wl.softmax_scale, wl.causal)
+        O.backward(qs, ks, vs, [0, L], [0, L], wl.softmax_scale, wl.causal, dos)
+        spent += time.perf_counter() - t0
+        flop_done += 3.5 * 4.0 * L * L * wl.head_dim * (0.5 if wl.causal else 1.0)
+        h_done += 1
+    sample_desc = f"sequence 0 ({L} tokens), {h_done} of {wl.n_q_heads} query heads, forward+backward"
+    return {
+        "value": flop_done / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": sample_desc,
+        "seconds": spent,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--workload", default="packed16k", help="packed16k (default) or any name in workloads")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this attention path has no multi-GPU mode",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    primary = W.packed_16k()
+    log(f"device {torch.cuda.get_device_name(0)}; warming up")
+    warm_gpu(1.0)
+    log(f"primary workload {primary.name}")
+    res = run_workload(primary, a.steps, a.warmup, profile=True)
+    secondary = {}
+    if not a.no_secondary:
+        for wl in (W.single_16k_full(), W.a100_shape(4096)):
+            log(f"secondary workload {wl.name}")
+            r = run_workload(wl, max(3, a.steps // 4), 2, profile=True)
+            secondary[wl.name] = {
+                "fwd_tflops": r["fwd_tflops"], "fwdbwd_tflops": r["fwdbwd_tflops"], "fwd_ms": r["fwd_ms"],
+                "step_ms": r["step_ms"], "frac_fwd": r["fwd_tflops"] / PEAK_BF16_TFLOPS,
+                "frac_fwdbwd": r["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
+                "kernels": r["kernels"],
+            }
+    # dominant kernel of the step: the one with the largest total time
+    kern = res["kernels"]
+    dom = max(kern, key=lambda k: kern[k]["avg_ms"]) if kern else "attn_fwd"
+    dom_ms = kern[dom]["avg_ms"] if kern else res["fwd_ms"]
+    flop = kernel_flop(dom, primary)
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma",
+        "achieved": flop / (dom_ms * 1e-3) / 1e12,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": flop / (dom_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "traffic": None,
+        "avg_ms": dom_ms,
+        "flop_per_launch": flop,
+    }
+    for k, v in kern.items():
+        f = kernel_flop(k, primary)
+        v["tflops"] = f / (v["avg_ms"] * 1e-3) / 1e12 if f else None
+        v["gbs"] = kernel_bytes(k, primary) / (v["avg_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": res["fwdbwd_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": res["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": primary.name, **primary.describe(), "pass": "fwd (with LSE) + bwd"},
+        "fwd_tflops": res["fwd_tflops"],
+        "fwd_ms": res["fwd_ms"],
+        "frac_of_peak_fwd": res["fwd_tflops"] / PEAK_BF16_TFLOPS,
+        "frac_of_peak_fwdbwd": res["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
+        "step_ms_median": res["step_ms_median"],
+        "fwd_ms_median": res["fwd_ms_median"],
+        "kernels": kern,
+        "roofline": roofline,
+        "secondary": secondary,
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (float64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(primary)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,240 @@
+"""MI355X (gfx950) exact attention over packed variable-length sequences.
+
+Thin Python binding over the C ABI of ``libattn_varlen.so`` (declared in
+``include/attn_varlen.h``): it checks tensor shapes, dtypes and devices, allocates
+outputs with PyTorch and passes raw pointers plus the current HIP stream. Every
+step of the computation runs in the library's HIP kernels; there is no other
+code path.
+
+Entry points (same names as the C functions):
+  * ``attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+    softmax_scale=None, causal=False, return_lse=False, out=None, lse=None)``
+  * ``attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k,
+    max_seqlen_q, max_seqlen_k, softmax_scale=None, causal=False, ...)``
+  * ``attn_varlen_func(...)``: autograd wrapper (forward, then ``.backward(dout)``).
+
+Shapes: q ``(total_q, Hq, D)``, k and v ``(total_k, Hkv, D)``, bf16, contiguous;
+cu_seqlens int32 on the same device; lse fp32 ``(Hq, total_q)``. The reference
+call shape is the varlen attention call of the "FA2 vs NATTEN on A100" issue's
+benchmark script and the varlen entry point in the FlashAttention repository
+guide's Public API.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import LibraryMissing, lib
+
+__all__ = [
+    "attn_varlen_fwd",
+    "attn_varlen_bwd",
+    "attn_varlen_bwd_workspace_size",
+    "attn_varlen_error_string",
+    "attn_varlen_version",
+    "attn_varlen_schedule_host",
+    "attn_varlen_schedule_device",
+    "attn_varlen_func",
+    "attn_varlen_profile_enable",
+    "attn_varlen_profile_records",
+    "AttnVarlenError",
+    "LibraryMissing",
+]
+
+
+class AttnVarlenError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where} failed with code {code}: {attn_varlen_error_string(code)}")
+
+
+def attn_varlen_error_string(code: int) -> str:
+    return lib().attn_varlen_error_string(int(code)).decode()
+
+
+def attn_varlen_version() -> Tuple[int, int]:
+    v = lib().attn_varlen_version()
+    return v >> 16, v & 0xFFFF
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check_bf16(name: str, t: torch.Tensor, dev: torch.device):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D (tokens, heads, head_dim), got {tuple(t.shape)}")
+
+
+def _check_inputs(q, k, v, cu_q, cu_k):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(n, t, dev)
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must have the same shape")
+    if q.shape[2] != k.shape[2]:
+        raise ValueError("q and k must have the same head_dim")
+    for n, t in (("cu_seqlens_q", cu_q), ("cu_seqlens_k", cu_k)):
+        if t.dtype != torch.int32 or t.device != dev or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 1-D int32 tensor on {dev}")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length >= 2")
+    return dev
+
+
+def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                    softmax_scale: Optional[float] = None, causal: bool = False, return_lse: bool = False,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Forward pass. Returns ``out`` or ``(out, lse)`` when ``return_lse`` (or ``lse`` is given)."""
+    dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.shape != (Hq, total_q) or not lse.is_contiguous() or lse.device != dev:
+            raise ValueError(f"lse must be contiguous float32 ({Hq}, {total_q}) on {dev}")
+    rc = lib().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                               cu_seqlens_q.numel() - 1, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k),
+                               Hq, Hkv, D, float(softmax_scale), int(bool(causal)), _ptr(out), _ptr(lse),
+                               _stream(dev))
+    if rc != 0:
+        raise AttnVarlenError(rc, "attn_varlen_fwd")
+    return (out, lse) if lse is not None else out
+
+
+def attn_varlen_bwd_workspace_size(num_seqs: int, total_q: int, total_k: int, n_q_heads: int, n_kv_heads: int,
+                                   head_dim: int) -> int:
+    return int(lib().attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, n_q_heads, n_kv_heads, head_dim))
+
+
+def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                    lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                    max_seqlen_k: int, softmax_scale: Optional[float] = None, causal: bool = False,
+                    dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                    dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward pass: returns ``(dq, dk, dv)`` for the loss ``sum(dout * out)``."""
+    dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _check_bf16("dout", dout, dev)
+    _check_bf16("out", out, dev)
+    if dout.shape != q.shape or out.shape != q.shape:
+        raise ValueError("dout and out must have the shape of q")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    if lse.dtype != torch.float32 or lse.shape != (Hq, total_q) or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError(f"lse must be contiguous float32 ({Hq}, {total_q}) on {dev}")
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_bf16(n, t, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+    num_seqs = cu_seqlens_q.numel() - 1
+    ws_bytes = attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    rc = lib().attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
+                               total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, float(softmax_scale),
+                               int(bool(causal)), _ptr(dout), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc != 0:
+        raise AttnVarlenError(rc, "attn_varlen_bwd")
+    return dq, dk, dv
+
+
+def attn_varlen_schedule_host(cu_seqlens_q, block_m: int):
+    """Host ranking of query blocks: list of (sequence, block) in the order the kernels visit them."""
+    import numpy as np
+
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int32))
+    n = lib().attn_varlen_schedule_host(cu.ctypes.data_as(ctypes.c_void_p), len(cu) - 1, block_m, None, None, 0)
+    if n < 0:
+        raise AttnVarlenError(int(n), "attn_varlen_schedule_host")
+    seq = np.zeros(max(n, 1), dtype=np.int32)
+    blk = np.zeros(max(n, 1), dtype=np.int32)
+    n2 = lib().attn_varlen_schedule_host(cu.ctypes.data_as(ctypes.c_void_p), len(cu) - 1, block_m,
+                                         seq.ctypes.data_as(ctypes.c_void_p), blk.ctypes.data_as(ctypes.c_void_p), n)
+    assert n2 == n
+    return list(zip(seq[:n].tolist(), blk[:n].tolist()))
+
+
+def attn_varlen_schedule_device(cu_seqlens_q: torch.Tensor, max_seqlen_q: int, block_m: int, count: int):
+    """Device ranking of the first ``count`` ranks (the decode the kernels run)."""
+    dev = cu_seqlens_q.device
+    seq = torch.full((count,), -2, dtype=torch.int32, device=dev)
+    blk = torch.full((count,), -2, dtype=torch.int32, device=dev)
+    rc = lib().attn_varlen_schedule_device(_ptr(cu_seqlens_q), cu_seqlens_q.numel() - 1, int(max_seqlen_q), block_m,
+                                           _ptr(seq), _ptr(blk), count, _stream(dev))
+    if rc != 0:
+        raise AttnVarlenError(rc, "attn_varlen_schedule_device")
+    return seq, blk
+
+
+class _AttnVarlenFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal):
+        out, lse = attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, return_lse=True)
+        ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
+        ctx.args = (max_q, max_k, softmax_scale, causal)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, softmax_scale, causal = ctx.args
+        dq, dk, dv = attn_varlen_bwd(dout.contiguous(), q, k, v, out, lse, cu_q, cu_k, max_q, max_k, softmax_scale,
+                                     causal)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
+def attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                     causal=False):
+    """Differentiable varlen attention (forward kernel, then the backward kernels on ``.backward``)."""
+    return _AttnVarlenFunction.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
+                                     causal)
+
+
+def attn_varlen_profile_enable(enable: bool = True) -> None:
+    """Start (drop earlier records) or stop per-launch event timing inside the library."""
+    lib().attn_varlen_profile_enable(1 if enable else 0)
+
+
+def attn_varlen_profile_records():
+    """List of (kernel name, ms) for the launches recorded in the current session (waits for them)."""
+    l = lib()
+    n = l.attn_varlen_profile_count()
+    out = []
+    buf = ctypes.create_string_buffer(64)
+    ms = ctypes.c_float()
+    for i in range(n):
+        rc = l.attn_varlen_profile_get(i, buf, 64, ctypes.byref(ms))
+        if rc != 0:
+            raise AttnVarlenError(rc, "attn_varlen_profile_get")
+        out.append((buf.value.decode(), float(ms.value)))
+    return out

@@ -1,0 +1,179 @@
+// av_api.cpp — the C ABI declared in include/attn_varlen.h: argument checks
+// (all before any HIP call) and dispatch to the kernel launchers.
+#include "../../include/attn_varlen.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "av_launch.h"
+#include "av_sched.h"
+
+namespace {
+
+constexpr int kVersionMajor = 1;
+constexpr int kVersionMinor = 0;
+constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_common(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                 int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t max_q, int32_t max_k, int32_t Hq,
+                 int32_t Hkv, int32_t D, float scale, int32_t causal) {
+  if (!q || !k || !v || !cu_q || !cu_k) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (D != 64 && D != 128 && D != 256) return ATTN_VARLEN_ERR_BAD_HEAD_DIM;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return ATTN_VARLEN_ERR_BAD_HEADS;
+  if (num_seqs < 1 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (max_q > total_q || max_k > total_k) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (total_q > INT32_MAX || total_k > INT32_MAX) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  // the largest grid any kernel launches (query or key blocks of 64 rows, times
+  // the query heads, 256 threads each) must stay below 2^32 work-items
+  const int64_t blocks = (total_q + total_k) / 64 + 2 * (int64_t)num_seqs;
+  if (blocks * (int64_t)Hq * 256 >= kMaxGridThreads) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (!std::isfinite(scale)) return ATTN_VARLEN_ERR_BAD_SCALE;
+  if (causal != 0 && causal != 1) return ATTN_VARLEN_ERR_BAD_FLAG;
+  return ATTN_VARLEN_OK;
+}
+
+av::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                          int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t max_q, int32_t max_k,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t causal, void* stream) {
+  av::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.max_q = max_q;
+  a.max_k = max_k;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.scale = scale;
+  a.causal = causal;
+  a.out = nullptr;
+  a.lse = nullptr;
+  a.stream = stream;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, float softmax_scale, int32_t causal, void* out, float* lse, void* stream) {
+  int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                        n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
+  if (rc != ATTN_VARLEN_OK) return rc;
+  if (!out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (total_q == 0) return ATTN_VARLEN_OK;
+  av::FwdArgs a = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
+                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, stream);
+  a.out = out;
+  a.lse = lse;
+  return av::launch_fwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+}
+
+size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim) {
+  (void)num_seqs;
+  (void)total_k;
+  (void)n_kv_heads;
+  (void)head_dim;
+  if (total_q < 0 || n_q_heads <= 0) return 0;
+  return av::bwd_workspace_bytes(total_q, n_q_heads);
+}
+
+int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, float softmax_scale, int32_t causal, const void* dout, const void* out,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                        n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
+  if (rc != ATTN_VARLEN_OK) return rc;
+  if (!dout || !out || !lse || !dq || !dk || !dv) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return ATTN_VARLEN_ERR_MISALIGNED;
+  const size_t need = av::bwd_workspace_bytes(total_q, n_q_heads);
+  if (!workspace || workspace_bytes < need) return ATTN_VARLEN_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;
+  av::BwdArgs a;
+  a.f = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, stream);
+  a.dout = dout;
+  a.out = out;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  return av::launch_bwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+}
+
+const char* attn_varlen_error_string(int code) {
+  switch (code) {
+    case ATTN_VARLEN_OK: return "success";
+    case ATTN_VARLEN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case ATTN_VARLEN_ERR_BAD_HEAD_DIM: return "head_dim must be 64, 128 or 256";
+    case ATTN_VARLEN_ERR_BAD_HEADS: return "head counts must be positive with n_q_heads a multiple of n_kv_heads";
+    case ATTN_VARLEN_ERR_BAD_SEQLEN: return "bad sequence sizes (num_seqs, totals or max seqlens)";
+    case ATTN_VARLEN_ERR_MISALIGNED: return "a tensor pointer is misaligned (16 bytes; lse 4 bytes)";
+    case ATTN_VARLEN_ERR_BAD_SCALE: return "softmax_scale is not finite";
+    case ATTN_VARLEN_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case ATTN_VARLEN_ERR_BAD_FLAG: return "causal must be 0 or 1";
+    case ATTN_VARLEN_ERR_HIP: return "HIP runtime error at kernel launch";
+    default: return "unknown error code";
+  }
+}
+
+int attn_varlen_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
+
+int64_t attn_varlen_schedule_host(const int32_t* cu_seqlens_q_host, int32_t num_seqs, int32_t block_m,
+                                  int32_t* seq_out, int32_t* block_out, int64_t capacity) {
+  if (!cu_seqlens_q_host || (capacity > 0 && (!seq_out || !block_out))) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (num_seqs < 1 || block_m < 1) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  for (int b = 0; b < num_seqs; ++b)
+    if (cu_seqlens_q_host[b + 1] < cu_seqlens_q_host[b]) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  return av::rank_enumerate_host(cu_seqlens_q_host, num_seqs, block_m, seq_out, block_out, capacity);
+}
+
+int attn_varlen_schedule_device(const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t max_seqlen_q,
+                                int32_t block_m, int32_t* seq_out, int32_t* block_out, int32_t count,
+                                void* stream) {
+  if (!cu_seqlens_q || !seq_out || !block_out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (num_seqs < 1 || block_m < 1 || max_seqlen_q < 0 || count < 0) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (count == 0) return ATTN_VARLEN_OK;
+  return av::launch_schedule_probe(cu_seqlens_q, num_seqs, max_seqlen_q, block_m, seq_out, block_out, count,
+                                   stream) == hipSuccess
+             ? ATTN_VARLEN_OK
+             : ATTN_VARLEN_ERR_HIP;
+}
+
+int attn_varlen_profile_enable(int enable) { return av::prof_enable(enable); }
+
+int attn_varlen_profile_count(void) { return av::prof_count(); }
+
+int attn_varlen_profile_get(int index, char* name, int name_capacity, float* ms) {
+  const int rc = av::prof_get(index, name, name_capacity, ms);
+  if (rc == -1) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (rc != 0) return ATTN_VARLEN_ERR_HIP;
+  return ATTN_VARLEN_OK;
+}
+
+}  // extern "C"

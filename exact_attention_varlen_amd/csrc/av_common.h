@@ -1,0 +1,184 @@
+// av_common.h — gfx950 device building blocks shared by the attention kernels:
+// bf16 MFMA tile operations, bf16 conversion, wave-level exchanges, the
+// work-item decode and the operand lane maps.
+//
+// MFMA used: v_mfma_f32_32x32x16_bf16 (D = A*B + C, A 32x16, B 16x32, fp32 C/D).
+// Operand lanes: lane l supplies A row (l % 32) and B column (l % 32), each with
+// 8 consecutive k values of k-group (l / 32). Result lanes: lane l, register v
+// holds D[8*(v/4) + 4*(l/32) + (v%4)][l % 32].
+//
+// Row permutations used so that no operand needs an in-register shuffle:
+//  * kperm(r): A-operand row r of the score product S^T = K * Q^T reads key
+//    kperm(r) of the 32-key block. Then result register v of lane half h holds
+//    key 16*(v/8) + 8*h + (v%8): registers 8s..8s+7 are 8 consecutive keys, which
+//    is exactly the B-operand k-group of the next product (P^T as B operand)
+//    for k-step s. Any consistent key order is exact, because the next product
+//    sums over keys.
+//  * dperm(r): A-operand row r of O^T = V^T * P^T reads head-dim row dperm(r).
+//    Then result register v of lane half h holds head-dim 16*h + v, so each lane
+//    stores 16 consecutive output values.
+#ifndef AV_COMMON_H
+#define AV_COMMON_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "av_sched.h"
+
+namespace av {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Round-to-nearest-even float -> bf16 of two values, packed (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Eight fp32 values -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float x3, float x4, float x5, float x6,
+                                            float x7) {
+  uint4 u;
+  u.x = pack_bf16x2(x0, x1);
+  u.y = pack_bf16x2(x2, x3);
+  u.z = pack_bf16x2(x4, x5);
+  u.w = pack_bf16x2(x6, x7);
+  return as_bf16x8(u);
+}
+
+// Eight fp32 values -> bf16 parts hi + lo with x ~= hi + lo to about 16 bits of
+// mantissa (lo is the bf16 rounding of the residual x - hi).
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint4 h, l;
+  uint32_t* hw = reinterpret_cast<uint32_t*>(&h);
+  uint32_t* lw = reinterpret_cast<uint32_t*>(&l);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    hw[i] = w;
+    const float r0 = x[2 * i] - __uint_as_float(w << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(w & 0xffff0000u);
+    lw[i] = pack_bf16x2(r0, r1);
+  }
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Value of lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int kperm(int r) {
+  return 16 * (r >> 4) + 8 * ((r >> 2) & 1) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+__device__ __forceinline__ int dperm(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// 16-byte loads/stores.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// ---------------------------------------------------------------------------
+// Work-item decode: rank -> (sequence, query block), computed by one wave with
+// all lanes agreeing on the result. See av_sched.h for the ranking.
+// ---------------------------------------------------------------------------
+
+// Number of blocks of sequence b (0 beyond num_seqs).
+__device__ __forceinline__ int seq_blocks(const int32_t* cu, int b, int num_seqs, int bm) {
+  if (b >= num_seqs) return 0;
+  return ceil_div(cu[b + 1] - cu[b], bm);
+}
+
+// C(k) = sum_b max(0, nb_b - k), per lane for the lane's own k.
+__device__ __forceinline__ int count_at_least(const int32_t* cu, int num_seqs, int bm, int nb_lane, int k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int acc = 0;
+  if (num_seqs <= kWave) {
+    for (int bb = 0; bb < num_seqs; ++bb) {
+      const int nb = __builtin_amdgcn_readlane(nb_lane, bb);
+      acc += max(0, nb - k);
+    }
+  } else {
+    for (int base = 0; base < num_seqs; base += kWave) {
+      const int nbc = seq_blocks(cu, base + lane, num_seqs, bm);
+      const int n = min(kWave, num_seqs - base);
+      for (int bb = 0; bb < n; ++bb) {
+        const int nb = __builtin_amdgcn_readlane(nbc, bb);
+        acc += max(0, nb - k);
+      }
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int highest_bit(uint64_t m) { return 63 - __builtin_clzll(m); }
+
+// Returns false when `rank` is past the last block. Must be called by all 64
+// lanes of a wave (the counts are evaluated with every lane active so that the
+// cross-lane reads see defined values).
+__device__ inline bool decode_rank(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int& b_out,
+                                   int& m_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (levels <= 0) return false;
+  const int nb_lane = seq_blocks(cu, lane, num_seqs, bm);
+  // pass 1: lane t probes k = t * stride
+  const int stride = ceil_div(levels, kWave);
+  const int k1 = lane * stride;
+  const int c1 = count_at_least(cu, num_seqs, bm, nb_lane, k1);
+  const uint64_t mask = __ballot((k1 < levels) && (c1 > rank));
+  if (mask == 0) return false;
+  const int t1 = highest_bit(mask);
+  int kstar = t1 * stride;
+  if (stride > 1) {
+    // pass 2: lane t probes k = t1 * stride + t inside the segment
+    const int k2 = t1 * stride + lane;
+    const int c2 = count_at_least(cu, num_seqs, bm, nb_lane, k2);
+    const uint64_t mask2 = __ballot((lane < stride) && (k2 < levels) && (c2 > rank));
+    kstar = t1 * stride + highest_bit(mask2);
+  }
+  // rank within level kstar: subtract the number of blocks of higher index
+  const int above = count_at_least(cu, num_seqs, bm, nb_lane, kstar + 1);
+  int j = rank - __builtin_amdgcn_readfirstlane(above);
+  for (int base = 0; base < num_seqs; base += kWave) {
+    const int nbc = seq_blocks(cu, base + lane, num_seqs, bm);
+    const uint64_t sel = __ballot(nbc > kstar);
+    const int pc = __popcll(sel);
+    if (j < pc) {
+      // position of the (j+1)-th set bit
+      uint64_t s = sel;
+      for (int i = 0; i < j; ++i) s &= s - 1;
+      b_out = base + __builtin_ctzll(s);
+      m_out = kstar;
+      return true;
+    }
+    j -= pc;
+  }
+  return false;
+}
+
+}  // namespace av
+
+#endif  // AV_COMMON_H

@@ -1,0 +1,61 @@
+// av_launch.h — internal interface between the C ABI (av_api.cpp) and the
+// kernel launchers. Arguments arrive here already validated.
+#ifndef AV_LAUNCH_H
+#define AV_LAUNCH_H
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace av {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int num_seqs;
+  int64_t total_q;
+  int64_t total_k;
+  int max_q;
+  int max_k;
+  int Hq;
+  int Hkv;
+  int D;
+  float scale;
+  int causal;
+  void* out;
+  float* lse;
+  void* stream;
+};
+
+struct BwdArgs {
+  FwdArgs f;  // q, k, v, packing, heads, scale, causal, stream (f.out / f.lse unused)
+  const void* dout;
+  const void* out;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: fp32 [Hq][total_q]
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_schedule_probe(const int32_t* cu_q, int num_seqs, int max_q, int block_m, int32_t* seq_out,
+                                 int32_t* block_out, int count, void* stream);
+
+// per-launch profiling (av_prof.cpp)
+void prof_begin(const char* name, hipStream_t stream);
+void prof_end(hipStream_t stream);
+int prof_enable(int enable);
+int prof_count();
+int prof_get(int i, char* name, int cap, float* ms);
+
+int64_t fwd_grid_size(int64_t total_q, int num_seqs, int Hq, int Hkv);
+size_t bwd_workspace_bytes(int64_t total_q, int Hq);
+
+}  // namespace av
+
+#endif  // AV_LAUNCH_H

@@ -1,0 +1,179 @@
+/*
+ * attn_varlen.h — C ABI of the MI355X (gfx950) exact-attention library for packed
+ * variable-length sequences with grouped-query heads.
+ *
+ * Sources (page title, section):
+ *  [A100]  "[BUG] FA2 vs NATTEN on A100: 3.5-4.8x perf gap; what is the 'flash2
+ *          varlen instability' in checks.py?" (cosmos-framework issue), benchmark
+ *          script: attention(q, k, v, cumulative_seqlen_Q, cumulative_seqlen_KV,
+ *          max_seqlen_Q, max_seqlen_KV); cumulative seqlens are int32 device tensors,
+ *          the max seqlens host integers; 32 query heads over 8 KV heads.
+ *  [LSE]   "[FA4/B200] return_lse=True makes D64 forward about 19% faster", repro
+ *          script, make_call: caller-allocated out and an optional fp32 lse buffer,
+ *          with and without the LSE output.
+ *  [HD256] "FA4 head_dim=256 B200 Regression Check", Environment: head_dim =
+ *          head_dim_v, softmax_scale = head_dim ** -0.5, causal and non-causal.
+ *  [GUIDE] FlashAttention repository guide (CLAUDE.md), Public API (varlen entry
+ *          point with cu_seqlens_q / cu_seqlens_k; last dimension contiguous,
+ *          16-byte aligned), Backward Kernels (preprocess, main, postprocess).
+ *
+ * Operation (forward). For each packed sequence b with query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b],
+ * cu_seqlens_k[b+1]), each query head h and its KV head g = h / (n_q_heads /
+ * n_kv_heads):
+ *     s_ij  = softmax_scale * <q_i, k_j>          (fp32 accumulation of bf16 inputs)
+ *     visible(i, j) = !causal || j <= i + Lk - Lq (causal mask aligned bottom-right)
+ *     lse_i = ln sum_{visible j} exp(s_ij)
+ *     out_i = sum_{visible j} exp(s_ij - lse_i) * v_j
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Layouts (all row-major, last dimension unit-stride, no padding):
+ *     q, out, dout, dq : bf16 [total_q][n_q_heads][head_dim]
+ *     k, v, dk, dv     : bf16 [total_k][n_kv_heads][head_dim]
+ *     lse              : fp32 [n_q_heads][total_q]
+ *     cu_seqlens_q/_k  : int32 [num_seqs + 1], device memory, cu[0] = 0,
+ *                        non-decreasing, cu[num_seqs] = total
+ * bf16 is IEEE bfloat16 (1-8-7) stored as 16-bit words; outputs are rounded to
+ * nearest-even.
+ *
+ * Ownership: the caller allocates every buffer (device memory) and keeps it alive
+ * until the work on `stream` is done. The library allocates nothing, frees
+ * nothing and keeps no pointer after a call returns.
+ *
+ * Execution: calls are asynchronous on `stream` (a hipStream_t, passed as void*;
+ * NULL is the default stream) and never synchronise the host. They are
+ * re-entrant and stateless. Identical inputs give bit-identical outputs (no
+ * atomics; every reduction runs in a fixed order).
+ *
+ * Errors: 0 on success, a negative ATTN_VARLEN_ERR_* code otherwise. Every
+ * argument check runs before any HIP call, so a rejected call touches no device
+ * state. Preconditions on device-resident data (the cu_seqlens contents agree
+ * with num_seqs, totals and max seqlens) are not checked: a violation gives
+ * undefined results.
+ */
+#ifndef ATTN_VARLEN_H
+#define ATTN_VARLEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_VARLEN_OK = 0,
+  ATTN_VARLEN_ERR_NULL_POINTER = -1,      /* a required pointer is NULL */
+  ATTN_VARLEN_ERR_BAD_HEAD_DIM = -2,      /* head_dim not in {64, 128, 256} */
+  ATTN_VARLEN_ERR_BAD_HEADS = -3,         /* heads <= 0 or n_q_heads % n_kv_heads != 0 */
+  ATTN_VARLEN_ERR_BAD_SEQLEN = -4,        /* num_seqs < 1, negative totals/max, max > total, or too large */
+  ATTN_VARLEN_ERR_MISALIGNED = -5,        /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
+  ATTN_VARLEN_ERR_BAD_SCALE = -6,         /* softmax_scale is not finite */
+  ATTN_VARLEN_ERR_WORKSPACE = -7,         /* workspace NULL or smaller than attn_varlen_bwd_workspace_size() */
+  ATTN_VARLEN_ERR_BAD_FLAG = -8,          /* causal not 0 or 1 */
+  ATTN_VARLEN_ERR_HIP = -9                /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * Forward pass. [A100] benchmark script `call`; [LSE] make_call (out=, lse=,
+ * return_lse); [GUIDE] Public API.
+ *   q, k, v            inputs (layouts above)
+ *   cu_seqlens_q/_k    packing of queries / keys, device int32 [num_seqs + 1]
+ *   num_seqs           number of packed sequences (>= 1); zero-length sequences are legal
+ *   total_q, total_k   cu_seqlens_q[num_seqs], cu_seqlens_k[num_seqs]
+ *   max_seqlen_q/_k    upper bounds of the per-sequence lengths (host values)
+ *   n_q_heads, n_kv_heads, head_dim   head counts (n_q_heads % n_kv_heads == 0) and D
+ *   softmax_scale      multiplies the fp32 dot products (any finite value)
+ *   causal             0 or 1
+ *   out                output, bf16 [total_q][n_q_heads][head_dim]
+ *   lse                optional fp32 [n_q_heads][total_q]; NULL skips the LSE write
+ */
+int attn_varlen_fwd(const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t num_seqs, int64_t total_q, int64_t total_k,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    float softmax_scale, int32_t causal,
+                    void* out, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace attn_varlen_bwd needs for these sizes: the fp32 row
+ * term Delta_i = sum_d dout_id * out_id per query row and head ([GUIDE] Backward
+ * Kernels: the preprocess kernel), [n_q_heads][total_q], rounded up to 256 bytes.
+ */
+size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim);
+
+/*
+ * Backward pass: gradients of sum(dout * out) with respect to q, k, v for the
+ * forward defined above ([A100] benchmark script `fb`: forward then
+ * out.backward(dout); [GUIDE] Backward Kernels). Arguments up to `causal` are
+ * those of the forward call that produced `out` and `lse`.
+ *   dout, out          bf16 [total_q][n_q_heads][head_dim]
+ *   lse                fp32 [n_q_heads][total_q] from the forward (required)
+ *   dq                 bf16 [total_q][n_q_heads][head_dim]     (written)
+ *   dk, dv             bf16 [total_k][n_kv_heads][head_dim]    (written; summed over
+ *                      the query heads of each KV head's group)
+ *   workspace          device scratch of at least attn_varlen_bwd_workspace_size()
+ *                      bytes, 16-byte aligned; contents on entry are ignored
+ * Every element of dq, dk, dv is written (keys no query can see get zero).
+ */
+int attn_varlen_bwd(const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int32_t num_seqs, int64_t total_q, int64_t total_k,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    float softmax_scale, int32_t causal,
+                    const void* dout, const void* out, const float* lse,
+                    void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of an error code. Never NULL. */
+const char* attn_varlen_error_string(int code);
+
+/* Library ABI version: (major << 16) | minor. */
+int attn_varlen_version(void);
+
+/*
+ * Work-list inspection (host, no GPU needed): the order in which the forward
+ * visits query blocks. Query blocks of `block_m` rows are ranked by descending
+ * block index (longest causal work first), ties by ascending sequence. Writes the
+ * sequence index and block index of rank r to seq_out[r], block_out[r] for
+ * r < min(capacity, count) and returns count, or a negative error code.
+ * cu_seqlens_q_host is a host array of num_seqs + 1 entries.
+ */
+int64_t attn_varlen_schedule_host(const int32_t* cu_seqlens_q_host, int32_t num_seqs, int32_t block_m,
+                                  int32_t* seq_out, int32_t* block_out, int64_t capacity);
+
+/*
+ * The same ranking computed by the device code path the kernels use, for
+ * `count` ranks starting at 0: seq_out / block_out are device int32 [count];
+ * ranks beyond the number of blocks get -1. Asynchronous on `stream`.
+ */
+int attn_varlen_schedule_device(const int32_t* cu_seqlens_q, int32_t num_seqs, int32_t max_seqlen_q,
+                                int32_t block_m, int32_t* seq_out, int32_t* block_out, int32_t count,
+                                void* stream);
+
+/*
+ * Per-launch timing, for benchmarks. While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on the launch's stream (the
+ * events belong to the library and are reused). attn_varlen_profile_enable(1)
+ * starts a new session (drops earlier records); (0) stops recording. Records
+ * beyond 65536 per session are dropped. Not meant for concurrent use from
+ * several host threads.
+ *   attn_varlen_profile_count   number of launches recorded in the session
+ *   attn_varlen_profile_get     kernel name (copied, NUL-terminated, truncated to
+ *                               name_capacity) and its duration in ms; waits for
+ *                               the launch to finish. Returns
+ *                               ATTN_VARLEN_ERR_BAD_SEQLEN for an index out of
+ *                               range, ATTN_VARLEN_ERR_HIP if the events fail.
+ */
+int attn_varlen_profile_enable(int enable);
+int attn_varlen_profile_count(void);
+int attn_varlen_profile_get(int index, char* name, int name_capacity, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_VARLEN_H */

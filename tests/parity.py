@@ -1,0 +1,111 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs, run the float64 oracle on the same bits, compare with the stated
+tolerances.
+
+Tolerances (fixed for this attention path, bf16 inputs and outputs):
+  out    max |gpu - ref| <= 1e-2  and  ||gpu - ref||_F / ||ref||_F <= 5e-3
+  lse    max |gpu - ref| <= 1e-3 over rows with a visible key; -inf elsewhere
+  dq, dk, dv   ||gpu - ref||_F / ||ref||_F <= 2e-2
+"""
+from __future__ import annotations
+
+import sys
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+import exact_attention_varlen_amd as A
+import workloads as W
+
+OUT_MAX_ABS = 1e-2
+OUT_REL_FRO = 5e-3
+LSE_MAX_ABS = 1e-3
+GRAD_REL_FRO = 2e-2
+
+
+def announce(msg: str) -> None:
+    """Name the case on the real stderr before a GPU step (survives a lost process)."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def device() -> torch.device:
+    return torch.device("cuda:0")
+
+
+def to_dev(inp: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+    dev = device()
+    return {k: v.to(dev) for k, v in inp.items()}
+
+
+def gpu_fwd(wl: W.Workload, d: Dict[str, torch.Tensor], return_lse: bool = True):
+    return A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                             wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=return_lse)
+
+
+def gpu_bwd(wl: W.Workload, d: Dict[str, torch.Tensor], out, lse):
+    return A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                             wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
+    n = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (n if n > 0 else 1.0))
+
+
+def check_out(x: np.ndarray, ref: np.ndarray, what: str = "out"):
+    assert np.all(np.isfinite(x)), f"{what}: non-finite values"
+    mabs = float(np.abs(x - ref).max()) if x.size else 0.0
+    rf = rel_fro(x, ref)
+    assert mabs <= OUT_MAX_ABS, f"{what}: max-abs {mabs:.3e} > {OUT_MAX_ABS}"
+    assert rf <= OUT_REL_FRO, f"{what}: rel-Frobenius {rf:.3e} > {OUT_REL_FRO}"
+    return mabs, rf
+
+
+def check_lse(x: np.ndarray, ref: np.ndarray, what: str = "lse"):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(x), fin), f"{what}: finite pattern differs"
+    assert np.all(x[~fin] == -np.inf), f"{what}: rows without a visible key must be -inf"
+    mabs = float(np.abs(x[fin] - ref[fin]).max()) if fin.any() else 0.0
+    assert mabs <= LSE_MAX_ABS, f"{what}: max-abs {mabs:.3e} > {LSE_MAX_ABS}"
+    return mabs
+
+
+def check_grad(x: np.ndarray, ref: np.ndarray, what: str):
+    assert np.all(np.isfinite(x)), f"{what}: non-finite values"
+    rf = rel_fro(x, ref)
+    assert rf <= GRAD_REL_FRO, f"{what}: rel-Frobenius {rf:.3e} > {GRAD_REL_FRO}"
+    return rf
+
+
+def sample_rows(cu, per_seq: int = 6, extra: int = 64, seed: int = 0, tail_only: bool = False,
+                tail: int = 256) -> np.ndarray:
+    """Deterministic query/key rows: each sequence's edges and middle, plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    total = cu[-1]
+    for b in range(len(cu) - 1):
+        c, L = cu[b], cu[b + 1] - cu[b]
+        if L == 0:
+            continue
+        if tail_only:
+            lo = max(0, L - tail)
+            cand = [L - 1, L - 2, lo, (lo + L) // 2]
+        else:
+            cand = [0, 1, L // 3, L // 2, L - 2, L - 1]
+        for x in cand[:per_seq]:
+            if 0 <= x < L:
+                rows.add(c + x)
+    if extra and total > 0:
+        if tail_only:
+            pool = np.concatenate([np.arange(max(cu[b], cu[b + 1] - tail), cu[b + 1]) for b in range(len(cu) - 1)])
+            pick = rng.choice(pool, size=min(extra, pool.size), replace=False) if pool.size else []
+        else:
+            pick = rng.choice(total, size=min(extra, total), replace=False)
+        rows.update(int(x) for x in pick)
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,166 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments with its error codes before touching the device; the host
+work ranking is checked by brute force."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import exact_attention_varlen_amd as A
+from exact_attention_varlen_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_varlen.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_varlen_\w+)\s*\(", text)))
+
+
+def header_enums():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_VARLEN_\w+)\s*=\s*(-?\d+)", text)}
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    l = _lib.lib()
+    names = header_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(l, n), n
+    assert set(names) == set(_lib.exported_names())
+
+
+def test_version_and_error_strings():
+    assert A.attn_varlen_version() == (1, 0)
+    for name, code in header_enums().items():
+        s = A.attn_varlen_error_string(code)
+        assert s and s != "unknown error code", name
+    assert A.attn_varlen_error_string(12345) == "unknown error code"
+
+
+E = header_enums()
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced because validation fails first
+
+
+def fwd_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=1, total_q=16, total_k=16, max_q=16, max_k=16,
+             Hq=4, Hkv=2, D=96, scale=0.125, causal=0, out=FAKE, lse=None, stream=None)
+    a.update(over)
+    return _lib.lib().attn_varlen_fwd(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"], a["total_q"],
+                                      a["total_k"], a["max_q"], a["max_k"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                      a["causal"], a["out"], a["lse"], a["stream"])
+
+
+def bwd_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=1, total_q=16, total_k=16, max_q=16, max_k=16,
+             Hq=4, Hkv=2, D=96, scale=0.125, causal=0, dout=FAKE, out=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    return _lib.lib().attn_varlen_bwd(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"], a["total_q"],
+                                      a["total_k"], a["max_q"], a["max_k"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                      a["causal"], a["dout"], a["out"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                                      a["ws_bytes"], a["stream"])
+
+
+# Each case is invalid in exactly the named way (D=96 is also invalid, so cases that
+# test other checks fix D to a valid value and break one thing only where needed).
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), "ATTN_VARLEN_ERR_BAD_HEAD_DIM"),
+    (dict(D=32), "ATTN_VARLEN_ERR_BAD_HEAD_DIM"),
+    (dict(q=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(cu_k=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(D=128, out=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(D=128, Hq=6, Hkv=4), "ATTN_VARLEN_ERR_BAD_HEADS"),
+    (dict(D=128, Hq=0), "ATTN_VARLEN_ERR_BAD_HEADS"),
+    (dict(D=128, Hkv=-1), "ATTN_VARLEN_ERR_BAD_HEADS"),
+    (dict(D=128, num_seqs=0), "ATTN_VARLEN_ERR_BAD_SEQLEN"),
+    (dict(D=128, total_q=-1), "ATTN_VARLEN_ERR_BAD_SEQLEN"),
+    (dict(D=128, max_q=17), "ATTN_VARLEN_ERR_BAD_SEQLEN"),
+    (dict(D=128, max_k=-3), "ATTN_VARLEN_ERR_BAD_SEQLEN"),
+    (dict(D=128, total_q=1 << 40, max_q=16), "ATTN_VARLEN_ERR_BAD_SEQLEN"),
+    (dict(D=128, q=FAKE + 8), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=128, out=FAKE + 2), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=128, lse=FAKE + 2), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=128, cu_q=FAKE + 1), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=128, scale=float("nan")), "ATTN_VARLEN_ERR_BAD_SCALE"),
+    (dict(D=128, scale=float("inf")), "ATTN_VARLEN_ERR_BAD_SCALE"),
+    (dict(D=128, causal=2), "ATTN_VARLEN_ERR_BAD_FLAG"),
+])
+def test_fwd_argument_errors(over, code):
+    assert fwd_call(**over) == E[code]
+
+
+def test_fwd_empty_problem_is_a_no_op():
+    # total_q == 0 returns success without launching anything
+    assert fwd_call(D=64, total_q=0, max_q=0) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), "ATTN_VARLEN_ERR_BAD_HEAD_DIM"),
+    (dict(D=64, dout=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(D=64, lse=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(D=64, dv=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(D=64, ws=None), "ATTN_VARLEN_ERR_WORKSPACE"),
+    (dict(D=64, ws_bytes=16 * 4 * 4 - 1), "ATTN_VARLEN_ERR_WORKSPACE"),
+    (dict(D=64, ws=FAKE + 4), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=64, dk=FAKE + 8), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=64, lse=FAKE + 1), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(D=64, Hq=3, Hkv=2), "ATTN_VARLEN_ERR_BAD_HEADS"),
+    (dict(D=64, causal=-1), "ATTN_VARLEN_ERR_BAD_FLAG"),
+])
+def test_bwd_argument_errors(over, code):
+    assert bwd_call(**over) == E[code]
+
+
+def test_bwd_workspace_size():
+    ws = A.attn_varlen_bwd_workspace_size(3, 1000, 900, 32, 8, 128)
+    assert ws >= 1000 * 32 * 4 and ws % 256 == 0
+    assert A.attn_varlen_bwd_workspace_size(1, 0, 0, 4, 2, 64) == 0
+
+
+def test_schedule_device_argument_errors():
+    l = _lib.lib()
+    assert l.attn_varlen_schedule_device(None, 1, 16, 128, FAKE, FAKE, 4, None) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+    assert l.attn_varlen_schedule_device(FAKE, 0, 16, 128, FAKE, FAKE, 4, None) == E["ATTN_VARLEN_ERR_BAD_SEQLEN"]
+    assert l.attn_varlen_schedule_device(FAKE, 1, 16, 128, FAKE, FAKE, 0, None) == 0
+
+
+def brute_force_schedule(lengths, bm):
+    items = []
+    for b, L in enumerate(lengths):
+        for m in range(-(-L // bm)):
+            items.append((b, m))
+    # descending block index, ties by ascending sequence
+    return sorted(items, key=lambda t: (-t[1], t[0]))
+
+
+@pytest.mark.parametrize("lengths,bm", [
+    ([200, 312], 128),
+    ([3523, 2702, 2219, 1292, 1438, 413, 544, 319, 929, 3005], 128),
+    ([0, 5, 0, 130, 1, 128, 129, 0], 64),
+    ([131072], 128),
+    ([0], 128),
+    (list(range(0, 300, 7)), 32),
+])
+def test_schedule_host_matches_brute_force(lengths, bm):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    got = A.attn_varlen_schedule_host(cu, bm)
+    assert got == brute_force_schedule(lengths, bm)
+    # every block exactly once; the causal work (block index + 1) never increases along the order
+    assert len(set(got)) == len(got) == sum(-(-L // bm) for L in lengths)
+    work = [m for _, m in got]
+    assert all(a >= b for a, b in zip(work, work[1:]))
+
+
+def test_schedule_host_random():
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        lengths = rng.integers(0, 600, size=rng.integers(1, 90)).tolist()
+        bm = int(rng.choice([32, 64, 128]))
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        assert A.attn_varlen_schedule_host(cu, bm) == brute_force_schedule(lengths, bm)

@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle on
+the same seeded inputs, element by element, plus the bitwise and structural
+checks of the kernels. Tolerances are in tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_varlen_amd as A
+import oracle.attention as O
+import workloads as W
+from parity import (announce, check_grad, check_lse, check_out, f64, gpu_bwd, gpu_fwd, sample_rows, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_parity(wl: W.Workload, backward: bool = True):
+    inp = W.make_inputs(wl)
+    d = to_dev(inp)
+    announce(f"fwd {wl.name} seqlens_q={wl.seqlens_q} seqlens_k={wl.seqlens_k} Hq={wl.n_q_heads} "
+             f"Hkv={wl.n_kv_heads} D={wl.head_dim} causal={wl.causal}")
+    out, lse = gpu_fwd(wl, d)
+    torch.cuda.synchronize()
+    q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
+    ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal)
+    check_out(f64(out), ref_o)
+    check_lse(f64(lse), ref_l)
+    if not backward:
+        return
+    announce(f"bwd {wl.name}")
+    dq, dk, dv = gpu_bwd(wl, d, out, lse)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do)
+    check_grad(f64(dq), rq, "dq")
+    check_grad(f64(dk), rk, "dk")
+    check_grad(f64(dv), rv, "dv")
+
+
+# --------------------------------------------------------------------------
+# small and medium problems: full tensors, several tiles, ragged tails
+# --------------------------------------------------------------------------
+
+SMALL = [
+    W.tiny(False),
+    W.tiny(True),
+]
+for D in (64, 128, 256):
+    for c in (False, True):
+        SMALL.append(W.Workload(f"ragged-d{D}-{'c' if c else 'f'}", [1, 77, 300, 513, 0, 129], 8, 2, D, c))
+SMALL += [
+    W.Workload("mha-d64-f", [640, 383], 4, 4, 64, False),
+    W.Workload("mqa-d128-c", [257, 64, 191], 8, 1, 128, True),
+    W.Workload("lq-ne-lk-d128-f", [100, 300, 5, 0], 4, 1, 128, False, seqlens_k=[250, 64, 0, 33]),
+    W.Workload("lq-ne-lk-d128-c", [100, 300, 5, 0], 4, 1, 128, True, seqlens_k=[250, 64, 0, 33]),
+    W.Workload("lq-ne-lk-d64-c", [129, 3, 200], 2, 2, 64, True, seqlens_k=[300, 1, 70]),
+    W.Workload("lq-ne-lk-d256-c", [65, 190], 2, 1, 256, True, seqlens_k=[200, 64]),
+    W.Workload("single-token-seqs-d128-c", [1, 1, 2, 1], 4, 2, 128, True),
+    W.Workload("scale-zero-d64-f", [150, 90], 2, 1, 64, False, softmax_scale=0.0),
+    W.Workload("scale-large-d128-c", [200], 4, 2, 128, True, softmax_scale=0.5),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_parity_small(wl):
+    full_parity(wl)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads
+# --------------------------------------------------------------------------
+
+def test_parity_single_4096_gqa_d128():
+    full_parity(W.a100_shape(4096))
+
+
+def test_parity_packed16k_causal_d128():
+    full_parity(W.packed_16k())
+
+
+def sampled_parity(wl: W.Workload, dkdv_mode: str):
+    """Full-size GPU run; oracle on sampled rows (O, LSE, dQ; dK/dV per dkdv_mode)."""
+    inp = W.make_inputs(wl, with_dout=wl.backward)
+    d = to_dev(inp)
+    cu_q, cu_k = wl.cu_seqlens_q, wl.cu_seqlens_k
+    announce(f"fwd {wl.name} (full size, sampled oracle)")
+    out, lse = gpu_fwd(wl, d)
+    dq = dk = dv = None
+    if wl.backward:
+        announce(f"bwd {wl.name} (full size, sampled oracle)")
+        dq, dk, dv = gpu_bwd(wl, d, out, lse)
+    torch.cuda.synchronize()
+    q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+    rows = sample_rows(cu_q, extra=64)
+    r, ro, rl = O.forward_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, rows)
+    check_out(f64(out[torch.as_tensor(r)]), ro)
+    check_lse(f64(lse[:, torch.as_tensor(r)]), rl)
+    if not wl.backward:
+        return
+    do = W.to_f64(inp["dout"])
+    r, rdq = O.backward_dq_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, rows)
+    check_grad(f64(dq[torch.as_tensor(r)]), rdq, "dq(sampled rows)")
+    if dkdv_mode in ("tail", "spread"):
+        krows = sample_rows(cu_k, extra=32, tail_only=(dkdv_mode == "tail"))
+        if dkdv_mode == "spread":  # keep the oracle cost bounded: keys of the first two sequences only
+            krows = krows[krows < cu_k[min(2, len(cu_k) - 1)]]
+        r, rdk, rdv = O.backward_dkdv_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, krows)
+        check_grad(f64(dk[torch.as_tensor(r)]), rdk, "dk(sampled rows)")
+        check_grad(f64(dv[torch.as_tensor(r)]), rdv, "dv(sampled rows)")
+    check_gradient_sums(wl, d, dk, dv)
+
+
+def check_gradient_sums(wl, d, dk, dv):
+    """Any-size properties of the exact gradient, per sequence and KV head:
+    sum_j dK_j = 0 and sum_j dV_j = sum over the group's heads and rows of dO_i
+    (each query row with a visible key has softmax weights summing to one)."""
+    r = wl.n_q_heads // wl.n_kv_heads
+    cu_q, cu_k = wl.cu_seqlens_q, wl.cu_seqlens_k
+    dkf = dk.float()
+    dvf = dv.float()
+    dof = d["dout"].float()
+    for b in range(len(cu_q) - 1):
+        ks, ke = cu_k[b], cu_k[b + 1]
+        qs, qe = cu_q[b], cu_q[b + 1]
+        if ke == ks or qe == qs:
+            continue
+        n = ke - ks
+        for g in range(wl.n_kv_heads):
+            sk = dkf[ks:ke, g].double().sum(0)
+            sv = dvf[ks:ke, g].double().sum(0)
+            want = dof[qs:qe, g * r:(g + 1) * r].double().sum((0, 1))
+            scale_k = dkf[ks:ke, g].double().pow(2).mean().sqrt() * (n ** 0.5)
+            scale_v = dvf[ks:ke, g].double().pow(2).mean().sqrt() * (n ** 0.5)
+            assert float(sk.norm() / (scale_k * sk.numel() ** 0.5 + 1e-30)) < 0.05, "sum of dK is not ~0"
+            assert float((sv - want).norm() / (scale_v * sv.numel() ** 0.5 + 1e-30)) < 0.05, "sum of dV mismatch"
+
+
+FULL_SIZE = [
+    (W.long_65k(), "tail"),
+    (W.hd64_mha(), "none"),
+    (W.hd256_gqa(8, 4096, False), "spread"),
+    (W.hd256_gqa(8, 4096, True), "tail"),
+    (W.hd256_gqa(2, 16384, False), "none"),
+    (W.hd256_gqa(2, 16384, True), "tail"),
+    (W.hd256_gqa(1, 32768, False), "none"),
+    (W.hd256_gqa(1, 32768, True), "tail"),
+    (W.hd256_gqa(1, 131072, False), "none"),
+    (W.hd256_gqa(1, 131072, True), "tail"),
+    (W.single_16k_full(), "none"),
+]
+
+
+@pytest.mark.parametrize("wl,mode", FULL_SIZE, ids=[w.name for w, _ in FULL_SIZE])
+def test_parity_full_size_sampled(wl, mode):
+    sampled_parity(wl, mode)
+
+
+# --------------------------------------------------------------------------
+# bitwise and structural properties of the kernels
+# --------------------------------------------------------------------------
+
+def _run_all(wl, d):
+    out, lse = gpu_fwd(wl, d)
+    dq, dk, dv = gpu_bwd(wl, d, out, lse)
+    torch.cuda.synchronize()
+    return out, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_deterministic(causal):
+    wl = W.Workload("det", [700, 33, 1200], 8, 2, 128, causal)
+    d = to_dev(W.make_inputs(wl))
+    announce(f"determinism causal={causal}")
+    a = _run_all(wl, d)
+    b = _run_all(wl, d)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_lse_flag_does_not_change_output():
+    wl = W.Workload("lseflag", [333, 1000], 16, 16, 64, False)
+    d = to_dev(W.make_inputs(wl, with_dout=False))
+    announce("lse on/off")
+    o1, _ = gpu_fwd(wl, d, return_lse=True)
+    o2 = gpu_fwd(wl, d, return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_separate_calls(causal):
+    wl = W.Workload("varlen-sep", [300, 1, 517, 128], 8, 4, 128, causal)
+    d = to_dev(W.make_inputs(wl))
+    announce(f"varlen vs separate causal={causal}")
+    out, lse, dq, dk, dv = _run_all(wl, d)
+    cu = wl.cu_seqlens_q
+    for b, L in enumerate(wl.seqlens_q):
+        s = slice(cu[b], cu[b + 1])
+        one = W.Workload("one", [L], 8, 4, 128, causal)
+        db = {k: (v[s].contiguous() if k in ("q", "k", "v", "dout") else v) for k, v in d.items()}
+        db["cu_seqlens_q"] = torch.tensor([0, L], dtype=torch.int32, device=out.device)
+        db["cu_seqlens_k"] = db["cu_seqlens_q"]
+        o1, l1, q1, k1, v1 = _run_all(one, db)
+        assert torch.equal(out[s], o1)
+        assert torch.equal(lse[:, s], l1)
+        assert torch.equal(dq[s], q1)
+        assert torch.equal(dk[s], k1)
+        assert torch.equal(dv[s], v1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_mha_with_repeated_kv(causal):
+    Hq, Hkv = 8, 2
+    wl = W.Workload("gqa", [400, 250], Hq, Hkv, 64, causal)
+    d = to_dev(W.make_inputs(wl))
+    announce(f"gqa vs mha causal={causal}")
+    out, lse, dq, dk, dv = _run_all(wl, d)
+    wm = W.Workload("mha", [400, 250], Hq, Hq, 64, causal)
+    dm = dict(d)
+    dm["k"] = d["k"].repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    dm["v"] = d["v"].repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    om, lm, qm, km, vm = _run_all(wm, dm)
+    assert torch.equal(out, om)
+    assert torch.equal(lse, lm)
+    assert torch.equal(dq, qm)
+    km = km.float().reshape(km.shape[0], Hkv, Hq // Hkv, -1).sum(2)
+    vm = vm.float().reshape(vm.shape[0], Hkv, Hq // Hkv, -1).sum(2)
+    assert float((dk.float() - km).norm() / km.norm()) < 1e-2
+    assert float((dv.float() - vm).norm() / vm.norm()) < 1e-2
+
+
+def test_no_writes_outside_outputs():
+    """Canary bytes around every output buffer must survive fwd and bwd."""
+    wl = W.Workload("canary", [130, 0, 77], 4, 2, 128, True, seqlens_k=[130, 40, 0])
+    inp = W.make_inputs(wl)
+    d = to_dev(inp)
+    dev = d["q"].device
+    pad = 4096
+    def padded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * pad,), 7, dtype=dtype, device=dev)
+        return buf, buf[pad:pad + n].view(shape)
+    ob, out = padded(d["q"].shape, torch.bfloat16)
+    lb, lse = padded((4, wl.total_q), torch.float32)
+    announce("canary fwd")
+    A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                      wl.max_seqlen_k, wl.softmax_scale, True, out=out, lse=lse)
+    qb, dq = padded(d["q"].shape, torch.bfloat16)
+    kb, dk = padded(d["k"].shape, torch.bfloat16)
+    vb, dv = padded(d["v"].shape, torch.bfloat16)
+    announce("canary bwd")
+    A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                      wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for buf in (ob, lb, qb, kb, vb):
+        assert torch.all(buf[:pad] == 7) and torch.all(buf[-pad:] == 7)
+    # keys of the middle sequence see no query (Lq = 0): zero gradients; rows of the
+    # last sequence see no key (Lk = 0): zero output, -inf LSE, zero dq
+    assert torch.all(dk[130:170] == 0) and torch.all(dv[130:170] == 0)
+    assert torch.all(out[130:] == 0) and torch.all(dq[130:] == 0)
+    assert torch.all(torch.isneginf(lse[:, 130:]))
+
+
+@pytest.mark.parametrize("lengths,bm", [
+    ([200, 312], 128),
+    (W.PACKED_16K_DOC_LENGTHS, 128),
+    ([0, 5, 0, 130, 1, 128, 129, 0], 64),
+    ([131072], 128),
+    (list(range(0, 9000, 97)), 128),
+])
+def test_device_schedule_matches_host(lengths, bm):
+    cu = W.cu_from_lengths(lengths)
+    host = A.attn_varlen_schedule_host(cu, bm)
+    announce(f"schedule decode {len(lengths)} seqs bm={bm}")
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
+    seq, blk = A.attn_varlen_schedule_device(cu_d, max(lengths), bm, len(host) + 5)
+    torch.cuda.synchronize()
+    seq, blk = seq.cpu().tolist(), blk.cpu().tolist()
+    assert list(zip(seq[:len(host)], blk[:len(host)])) == host
+    assert seq[len(host):] == [-1] * 5 and blk[len(host):] == [-1] * 5
+
+
+def test_autograd_wrapper_matches_direct_calls():
+    wl = W.Workload("autograd", [90, 300], 4, 2, 64, True)
+    d = to_dev(W.make_inputs(wl))
+    announce("autograd wrapper")
+    q = d["q"].clone().requires_grad_(True)
+    k = d["k"].clone().requires_grad_(True)
+    v = d["v"].clone().requires_grad_(True)
+    out = A.attn_varlen_func(q, k, v, d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+                             wl.softmax_scale, True)
+    out.backward(d["dout"])
+    o2, l2, dq, dk, dv = _run_all(wl, d)
+    assert torch.equal(out.detach(), o2)
+    assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
