@@ -33,6 +33,10 @@ int check_common(const void* q, const void* k, const void* v, const int32_t* cu_
   // the query heads, 256 threads each) must stay below 2^32 work-items
   const int64_t blocks = (total_q + total_k) / 64 + 2 * (int64_t)num_seqs;
   if (blocks * (int64_t)Hq * 256 >= kMaxGridThreads) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  // K/V rows are addressed with 32-bit buffer offsets relative to a sequence's
+  // first row: one sequence's rows (plus a 64-row tile overrun) must span < 2 GiB
+  if ((int64_t)(max_k + 64) * Hkv * D * 2 >= ((int64_t)1 << 31)) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if ((int64_t)(max_q + 64) * Hq * D * 2 >= ((int64_t)1 << 31)) return ATTN_VARLEN_ERR_BAD_SEQLEN;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
   if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return ATTN_VARLEN_ERR_MISALIGNED;
   if (!std::isfinite(scale)) return ATTN_VARLEN_ERR_BAD_SCALE;

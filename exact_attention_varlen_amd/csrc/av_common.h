@@ -83,11 +83,119 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8&
   lo = as_bf16x8(l);
 }
 
+// c + (sum of the two bf16 halves of w), one v_dot2 against (1, 1).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), c,
+                                         false);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Value of lane (l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// max(x, value of lane l ^ 32) without LDS traffic: v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second, so with
+// both operands x every lane ends up holding its own value and its partner's.
+__device__ __forceinline__ float max_xor32(float x) {
+  const int xi = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const int xi = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// HBM -> LDS staging without VGPRs (buffer_load_dwordx4 ... lds): each lane of a
+// wave moves 16 bytes to LDS address (m0 base + 16 * lane). Loads past the
+// buffer's num_records return zeros, which bounds-checks the sequence tail.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, range-checked against num_bytes).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = (int)num_bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
+// One wave-wide 16-byte-per-lane copy HBM -> LDS at (lds_wave_base + 16 * lane).
+// Written as inline assembly so that the compiler does not treat every later
+// LDS read as aliasing the copy and wait for all copies in flight; the callers
+// order the copies explicitly with wait_vmcnt() and lds_barrier(). The copy
+// writes no VGPR. lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_wave_base, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_wave_base), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  }
+}
+
+// Workgroup barrier that orders LDS accesses without the full memory fence of
+// __syncthreads (which would also wait for every copy in flight). Outstanding
+// LDS reads of this wave complete first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_ld16(const lds_char* p) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Transposing LDS read of 4 bf16 (ds_read_b64_tr_b16). Within each group of 16
+// lanes, result element j of lane i is element (i % 4) of the 8 bytes addressed
+// by lane 4 * j + i / 4: if lane 4j + c of the group addresses row (k0 + j),
+// columns [4c, 4c + 4) of a row-major tile, lane i receives column i of rows
+// k0 .. k0 + 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr4(const lds_char* p) {
+  const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<lds_char*>(p)));
+  return __builtin_bit_cast(uint2, t);
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS tile row (row r of a key tile):
+// chunk c of row r is stored at chunk position c ^ swz(r). It makes the MFMA
+// operand reads conflict-free: 16 consecutive rows read at one chunk hit 16
+// distinct positions, and 4 consecutive rows read at 4 consecutive chunks (the
+// transposed V reads) also hit 16 distinct positions. For head_dim 64 (two rows
+// per 256-byte bank row) the map is chosen per row pair instead.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 64) {
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  } else {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  }
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

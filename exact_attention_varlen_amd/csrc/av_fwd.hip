@@ -10,18 +10,29 @@
 // gfx950 design (one workgroup = 4 waves = one query block of 128 rows of one
 // query head; each wave owns 32 query rows):
 //  * Q^T stays in VGPRs for the whole item as the B operand of S^T = K Q^T.
-//  * Per key tile of 64 keys: K is staged row-major and V transposed into LDS
-//    (16-byte global loads, prefetched into VGPRs one tile ahead).
-//  * S^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16; the key and
-//    head-dim row permutations of av_common.h make the fp32 score registers the
-//    B operand of the PV product after a bf16 conversion, with no shuffles.
-//  * Each lane owns one query column: the running max m, the running sum l and
-//    the rescale factor are per-lane values; the row max needs one exchange with
-//    lane ^ 32 per tile, and the row sum is only combined at the end.
-//  * exp2 with the scale folded in: t = s * (scale * log2 e); the fp32 score is
-//    never rounded to bf16 before the exponent.
+//  * K and V tiles of 64 keys go HBM -> LDS with buffer_load ... lds (no VGPR
+//    staging, out-of-range rows read as zero), double-buffered: the loads of
+//    tile n+1 are in flight while tile n is computed. Rows are stored
+//    row-major with an XOR swizzle of 16-byte chunks (swz<D>).
+//  * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16. V^T comes
+//    from the row-major V tile through transposing LDS reads
+//    (ds_read_b64_tr_b16); the key permutation kperm makes the fp32 score
+//    registers the B operand of the PV product after a bf16 conversion.
+//  * Each lane owns one query column: running max, running sum and rescale
+//    factor are per-lane values; the row max needs one exchange with lane ^ 32
+//    per tile (v_permlane32_swap), the row sum is combined once at the end.
+//  * exp2 with the scale folded into one FMA per score. The running max is
+//    only moved (and O rescaled) when a tile's max exceeds it by more than
+//    kRescaleSlack (in log2 units), so P <= 2^kRescaleSlack and most tiles do
+//    no rescaling; the result is the same softmax, only the reference point of
+//    the exponentials changes. Two row sums are kept: the fp32 sum of P gives
+//    the LSE, and the sum of the bf16-rounded P that enter the PV product
+//    normalises O, so the rounding of P cancels in O's weighted average even
+//    when one key carries almost all of a row's weight.
 //  * Masking code runs only on key tiles that cross the causal diagonal or the
-//    end of the sequence; tiles past the causal range are never visited.
+//    end of the sequence (a separate instantiation of the tile step); tiles
+//    past the causal range are never visited. On masked tiles P is split into
+//    bf16 hi + lo parts so rows with very few visible keys stay accurate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,18 +41,22 @@
 
 namespace av {
 
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
 struct FwdTile {
-  static constexpr int BM = 128;     // query rows per workgroup
-  static constexpr int BN = 64;      // keys per tile
-  static constexpr int NT = 256;     // threads per workgroup
-  static constexpr int KP = D + 8;   // LDS row pitch of the K tile (bf16 elements)
-  static constexpr int VP = BN + 8;  // LDS row pitch of the V^T tile
-  static constexpr int K_CHUNKS = BN * D / 8 / NT;                 // 16-byte K loads per thread
-  static constexpr int V_UNITS = (BN / 4) * (D / 8);               // (4 keys x 16 bytes) units per tile
-  static constexpr int V_ITERS = (V_UNITS + NT - 1) / NT;          // units per thread
-  static constexpr int LDS_ELEMS = BN * KP + D * VP;
-  static constexpr size_t LDS_BYTES = (size_t)LDS_ELEMS * 2;
+  static constexpr int BM = 128;                    // query rows per workgroup
+  static constexpr int BN = 64;                     // keys per tile
+  static constexpr int NT = 256;                    // threads per workgroup
+  static constexpr int ROW = D * 2;                 // bytes per key row in LDS
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int TILE = BN * ROW;             // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;            // K then V
+  static constexpr size_t LDS_BYTES = 2 * STAGE;    // two stages
+  static constexpr int DMA_PER_TILE = TILE / 1024;  // wave-wide 1 KB loads per K (or V) tile
+  static constexpr int DMA_PER_WAVE = 2 * DMA_PER_TILE / 4;
+  static constexpr int ROWS_PER_DMA = 1024 / ROW;
+  static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
 };
 
 struct FwdParams {
@@ -56,87 +71,134 @@ struct FwdParams {
   int total_q;
   int Hq;
   int Hkv;
-  int levels;  // ceil(max_seqlen_q / BM)
-  float scale_log2;  // softmax_scale * log2(e)
+  int levels;        // ceil(max_seqlen_q / BM)
+  float scale_log2;  // |softmax_scale| * log2(e)
+  int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
 };
 
+// Issue this wave's share of the K and V tile loads (keys n0 .. n0+63) into
+// the LDS stage at `stage`.
 template <int D>
-struct KVStage {
-  uint4 k[FwdTile<D>::K_CHUNKS];
-  uint4 v[FwdTile<D>::V_ITERS][4];
-};
-
-// Global -> VGPR loads of key tile starting at key n0 (sequence-relative).
-template <int D>
-__device__ __forceinline__ void kv_load(KVStage<D>& st, const uint16_t* kbase, const uint16_t* vbase, int64_t pitch,
-                                        int n0, int Lk) {
+__device__ __forceinline__ void issue_tile(uint32_t stage, const i32x4& rk, const i32x4& rv, uint32_t pitch, int n0,
+                                           int wave, int lane) {
   using T = FwdTile<D>;
-  const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < T::K_CHUNKS; ++i) {
-    const int c = tid + T::NT * i;
-    const int key = c / (D / 8);
-    const int dc = c % (D / 8);
-    const int kg = n0 + key;
-    st.k[i] = (kg < Lk) ? ld16(kbase + (int64_t)kg * pitch + dc * 8) : zero_u4();
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int qd = wave * T::DMA_PER_WAVE + i;  // which 1 KB block of the stage
+    const bool is_v = qd >= T::DMA_PER_TILE;
+    const int blk = is_v ? qd - T::DMA_PER_TILE : qd;
+    const int row = blk * T::ROWS_PER_DMA + lane / T::CPR;
+    const int pos = lane % T::CPR;
+    const int c = pos ^ swz<D>(row);
+    const uint32_t voff = (uint32_t)(n0 + row) * pitch + (uint32_t)c * 16u;
+    lds_dma16(is_v ? rv : rk, stage + (is_v ? T::TILE : 0) + blk * 1024, voff);
   }
+}
+
+// 32 keys (one half of a key tile) of the online softmax for one wave (32
+// query columns): S^T = K Q^T, running max / sum update, O^T += V^T P^T.
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void fwd_half(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
+                                         float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk,
+                                         int qlim, const uint32_t* koff, const uint32_t* voff0,
+                                         const uint32_t* voff1, int half) {
+  using T = FwdTile<D>;
+  f32x16 s = zero16();
 #pragma unroll
-  for (int i = 0; i < T::V_ITERS; ++i) {
-    const int u = tid + T::NT * i;
-    const int kgrp = u / (D / 8);
-    const int dc = u % (D / 8);
+  for (int kk = 0; kk < D / 16; ++kk) s = mfma32x32x16(as_bf16x8(lds_ld16(Ks + koff[kk])), qf[kk], s);
+  // mask, max over the 32 keys (this lane's 16 and lane ^ 32's 16). Masked
+  // scores are excluded by selects, never by -inf arithmetic, so that any
+  // finite scale (0 included) is safe.
+  float mx = -INFINITY;
+  uint32_t vis_bits = 0xffffu;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kg = n0 + 4 * kgrp + e;
-      st.v[i][e] = (u < T::V_UNITS && kg < Lk) ? ld16(vbase + (int64_t)kg * pitch + dc * 8) : zero_u4();
+  for (int v = 0; v < 16; ++v) {
+    float x = s[v];
+    if (MASK) {
+      const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
+      const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
+      vis_bits = vis ? vis_bits : (vis_bits & ~(1u << v));
+      x = vis ? x : -INFINITY;
+    }
+    mx = fmaxf(mx, x);
+  }
+  mx = max_xor32(mx);
+  const float cand = (mx == -INFINITY) ? -INFINITY : mx * c;
+  if (__ballot(cand > m_ref + kRescaleSlack)) {
+    const float mn = fmaxf(m_ref, cand);
+    // 0 when m_ref = -inf (O and l are still 0); rows that have seen no visible
+    // key yet keep mn = -inf and must not form exp2(-inf - -inf)
+    const float alpha = fast_exp2(m_ref - (mn == -INFINITY ? 0.f : mn));
+    m_ref = mn;
+    l_run *= alpha;
+    l_o *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+  }
+  const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float e = fast_exp2(__builtin_fmaf(s[v], c, -msub));
+    if (MASK) e = ((vis_bits >> v) & 1u) ? e : 0.f;
+    s[v] = e;
+    l_run += e;
+  }
+  // O^T += V^T P^T; V^T operand rows are head-dims (transposing reads)
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] = s[8 * ks + e];
+    bf16x8 pb, pl;
+    if (MASK) {
+      split_bf16x8(pv, pb, pl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l_o += pv[e];
+    } else {
+      uint4 u;
+      u.x = pack_bf16x2(pv[0], pv[1]);
+      u.y = pack_bf16x2(pv[2], pv[3]);
+      u.z = pack_bf16x2(pv[4], pv[5]);
+      u.w = pack_bf16x2(pv[6], pv[7]);
+      l_o = add_bf16x2(u.x, l_o);
+      l_o = add_bf16x2(u.y, l_o);
+      l_o = add_bf16x2(u.z, l_o);
+      l_o = add_bf16x2(u.w, l_o);
+      pb = as_bf16x8(u);
+    }
+    const lds_char* vrow = Vs + 16 * ks * T::ROW;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const uint2 lo = lds_read_tr4(vrow + voff0[db]);
+      const uint2 hi = lds_read_tr4(vrow + voff1[db]);
+      const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      o[db] = mfma32x32x16(va, pb, o[db]);
+      if (MASK) o[db] = mfma32x32x16(va, pl, o[db]);
     }
   }
 }
 
-// VGPR -> LDS: K row-major, V transposed (V^T[d][key], 4 keys per 8-byte write).
-template <int D>
-__device__ __forceinline__ void kv_store(const KVStage<D>& st, uint16_t* Ks, uint16_t* Vt) {
+// One key tile (64 keys = two halves).
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
+                                         float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk,
+                                         int qlim, const uint32_t* koff, const uint32_t* voff0,
+                                         const uint32_t* voff1, int half) {
   using T = FwdTile<D>;
-  const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < T::K_CHUNKS; ++i) {
-    const int c = tid + T::NT * i;
-    const int key = c / (D / 8);
-    const int dc = c % (D / 8);
-    st16(Ks + key * T::KP + dc * 8, st.k[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < T::V_ITERS; ++i) {
-    const int u = tid + T::NT * i;
-    if (u < T::V_UNITS) {
-      const int kgrp = u / (D / 8);
-      const int dc = u % (D / 8);
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&st.v[i][0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&st.v[i][1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&st.v[i][2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&st.v[i][3]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // head-dim 2w (low halves) and 2w+1 (high halves) of the 4 keys
-        uint2 lo, hi;
-        lo.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-        lo.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-        hi.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-        hi.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-        const int d = dc * 8 + 2 * w;
-        *reinterpret_cast<uint2*>(Vt + d * T::VP + 4 * kgrp) = lo;
-        *reinterpret_cast<uint2*>(Vt + (d + 1) * T::VP + 4 * kgrp) = hi;
-      }
-    }
-  }
+  for (int kb = 0; kb < 2; ++kb)
+    fwd_half<D, MASK, CAUSAL>(Ks + kb * 32 * T::ROW, Vs + kb * 32 * T::ROW, qf, o, m_ref, l_run, l_o, c,
+                              n0 + kb * 32, Lk, qlim, koff, voff0, voff1, half);
 }
 
 template <int D, bool CAUSAL, bool WRITE_LSE>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(FwdParams p) {
   using T = FwdTile<D>;
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* Ks = smem;
-  uint16_t* Vt = smem + T::BN * T::KP;
+  lds_char* lds = (lds_char*)smem;
 
   const int r = p.Hq / p.Hkv;
   const int64_t L = xcd_logical(blockIdx.x, r);
@@ -152,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const int Lk = p.cu_k[b + 1] - ck;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -163,143 +225,107 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   int kend = Lk;
   if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
   const int ntiles = ceil_div(kend, T::BN);
-  // keys below kfull are visible to every row of the block (and below Lk)
+  // tiles [0, nfull) need no mask: every key is below Lk and visible to every row
   const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
+  const int nfull = min(ntiles, kfull / T::BN);
 
-  // Q^T operand: 8 consecutive head-dims of this lane's query per k-step.
+  // K / V buffer resources for this (sequence, KV head): rows past Lk read as 0
+  const uint32_t pitch = (uint32_t)p.Hkv * D * 2;
+  const uint32_t nbytes = (Lk > 0) ? (uint32_t)(Lk - 1) * pitch + D * 2 : 0u;
+  const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
+  const i32x4 rk = make_rsrc(p.k + kvoff, nbytes);
+  const i32x4 rv = make_rsrc(p.v + kvoff, nbytes);
+  const uint32_t lds0 = lds_addr(lds);
+
+  if (ntiles > 0) issue_tile<D>(lds0, rk, rv, pitch, 0, wave, lane);
+
+  // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
+  // (sign-flipped when the scale is negative, so the scale applied is positive).
   bf16x8 qf[D / 16];
   {
     const uint16_t* qrow = p.q + ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * half;
+    const uint32_t flip = p.neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = as_bf16x8(qvalid ? ld16(qrow + 16 * kk) : zero_u4());
+    for (int kk = 0; kk < D / 16; ++kk) {
+      uint4 u = qvalid ? ld16(qrow + 16 * kk) : zero_u4();
+      u.x ^= flip;
+      u.y ^= flip;
+      u.z ^= flip;
+      u.w ^= flip;
+      qf[kk] = as_bf16x8(u);
+    }
+  }
+
+  // per-lane LDS byte offsets of the MFMA operand reads (the swizzle depends on
+  // the row mod 16, which is the same for every 32-key half and every tile)
+  uint32_t koff[D / 16];
+  {
+    const int row = kperm(col);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = row * T::ROW + (((2 * kk + half) ^ swz<D>(row)) << 4);
+  }
+  uint32_t voff0[D / 32], voff1[D / 32];
+  {
+    const int grp = lane >> 4;  // 16-lane group: head-dim half (grp & 1) and key half (grp >> 1)
+    const int i = lane & 15;
+    const int j = i >> 2;   // key within the 4-key read
+    const int cc = i & 3;   // 4-column piece
+    const int key0 = 8 * half + j;
+    const int key1 = key0 + 4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int chunk = db * 4 + 2 * (grp & 1) + (cc >> 1);
+      voff0[db] = key0 * T::ROW + ((chunk ^ swz<D>(key0)) << 4) + (cc & 1) * 8;
+      voff1[db] = key1 * T::ROW + ((chunk ^ swz<D>(key1)) << 4) + (cc & 1) * 8;
+    }
   }
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = zero16();
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  const int64_t kvpitch = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + (int64_t)ck * kvpitch + (int64_t)g * D;
-  const uint16_t* vbase = p.v + (int64_t)ck * kvpitch + (int64_t)g * D;
-
-  KVStage<D> st;
-  if (ntiles > 0) {
-    kv_load<D>(st, kbase, vbase, kvpitch, 0, Lk);
-    kv_store<D>(st, Ks, Vt);
-  }
-  __syncthreads();
-
-  const int krow = kperm(col);
-  const int drow = dperm(col);
+  float m_ref = -INFINITY;
+  float l_run = 0.f;  // sum of P (fp32): the LSE
+  float l_o = 0.f;    // sum of the P values as they enter the PV product: normalises O
+  const float c = p.scale_log2;
   const int qlim = qi + (Lk - Lq);  // last visible key of this lane's query (causal)
 
   for (int n = 0; n < ntiles; ++n) {
-    const int n0 = n * T::BN;
-    if (n + 1 < ntiles) kv_load<D>(st, kbase, vbase, kvpitch, n0 + T::BN, Lk);
-
-    // S^T = K Q^T for the two 32-key halves of the tile
-    f32x16 s[T::BN / 32];
-#pragma unroll
-    for (int kb = 0; kb < T::BN / 32; ++kb) {
-      f32x16 acc = zero16();
-      const uint16_t* kr = Ks + (kb * 32 + krow) * T::KP + 8 * half;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) acc = mfma32x32x16(as_bf16x8(ld16(kr + 16 * kk)), qf[kk], acc);
-      s[kb] = acc;
-    }
-
-    // scale, mask, running max
-    const bool need_mask = (n0 + T::BN > kfull);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < T::BN / 32; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float t = s[kb][v] * p.scale_log2;
-        if (need_mask) {
-          const int key = n0 + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-          const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
-          t = vis ? t : -INFINITY;
-        }
-        s[kb][v] = t;
-        mx = fmaxf(mx, t);
-      }
-    }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float base = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - base);
-    m_run = m_new;
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < T::BN / 32; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = fast_exp2(s[kb][v] - base);
-        s[kb][v] = e;
-        lsum += e;
-      }
-    }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-    }
-
-    // O^T += V^T P^T. On masked tiles (the causal diagonal and the sequence
-    // tail, where rows with only a few visible keys live and one P value can
-    // carry most of a row's weight) P is split into bf16 hi + lo parts so that
-    // its rounding does not show in the output.
-#pragma unroll
-    for (int kb = 0; kb < T::BN / 32; ++kb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[kb][8 * ks + e];
-        bf16x8 pb, pl;
-        split_bf16x8(pv, pb, pl);
-        const uint16_t* vr = Vt + drow * T::VP + kb * 32 + 16 * ks + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 va = as_bf16x8(ld16(vr + db * 32 * T::VP));
-          o[db] = mfma32x32x16(va, pb, o[db]);
-          if (need_mask) o[db] = mfma32x32x16(va, pl, o[db]);
-        }
-      }
-    }
-
-    __syncthreads();
+    lds_char* cur = lds + (n & 1) * T::STAGE;
     if (n + 1 < ntiles) {
-      kv_store<D>(st, Ks, Vt);
-      __syncthreads();
+      issue_tile<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
+      wait_vmcnt<T::DMA_PER_WAVE>();  // this wave's copies of tile n have landed
+    } else {
+      wait_vmcnt<0>();
     }
+    lds_barrier();  // ... and every other wave's
+    if (n < nfull)
+      fwd_tile<D, false, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, koff, voff0, voff1,
+                                 half);
+    else
+      fwd_tile<D, true, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, koff, voff0, voff1,
+                                half);
+    lds_barrier();  // stage (n & 1) is free for tile n + 2
   }
 
   // epilogue: O = O / l, LSE = ln(2) * (m + log2 l)
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = add_xor32(l_run);
+  const float lo_tot = add_xor32(l_o);
   if (qvalid) {
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    uint16_t* orow = p.out + ((int64_t)(cq + qi) * p.Hq + h) * D + 16 * half;
+    const float inv = (lo_tot > 0.f) ? 1.f / lo_tot : 0.f;
+    uint16_t* orow = p.out + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      uint4 a, c;
-      a.x = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
-      a.y = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
-      a.z = pack_bf16x2(o[db][4] * inv, o[db][5] * inv);
-      a.w = pack_bf16x2(o[db][6] * inv, o[db][7] * inv);
-      c.x = pack_bf16x2(o[db][8] * inv, o[db][9] * inv);
-      c.y = pack_bf16x2(o[db][10] * inv, o[db][11] * inv);
-      c.z = pack_bf16x2(o[db][12] * inv, o[db][13] * inv);
-      c.w = pack_bf16x2(o[db][14] * inv, o[db][15] * inv);
-      st16(orow + db * 32, a);
-      st16(orow + db * 32 + 8, c);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint2 w;
+        w.x = pack_bf16x2(o[db][4 * gq + 0] * inv, o[db][4 * gq + 1] * inv);
+        w.y = pack_bf16x2(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * gq) = w;
+      }
     }
     if (WRITE_LSE && half == 0) {
-      p.lse[(int64_t)h * p.total_q + cq + qi] = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)h * p.total_q + cq + qi] =
+          (l_tot > 0.f && m_ref != -INFINITY) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -328,7 +354,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.levels = ceil_div(a.max_q, T::BM);
-  p.scale_log2 = a.scale * kLog2e;
+  p.scale_log2 = fabsf(a.scale) * kLog2e;
+  p.neg_scale = a.scale < 0.f ? 1 : 0;
   const int r = a.Hq / a.Hkv;
   const int64_t grid = grid_for(a.total_q, a.num_seqs, T::BM, a.Hq, r);
   if (grid == 0 || p.levels == 0) return hipSuccess;
@@ -350,7 +377,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
   switch (a.D) {
     case 64: return launch_fwd_d<64>(a);
     case 128: return launch_fwd_d<128>(a);
-    case 256: return launch_fwd_d<256>(a);
+    case 256: return launch_fwd_d256(a);
     default: return hipErrorInvalidValue;
   }
 }
