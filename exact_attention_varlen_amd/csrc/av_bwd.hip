@@ -3,70 +3,53 @@
 //
 // The FlashAttention repository guide (Backward Kernels) splits the backward
 // into a preprocess kernel, a main kernel and a postprocess kernel. Here:
-//  1. bwd_delta_kernel   Delta_i = sum_d dO_id * O_id per query row and head
-//                        (fp32), written to the caller's workspace.
-//  2. bwd_dkdv_kernel    key-stationary: a workgroup owns 128 keys of one KV
-//                        head and loops over every query head of that head's
-//                        group and every query block that can see the keys,
-//                        recomputing P from the LSE:
-//                          S = Q K^T, P = exp(S*scale - LSE), dP = dO V^T,
-//                          dS = P * (dP - Delta), dV += P^T dO, dK += dS^T Q.
-//                        The sum over the group's query heads happens in fp32
-//                        registers in a fixed order: no atomics and no scratch.
-//  3. bwd_dq_kernel      query-stationary: a workgroup owns 128 query rows of
-//                        one head and loops over the visible key tiles in
-//                        ascending order: dQ += dS K (fixed order).
-// dQ and dK are scaled by softmax_scale at the end.
+//  1. bwd_prep_kernel   per query row and head: Delta_i = sum_d dO_id * O_id
+//                       (fp32) and the LSE in base 2, lse2_i = lse_i * log2(e)
+//                       (+inf for rows without a visible key, so that
+//                       exp2(s - lse2) is exactly 0 there), into the caller's
+//                       workspace.
+//  2. bwd_dkdv_kernel   key-stationary: a workgroup owns 128 keys of one KV head
+//                       and loops over every query head of that head's group and
+//                       every 64-row query block that can see the keys,
+//                       recomputing P from the LSE:
+//                         S = Q K^T, P = exp2(S * scale * log2 e - lse2),
+//                         dP = dO V^T, dS = P * (dP - Delta),
+//                         dV += P^T dO, dK += dS^T Q.
+//                       The sum over the group's query heads happens in fp32
+//                       registers in a fixed order: no atomics, no scratch.
+//  3. bwd_dq_kernel     query-stationary: a workgroup owns 128 query rows of one
+//                       head and loops over the visible 64-key tiles in
+//                       ascending order: dQ += dS K.
+// dQ and dK are scaled by softmax_scale at the end. Head dim 256 uses the
+// register-staged main kernels of av_bwd_d256.hip after the same preprocess.
 //
-// MFMA lane maps and row permutations are those of av_common.h; the
-// transposed operands (Q^T, dO^T for the key-stationary kernel, K^T for the
-// query-stationary kernel) are written transposed into LDS at staging time.
+// gfx950 mapping (as in the forward): Q/dO tiles (dK/dV kernel) and K/V tiles
+// (dQ kernel) go HBM -> LDS by range-checked buffer-load DMA, double-buffered,
+// XOR-swizzled; the operands that contract over rows (Q^T, dO^T, K^T) are read
+// with ds_read_b64_tr_b16 from the row-major tiles; all products are
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "av_common.h"
 #include "av_launch.h"
+#include "av_tiles.h"
 
 namespace av {
 
+hipError_t launch_bwd_main_d256(const BwdArgs& a);  // av_bwd_d256.hip
+
+// workspace layout: Delta [Hq][total_q] fp32, then lse2 [Hq][total_q] fp32
+static inline size_t ws_plane_bytes(int64_t total_q, int Hq) {
+  const size_t b = (size_t)total_q * (size_t)Hq * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+size_t bwd_workspace_bytes(int64_t total_q, int Hq) { return 2 * ws_plane_bytes(total_q, Hq); }
+
 // ---------------------------------------------------------------------------
-// staging helpers: 4 consecutive rows x 16 bytes per unit
+// 1. preprocess
 // ---------------------------------------------------------------------------
-
-struct Rows4 {
-  uint4 r[4];
-};
-
-__device__ __forceinline__ void rows4_load(Rows4& x, const uint16_t* base, int64_t pitch, int row0, int nvalid,
-                                           int col8) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) x.r[e] = (row0 + e < nvalid) ? ld16(base + (int64_t)(row0 + e) * pitch + col8) : zero_u4();
-}
-
-// rows (row0 .. row0+3) of 8 columns (col8 .. col8+7) -> dst[row][col] row-major
-__device__ __forceinline__ void rows4_store(const Rows4& x, uint16_t* dst, int pitch, int row0, int col8) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) st16(dst + (row0 + e) * pitch + col8, x.r[e]);
-}
-
-// rows (row0 .. row0+3) of 8 columns -> dst[col][row] (transposed), 4 rows per 8-byte write
-__device__ __forceinline__ void rows4_store_t(const Rows4& x, uint16_t* dst, int pitch, int row0, int col8) {
-  const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&x.r[0]);
-  const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&x.r[1]);
-  const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&x.r[2]);
-  const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&x.r[3]);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint2 lo, hi;
-    lo.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-    lo.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-    hi.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-    hi.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-    const int c = col8 + 2 * w;
-    *reinterpret_cast<uint2*>(dst + c * pitch + row0) = lo;
-    *reinterpret_cast<uint2*>(dst + (c + 1) * pitch + row0) = hi;
-  }
-}
 
 __device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
   float acc = 0.f;
@@ -81,14 +64,11 @@ __device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
   return acc;
 }
 
-// ---------------------------------------------------------------------------
-// 1. preprocess
-// ---------------------------------------------------------------------------
-
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ dout,
-                                                        const uint16_t* __restrict__ out, float* __restrict__ delta,
-                                                        int total_q, int Hq) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ dout,
+                                                       const uint16_t* __restrict__ out, const float* __restrict__ lse,
+                                                       float* __restrict__ delta, float* __restrict__ lse2,
+                                                       int total_q, int Hq) {
   constexpr int LPR = D / 8;      // lanes per (row, head)
   constexpr int RPB = 256 / LPR;  // (row, head) pairs per workgroup pass
   const int64_t nrows = (int64_t)total_q * Hq;
@@ -102,22 +82,21 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
     if (sub == 0) {
       const int i = (int)(row / Hq);
       const int h = (int)(row - (int64_t)i * Hq);
-      delta[(int64_t)h * total_q + i] = acc;
+      const int64_t idx = (int64_t)h * total_q + i;
+      delta[idx] = acc;
+      const float l = lse[idx];
+      lse2[idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
   }
 }
-
-// ---------------------------------------------------------------------------
-// common parameters
-// ---------------------------------------------------------------------------
 
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;
   const float* delta;
+  const float* lse2;
   const int32_t* cu_q;
   const int32_t* cu_k;
   uint16_t* dq;
@@ -132,12 +111,16 @@ struct BwdParams {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-// LSE in base 2 for a query row; rows outside the sequence or without any
-// visible key get +inf so that exp2(s - lse2) is exactly 0 there.
-__device__ __forceinline__ float lse_log2(const float* lse, int64_t idx, bool valid) {
-  if (!valid) return INFINITY;
-  const float l = lse[idx];
-  return (l == -INFINITY) ? INFINITY : l * kLog2e;
+// Copy of 64 consecutive fp32 row values (rows row0 .. row0 + 63 of one head's
+// plane) into LDS at `dst`; rows past the sequence read as 0.
+__device__ __forceinline__ void rows64_f32_dma(uint32_t dst, const i32x4& rsrc, int row0, int lane) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(dst), "v"((uint32_t)(row0 + lane) * 4u), "s"(rsrc)
+      : "memory", "m0");
 }
 
 // ---------------------------------------------------------------------------
@@ -145,91 +128,105 @@ __device__ __forceinline__ float lse_log2(const float* lse, int64_t idx, bool va
 // ---------------------------------------------------------------------------
 
 template <int D>
-struct DkdvTile {
+struct DkdvCfg {
+  using QT = RowTile<D, 64>;
   static constexpr int NT = 256;
-  static constexpr int BNK = 128;                  // keys per workgroup (32 per wave)
-  static constexpr int BMQ = (D <= 128) ? 64 : 32; // query rows per step
-  static constexpr int RP = D + 8;                 // row-major pitch (Q, dO)
-  static constexpr int TP = BMQ + 8;               // transposed pitch (Q^T, dO^T)
-  static constexpr int UNITS = (BMQ / 4) * (D / 8);  // Rows4 units per tensor per step
-  static constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread per tensor
-  static constexpr int OFF_DOS = BMQ * RP;
-  static constexpr int OFF_QT = 2 * BMQ * RP;
-  static constexpr int OFF_DOT = 2 * BMQ * RP + D * TP;
-  static constexpr int OFF_F32 = 2 * BMQ * RP + 2 * D * TP;  // in bf16 elements (even)
-  static constexpr size_t LDS_BYTES = (size_t)OFF_F32 * 2 + 2 * BMQ * sizeof(float);
+  static constexpr int BNK = 128;  // keys per workgroup (32 per wave)
+  static constexpr int BMQ = 64;   // query rows per step
+  static constexpr int ROW = QT::ROW;
+  static constexpr int TILE = QT::BYTES;
+  static constexpr int F32 = 2 * TILE;        // lse2[64] then Delta[64]
+  static constexpr int STAGE = 2 * TILE + 512;
+  static constexpr size_t LDS_BYTES = 2 * STAGE;
+  static constexpr int DMA_PER_WAVE = 2 * QT::DMAS / 4;  // Q and dO copies
 };
 
 template <int D>
-struct QdoStage {
-  Rows4 q[DkdvTile<D>::UPT];
-  Rows4 d[DkdvTile<D>::UPT];
-  float lse2;
-  float dlt;
-};
-
-template <int D>
-__device__ __forceinline__ void qdo_load(QdoStage<D>& st, const BwdParams& p, int cq, int Lq, int h, int m0) {
-  using T = DkdvTile<D>;
-  const int tid = threadIdx.x;
-  const int64_t pitch = (int64_t)p.Hq * D;
-  const uint16_t* qb = p.q + (int64_t)(cq + m0) * pitch + (int64_t)h * D;
-  const uint16_t* db = p.dout + (int64_t)(cq + m0) * pitch + (int64_t)h * D;
-  const int nvalid = Lq - m0;
+__device__ __forceinline__ void issue_qdo(uint32_t stage, const i32x4& rq, const i32x4& rdo, const i32x4& rl,
+                                          const i32x4& rd, uint32_t pitch, int m0, int wave, int lane) {
+  using T = DkdvCfg<D>;
 #pragma unroll
-  for (int i = 0; i < T::UPT; ++i) {
-    const int u = tid + T::NT * i;
-    const int rg = u / (D / 8);
-    const int c8 = (u % (D / 8)) * 8;
-    if (u < T::UNITS) {
-      rows4_load(st.q[i], qb, pitch, 4 * rg, nvalid, c8);
-      rows4_load(st.d[i], db, pitch, 4 * rg, nvalid, c8);
-    }
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int qd = wave * T::DMA_PER_WAVE + i;
+    const bool is_do = qd >= T::QT::DMAS;
+    tile_dma<D, 64>(stage + (is_do ? T::TILE : 0), is_do ? rdo : rq, pitch, m0, is_do ? qd - T::QT::DMAS : qd, lane);
   }
-  if (tid < T::BMQ) {
-    const int i = m0 + tid;
-    const bool valid = i < Lq;
-    const int64_t idx = (int64_t)h * p.total_q + cq + i;
-    st.lse2 = lse_log2(p.lse, idx, valid);
-    st.dlt = valid ? p.delta[idx] : 0.f;
-  }
+  if (wave == 0) rows64_f32_dma(stage + T::F32, rl, m0, lane);
+  if (wave == 1) rows64_f32_dma(stage + T::F32 + 256, rd, m0, lane);
 }
 
+// waves 0 and 1 have one more copy per stage in flight than waves 2 and 3
 template <int D>
-__device__ __forceinline__ void qdo_store(const QdoStage<D>& st, uint16_t* smem) {
-  using T = DkdvTile<D>;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void wait_qdo_stage(int wave) {
+  using T = DkdvCfg<D>;
+  if (wave < 2)
+    wait_vmcnt<T::DMA_PER_WAVE + 1>();
+  else
+    wait_vmcnt<T::DMA_PER_WAVE>();
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
+                                          const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
+                                          f32x16* dv, float c, int m0, int klim, const OperandOffsets<D>& off,
+                                          int half) {
+  using T = DkdvCfg<D>;
 #pragma unroll
-  for (int i = 0; i < T::UPT; ++i) {
-    const int u = tid + T::NT * i;
-    const int rg = u / (D / 8);
-    const int c8 = (u % (D / 8)) * 8;
-    if (u < T::UNITS) {
-      rows4_store(st.q[i], smem, T::RP, 4 * rg, c8);
-      rows4_store(st.d[i], smem + T::OFF_DOS, T::RP, 4 * rg, c8);
-      rows4_store_t(st.q[i], smem + T::OFF_QT, T::TP, 4 * rg, c8);
-      rows4_store_t(st.d[i], smem + T::OFF_DOT, T::TP, 4 * rg, c8);
+  for (int qb = 0; qb < T::BMQ / 32; ++qb) {
+    const lds_char* qblk = Qs + qb * 32 * T::ROW;
+    const lds_char* dblk = dOs + qb * 32 * T::ROW;
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mfma32x32x16(as_bf16x8(lds_ld16(qblk + off.row_off[kk])), kf[kk], s);
+      dp = mfma32x32x16(as_bf16x8(lds_ld16(dblk + off.row_off[kk])), vf[kk], dp);
     }
-  }
-  float* f = reinterpret_cast<float*>(smem + T::OFF_F32);
-  if (tid < T::BMQ) {
-    f[tid] = st.lse2;
-    f[T::BMQ + tid] = st.dlt;
+    // register v <-> query qb*32 + 16*(v/8) + 8*half + (v%8) of the step
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int qo = qb * 32 + 16 * hh + 8 * half;
+      const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
+      const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
+      const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
+      const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = 8 * hh + e;
+        float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
+        if (MASK) pe = (m0 + qo + e >= klim) ? pe : 0.f;
+        pv[v] = pe;
+        dsv[v] = pe * (dp[v] - dl[e]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pb = to_bf16x8(pv[8 * ks + 0], pv[8 * ks + 1], pv[8 * ks + 2], pv[8 * ks + 3], pv[8 * ks + 4],
+                                  pv[8 * ks + 5], pv[8 * ks + 6], pv[8 * ks + 7]);
+      const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3],
+                                  dsv[8 * ks + 4], dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
+      const lds_char* qrows = qblk + 16 * ks * T::ROW;
+      const lds_char* drows = dblk + 16 * ks * T::ROW;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dv[db] = mfma32x32x16(tr_operand<D>(drows, off, db), pb, dv[db]);
+        dk[db] = mfma32x32x16(tr_operand<D>(qrows, off, db), sb, dk[db]);
+      }
+    }
   }
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  using T = DkdvTile<D>;
+  using T = DkdvCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
-  const uint16_t* Qs = smem;
-  const uint16_t* dOs = smem + T::OFF_DOS;
-  const uint16_t* Qt = smem + T::OFF_QT;
-  const uint16_t* dOt = smem + T::OFF_DOT;
-  const float* lse2_s = reinterpret_cast<const float*>(smem + T::OFF_F32);
-  const float* dlt_s = lse2_s + T::BMQ;
+  lds_char* lds = (lds_char*)smem;
 
-  // work item: (sequence, key block) ranked by descending work, x KV heads
+  // work item: (sequence, key block) ranked by descending work, x KV heads.
+  // The rank's level counts key blocks from the end of the sequence, so the
+  // blocks seen by the most query rows come first.
   const int64_t L = xcd_logical(blockIdx.x, 1);
   const int rank = (int)(L / p.Hkv);
   const int g = (int)(L % p.Hkv);
@@ -239,17 +236,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int Lq = p.cu_q[b + 1] - cq;
   const int ck = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - ck;
-  const int nblk = ceil_div(Lk, T::BNK) - 1 - lvl;  // the level counts key blocks from the end
-  const int n0 = nblk * T::BNK;
+  const int n0 = (ceil_div(Lk, T::BNK) - 1 - lvl) * T::BNK;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
   const int kj = n0 + wave * 32 + col;  // this lane's key (sequence-relative)
   const bool kvalid = kj < Lk;
   const int r = p.Hq / p.Hkv;
+
+  // query steps that can see a key of this block
+  int mfirst = 0;
+  if (CAUSAL) {
+    mfirst = n0 - (Lk - Lq);
+    mfirst = mfirst < 0 ? 0 : (mfirst > Lq ? Lq : mfirst);
+  }
+  const int sfirst = mfirst / T::BMQ;
+  const int nsteps = ceil_div(Lq, T::BMQ) - sfirst;
+  const int total = (nsteps > 0) ? nsteps * r : 0;
+  // steps whose first row is at or past this bound need no causal mask
+  const int mask_end = CAUSAL ? (n0 + T::BNK - 1) - (Lk - Lq) : 0;
+
+  const uint32_t pitch = (uint32_t)p.Hq * D * 2;
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int it, uint32_t stage) {
+    const int h = g * r + it / nsteps;
+    const int m0 = (sfirst + it % nsteps) * T::BMQ;
+    const int64_t qoff = ((int64_t)cq * p.Hq + h) * D;
+    const i32x4 rq = head_rows_rsrc<D>(p.q + qoff, Lq, pitch);
+    const i32x4 rdo = head_rows_rsrc<D>(p.dout + qoff, Lq, pitch);
+    const int64_t roff = (int64_t)h * p.total_q + cq;
+    const i32x4 rl = make_rsrc(p.lse2 + roff, (uint32_t)Lq * 4u);
+    const i32x4 rd = make_rsrc(p.delta + roff, (uint32_t)Lq * 4u);
+    issue_qdo<D>(stage, rq, rdo, rl, rd, pitch, m0, wave, lane);
+  };
+  if (total > 0) issue(0, lds0);
 
   // K^T and V^T operands (B of S = Q K^T and of dP = dO V^T)
   bf16x8 kf[D / 16], vf[D / 16];
@@ -261,6 +284,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       vf[kk] = as_bf16x8(kvalid ? ld16(p.v + off + 16 * kk) : zero_u4());
     }
   }
+  OperandOffsets<D> off;
+  operand_offsets<D>(off, lane);
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -268,120 +293,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     dk[db] = zero16();
     dv[db] = zero16();
   }
-
-  // query blocks that can see a key of this block
-  int mfirst = 0;
-  if (CAUSAL) {
-    mfirst = n0 - (Lk - Lq);
-    mfirst = mfirst < 0 ? 0 : (mfirst > Lq ? Lq : mfirst);
-  }
-  const int sfirst = mfirst / T::BMQ;
-  const int nsteps = ceil_div(Lq, T::BMQ) - sfirst;
-  const int total = (nsteps > 0) ? nsteps * r : 0;
-
-  const int qrow = kperm(col);
-  const int drow = dperm(col);
-  const int klim = kj - (Lk - Lq);  // queries i >= klim see this lane's key (causal)
-
-  QdoStage<D> st;
-  if (total > 0) {
-    qdo_load<D>(st, p, cq, Lq, g * r, sfirst * T::BMQ);
-    qdo_store<D>(st, smem);
-  }
-  __syncthreads();
+  const float c = p.scale_log2;
+  const int klim = kj - (Lk - Lq);  // query rows i >= klim see this lane's key (causal)
 
   for (int it = 0; it < total; ++it) {
+    const uint32_t cur = lds0 + (it & 1) * T::STAGE;
+    if (it + 1 < total) {
+      issue(it + 1, lds0 + ((it + 1) & 1) * T::STAGE);
+      wait_qdo_stage<D>(wave);
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
     const int m0 = (sfirst + it % nsteps) * T::BMQ;
-    if (it + 1 < total) {
-      const int h1 = g * r + (it + 1) / nsteps;
-      const int m1 = (sfirst + (it + 1) % nsteps) * T::BMQ;
-      qdo_load<D>(st, p, cq, Lq, h1, m1);
-    }
-    const bool need_mask = CAUSAL && (n0 + T::BNK - 1 - m0 > Lk - Lq);
-
-#pragma unroll
-    for (int qb = 0; qb < T::BMQ / 32; ++qb) {
-      f32x16 s = zero16(), dp = zero16();
-      const uint16_t* qr = Qs + (qb * 32 + qrow) * T::RP + 8 * half;
-      const uint16_t* dr = dOs + (qb * 32 + qrow) * T::RP + 8 * half;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32x32x16(as_bf16x8(ld16(qr + 16 * kk)), kf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(ld16(dr + 16 * kk)), vf[kk], dp);
-      }
-      // register v <-> query qb*32 + 16*(v/8) + 8*half + (v%8)
-      float l2[16], dl[16];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int qo = qb * 32 + 16 * hh + 8 * half;
-        const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
-        const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
-        const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
-        const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
-        l2[8 * hh + 0] = a0.x; l2[8 * hh + 1] = a0.y; l2[8 * hh + 2] = a0.z; l2[8 * hh + 3] = a0.w;
-        l2[8 * hh + 4] = a1.x; l2[8 * hh + 5] = a1.y; l2[8 * hh + 6] = a1.z; l2[8 * hh + 7] = a1.w;
-        dl[8 * hh + 0] = b0.x; dl[8 * hh + 1] = b0.y; dl[8 * hh + 2] = b0.z; dl[8 * hh + 3] = b0.w;
-        dl[8 * hh + 4] = b1.x; dl[8 * hh + 5] = b1.y; dl[8 * hh + 6] = b1.z; dl[8 * hh + 7] = b1.w;
-      }
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pe = fast_exp2(s[v] * p.scale_log2 - l2[v]);
-        if (need_mask) {
-          const int qi = m0 + qb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-          pe = (qi >= klim) ? pe : 0.f;
-        }
-        pv[v] = pe;
-        dsv[v] = pe * (dp[v] - dl[v]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pb = to_bf16x8(pv[8 * ks + 0], pv[8 * ks + 1], pv[8 * ks + 2], pv[8 * ks + 3], pv[8 * ks + 4],
-                                    pv[8 * ks + 5], pv[8 * ks + 6], pv[8 * ks + 7]);
-        const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3],
-                                    dsv[8 * ks + 4], dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
-        const int qo = qb * 32 + 16 * ks + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = db * 32 + drow;
-          dv[db] = mfma32x32x16(as_bf16x8(ld16(dOt + d * T::TP + qo)), pb, dv[db]);
-          dk[db] = mfma32x32x16(as_bf16x8(ld16(Qt + d * T::TP + qo)), sb, dk[db]);
-        }
-      }
-    }
-
-    __syncthreads();
-    if (it + 1 < total) {
-      qdo_store<D>(st, smem);
-      __syncthreads();
-    }
+    const lds_char* st = lds + (it & 1) * T::STAGE;
+    const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
+    if (CAUSAL && m0 < mask_end)
+      dkdv_step<D, true>(st, st + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
+    else
+      dkdv_step<D, false>(st, st + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
+    lds_barrier();
+    (void)cur;
   }
 
   if (kvalid) {
-    const int64_t off = ((int64_t)(ck + kj) * p.Hkv + g) * D + 16 * half;
+    const int64_t base = ((int64_t)(ck + kj) * p.Hkv + g) * D + 4 * half;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      uint4 a, c, e, f;
-      a.x = pack_bf16x2(dk[db][0] * p.scale, dk[db][1] * p.scale);
-      a.y = pack_bf16x2(dk[db][2] * p.scale, dk[db][3] * p.scale);
-      a.z = pack_bf16x2(dk[db][4] * p.scale, dk[db][5] * p.scale);
-      a.w = pack_bf16x2(dk[db][6] * p.scale, dk[db][7] * p.scale);
-      c.x = pack_bf16x2(dk[db][8] * p.scale, dk[db][9] * p.scale);
-      c.y = pack_bf16x2(dk[db][10] * p.scale, dk[db][11] * p.scale);
-      c.z = pack_bf16x2(dk[db][12] * p.scale, dk[db][13] * p.scale);
-      c.w = pack_bf16x2(dk[db][14] * p.scale, dk[db][15] * p.scale);
-      e.x = pack_bf16x2(dv[db][0], dv[db][1]);
-      e.y = pack_bf16x2(dv[db][2], dv[db][3]);
-      e.z = pack_bf16x2(dv[db][4], dv[db][5]);
-      e.w = pack_bf16x2(dv[db][6], dv[db][7]);
-      f.x = pack_bf16x2(dv[db][8], dv[db][9]);
-      f.y = pack_bf16x2(dv[db][10], dv[db][11]);
-      f.z = pack_bf16x2(dv[db][12], dv[db][13]);
-      f.w = pack_bf16x2(dv[db][14], dv[db][15]);
-      st16(p.dk + off + db * 32, a);
-      st16(p.dk + off + db * 32 + 8, c);
-      st16(p.dv + off + db * 32, e);
-      st16(p.dv + off + db * 32 + 8, f);
+      store_acc_row(p.dk + base + db * 32, dk[db], p.scale);
+      store_acc_row(p.dv + base + db * 32, dv[db], 1.f);
     }
   }
 }
@@ -391,74 +331,68 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 
 template <int D>
-struct DqTile {
+struct DqCfg {
+  using KV = RowTile<D, 64>;
   static constexpr int NT = 256;
-  static constexpr int BM = 128;   // query rows per workgroup (32 per wave)
-  static constexpr int BN = 64;    // keys per tile
-  static constexpr int RP = D + 8;
-  static constexpr int TP = BN + 8;
-  static constexpr int K_UNITS = (BN / 4) * (D / 8);
-  static constexpr int K_UPT = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_CHUNKS = BN * D / 8 / NT;
-  static constexpr int OFF_VS = BN * RP;
-  static constexpr int OFF_KT = 2 * BN * RP;
-  static constexpr size_t LDS_BYTES = (size_t)(2 * BN * RP + D * TP) * 2;
+  static constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+  static constexpr int BN = 64;   // keys per tile
+  static constexpr int ROW = KV::ROW;
+  static constexpr int TILE = KV::BYTES;
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr size_t LDS_BYTES = 2 * STAGE;
+  static constexpr int DMA_PER_WAVE = 2 * KV::DMAS / 4;
+  static constexpr int WAVES_PER_SIMD = (D <= 64) ? 2 : 1;
 };
 
 template <int D>
-struct KvdStage {
-  Rows4 k[DqTile<D>::K_UPT];
-  uint4 v[DqTile<D>::V_CHUNKS];
-};
-
-template <int D>
-__device__ __forceinline__ void kvd_load(KvdStage<D>& st, const uint16_t* kbase, const uint16_t* vbase,
-                                         int64_t pitch, int n0, int Lk) {
-  using T = DqTile<D>;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void issue_kv_dq(uint32_t stage, const i32x4& rk, const i32x4& rv, uint32_t pitch, int n0,
+                                           int wave, int lane) {
+  using T = DqCfg<D>;
 #pragma unroll
-  for (int i = 0; i < T::K_UPT; ++i) {
-    const int u = tid + T::NT * i;
-    if (u < T::K_UNITS) rows4_load(st.k[i], kbase + (int64_t)n0 * pitch, pitch, 4 * (u / (D / 8)), Lk - n0,
-                                   (u % (D / 8)) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < T::V_CHUNKS; ++i) {
-    const int c = tid + T::NT * i;
-    const int key = c / (D / 8);
-    const int kg = n0 + key;
-    st.v[i] = (kg < Lk) ? ld16(vbase + (int64_t)kg * pitch + (c % (D / 8)) * 8) : zero_u4();
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int qd = wave * T::DMA_PER_WAVE + i;
+    const bool is_v = qd >= T::KV::DMAS;
+    tile_dma<D, 64>(stage + (is_v ? T::TILE : 0), is_v ? rv : rk, pitch, n0, is_v ? qd - T::KV::DMAS : qd, lane);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void kvd_store(const KvdStage<D>& st, uint16_t* smem) {
-  using T = DqTile<D>;
-  const int tid = threadIdx.x;
+template <int D, bool MASK, bool CAUSAL>
+__device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, const bf16x8* df,
+                                        f32x16* dq, float c, float lse2, float dlt, int n0, int Lk, int qlim,
+                                        const OperandOffsets<D>& off, int half) {
+  using T = DqCfg<D>;
+  f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-  for (int i = 0; i < T::K_UPT; ++i) {
-    const int u = tid + T::NT * i;
-    if (u < T::K_UNITS) {
-      const int rg = u / (D / 8);
-      const int c8 = (u % (D / 8)) * 8;
-      rows4_store(st.k[i], smem, T::RP, 4 * rg, c8);
-      rows4_store_t(st.k[i], smem + T::OFF_KT, T::TP, 4 * rg, c8);
+  for (int kk = 0; kk < D / 16; ++kk) {
+    s = mfma32x32x16(as_bf16x8(lds_ld16(Ks + off.row_off[kk])), qf[kk], s);
+    dp = mfma32x32x16(as_bf16x8(lds_ld16(Vs + off.row_off[kk])), df[kk], dp);
+  }
+  float dsv[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float pe = fast_exp2(__builtin_fmaf(s[v], c, -lse2));
+    if (MASK) {
+      const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
+      const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
+      pe = vis ? pe : 0.f;
     }
+    dsv[v] = pe * (dp[v] - dlt);
   }
 #pragma unroll
-  for (int i = 0; i < T::V_CHUNKS; ++i) {
-    const int c = tid + T::NT * i;
-    st16(smem + T::OFF_VS + (c / (D / 8)) * T::RP + (c % (D / 8)) * 8, st.v[i]);
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3], dsv[8 * ks + 4],
+                                dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
+    const lds_char* krows = Ks + 16 * ks * T::ROW;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(tr_operand<D>(krows, off, db), sb, dq[db]);
   }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  using T = DqTile<D>;
+__global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(BwdParams p) {
+  using T = DqCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
-  const uint16_t* Ks = smem;
-  const uint16_t* Vs = smem + T::OFF_VS;
-  const uint16_t* Kt = smem + T::OFF_KT;
+  lds_char* lds = (lds_char*)smem;
 
   const int r = p.Hq / p.Hkv;
   const int64_t L = xcd_logical(blockIdx.x, r);
@@ -473,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int Lk = p.cu_k[b + 1] - ck;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -485,6 +419,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
   const int ntiles = ceil_div(kend, T::BN);
   const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
+  const int nfull = min(ntiles, kfull / T::BN);
+
+  const uint32_t pitch = (uint32_t)p.Hkv * D * 2;
+  const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
+  const i32x4 rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
+  const i32x4 rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
+  const uint32_t lds0 = lds_addr(lds);
+  if (ntiles > 0) issue_kv_dq<D>(lds0, rk, rv, pitch, 0, wave, lane);
 
   bf16x8 qf[D / 16], df[D / 16];
   {
@@ -496,87 +438,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     }
   }
   const int64_t lidx = (int64_t)h * p.total_q + cq + qi;
-  const float lse2 = lse_log2(p.lse, lidx, qvalid);
+  const float lse2 = qvalid ? p.lse2[lidx] : INFINITY;
   const float dlt = qvalid ? p.delta[lidx] : 0.f;
+  OperandOffsets<D> off;
+  operand_offsets<D>(off, lane);
 
   f32x16 dq[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = zero16();
-
-  const int64_t kvpitch = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + (int64_t)ck * kvpitch + (int64_t)g * D;
-  const uint16_t* vbase = p.v + (int64_t)ck * kvpitch + (int64_t)g * D;
-
-  KvdStage<D> st;
-  if (ntiles > 0) {
-    kvd_load<D>(st, kbase, vbase, kvpitch, 0, Lk);
-    kvd_store<D>(st, smem);
-  }
-  __syncthreads();
-
-  const int krow = kperm(col);
-  const int drow = dperm(col);
+  const float c = p.scale_log2;
   const int qlim = qi + (Lk - Lq);
 
   for (int n = 0; n < ntiles; ++n) {
-    const int n0 = n * T::BN;
-    if (n + 1 < ntiles) kvd_load<D>(st, kbase, vbase, kvpitch, n0 + T::BN, Lk);
-    const bool need_mask = (n0 + T::BN > kfull);
-
-#pragma unroll
-    for (int kb = 0; kb < T::BN / 32; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
-      const uint16_t* kr = Ks + (kb * 32 + krow) * T::RP + 8 * half;
-      const uint16_t* vr = Vs + (kb * 32 + krow) * T::RP + 8 * half;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32x32x16(as_bf16x8(ld16(kr + 16 * kk)), qf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(ld16(vr + 16 * kk)), df[kk], dp);
-      }
-      float dsv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pe = fast_exp2(s[v] * p.scale_log2 - lse2);
-        if (need_mask) {
-          const int key = n0 + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-          const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
-          pe = vis ? pe : 0.f;
-        }
-        dsv[v] = pe * (dp[v] - dlt);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3],
-                                    dsv[8 * ks + 4], dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
-        const uint16_t* kt = Kt + drow * T::TP + kb * 32 + 16 * ks + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(as_bf16x8(ld16(kt + db * 32 * T::TP)), sb, dq[db]);
-      }
-    }
-
-    __syncthreads();
     if (n + 1 < ntiles) {
-      kvd_store<D>(st, smem);
-      __syncthreads();
+      issue_kv_dq<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
+      wait_vmcnt<T::DMA_PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
     }
+    lds_barrier();
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const lds_char* Ks = cur + kb * 32 * T::ROW;
+      const lds_char* Vs = cur + T::TILE + kb * 32 * T::ROW;
+      if (n < nfull)
+        dq_half<D, false, CAUSAL>(Ks, Vs, qf, df, dq, c, lse2, dlt, n * T::BN + kb * 32, Lk, qlim, off, half);
+      else
+        dq_half<D, true, CAUSAL>(Ks, Vs, qf, df, dq, c, lse2, dlt, n * T::BN + kb * 32, Lk, qlim, off, half);
+    }
+    lds_barrier();
   }
 
   if (qvalid) {
-    uint16_t* row = p.dq + ((int64_t)(cq + qi) * p.Hq + h) * D + 16 * half;
+    uint16_t* row = p.dq + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * half;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      uint4 a, c;
-      a.x = pack_bf16x2(dq[db][0] * p.scale, dq[db][1] * p.scale);
-      a.y = pack_bf16x2(dq[db][2] * p.scale, dq[db][3] * p.scale);
-      a.z = pack_bf16x2(dq[db][4] * p.scale, dq[db][5] * p.scale);
-      a.w = pack_bf16x2(dq[db][6] * p.scale, dq[db][7] * p.scale);
-      c.x = pack_bf16x2(dq[db][8] * p.scale, dq[db][9] * p.scale);
-      c.y = pack_bf16x2(dq[db][10] * p.scale, dq[db][11] * p.scale);
-      c.z = pack_bf16x2(dq[db][12] * p.scale, dq[db][13] * p.scale);
-      c.w = pack_bf16x2(dq[db][14] * p.scale, dq[db][15] * p.scale);
-      st16(row + db * 32, a);
-      st16(row + db * 32 + 8, c);
-    }
+    for (int db = 0; db < D / 32; ++db) store_acc_row(row + db * 32, dq[db], p.scale);
   }
 }
 
@@ -593,8 +490,24 @@ static hipError_t set_lds_limit(K kern, size_t bytes, bool& done) {
   return e;
 }
 
+template <int D>
+static hipError_t launch_prep(const BwdArgs& a, float* delta, float* lse2) {
+  const FwdArgs& f = a.f;
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = f.total_q * f.Hq;
+  int64_t grid = (rows + RPB - 1) / RPB;
+  if (grid > 4096) grid = 4096;
+  hipStream_t stream = (hipStream_t)f.stream;
+  prof_begin("attn_bwd_prep", stream);
+  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.out), a.lse, delta, lse2,
+                     (int)f.total_q, f.Hq);
+  prof_end(stream);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a) {
+static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
   BwdParams p;
@@ -602,8 +515,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   p.k = static_cast<const uint16_t*>(f.k);
   p.v = static_cast<const uint16_t*>(f.v);
   p.dout = static_cast<const uint16_t*>(a.dout);
-  p.lse = a.lse;
   p.delta = a.delta;
+  p.lse2 = lse2;
   p.cu_q = f.cu_q;
   p.cu_k = f.cu_k;
   p.dq = static_cast<uint16_t*>(a.dq);
@@ -616,24 +529,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
 
-  // 1. Delta
-  if (f.total_q > 0) {
-    constexpr int RPB = 256 / (D / 8);
-    const int64_t rows = f.total_q * f.Hq;
-    int64_t grid = (rows + RPB - 1) / RPB;
-    if (grid > 4096) grid = 4096;
-    prof_begin("attn_bwd_delta", stream);
-    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.out), a.delta,
-                       (int)f.total_q, f.Hq);
-    prof_end(stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-
-  // 2. dK, dV
   if (f.total_k > 0) {
-    using T = DkdvTile<D>;
+    using T = DkdvCfg<D>;
     auto kern = bwd_dkdv_kernel<D, CAUSAL>;
     static bool done = false;
     hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
@@ -649,10 +546,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
       if (e != hipSuccess) return e;
     }
   }
-
-  // 3. dQ
   if (f.total_q > 0) {
-    using T = DqTile<D>;
+    using T = DqCfg<D>;
     auto kern = bwd_dq_kernel<D, CAUSAL>;
     static bool done = false;
     hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
@@ -673,7 +568,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
 
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
-  return a.f.causal ? launch_bwd_t<D, true>(a) : launch_bwd_t<D, false>(a);
+  float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(a.delta) + ws_plane_bytes(a.f.total_q, a.f.Hq));
+  if (a.f.total_q > 0) {
+    const hipError_t e = launch_prep<D>(a, a.delta, lse2);
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (D == 256) {
+    return launch_bwd_main_d256(a);
+  } else {
+    return a.f.causal ? launch_bwd_t<D, true>(a, lse2) : launch_bwd_t<D, false>(a, lse2);
+  }
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
@@ -683,11 +587,6 @@ hipError_t launch_bwd(const BwdArgs& a) {
     case 256: return launch_bwd_d<256>(a);
     default: return hipErrorInvalidValue;
   }
-}
-
-size_t bwd_workspace_bytes(int64_t total_q, int Hq) {
-  const size_t bytes = (size_t)total_q * (size_t)Hq * sizeof(float);
-  return (bytes + 255) / 256 * 256;
 }
 
 // ---------------------------------------------------------------------------

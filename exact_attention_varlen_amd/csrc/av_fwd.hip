@@ -38,6 +38,7 @@
 
 #include "av_common.h"
 #include "av_launch.h"
+#include "av_tiles.h"
 
 namespace av {
 
@@ -45,17 +46,15 @@ constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
 struct FwdTile {
-  static constexpr int BM = 128;                    // query rows per workgroup
-  static constexpr int BN = 64;                     // keys per tile
-  static constexpr int NT = 256;                    // threads per workgroup
-  static constexpr int ROW = D * 2;                 // bytes per key row in LDS
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int TILE = BN * ROW;             // bytes of one K or V tile
-  static constexpr int STAGE = 2 * TILE;            // K then V
-  static constexpr size_t LDS_BYTES = 2 * STAGE;    // two stages
-  static constexpr int DMA_PER_TILE = TILE / 1024;  // wave-wide 1 KB loads per K (or V) tile
-  static constexpr int DMA_PER_WAVE = 2 * DMA_PER_TILE / 4;
-  static constexpr int ROWS_PER_DMA = 1024 / ROW;
+  using KV = RowTile<D, 64>;
+  static constexpr int BM = 128;                      // query rows per workgroup
+  static constexpr int BN = 64;                       // keys per tile
+  static constexpr int NT = 256;                      // threads per workgroup
+  static constexpr int ROW = KV::ROW;                 // bytes per key row in LDS
+  static constexpr int TILE = KV::BYTES;              // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;              // K then V
+  static constexpr size_t LDS_BYTES = 2 * STAGE;      // two stages
+  static constexpr int DMA_PER_WAVE = 2 * KV::DMAS / 4;
   static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
 };
 
@@ -76,22 +75,17 @@ struct FwdParams {
   int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
 };
 
-// Issue this wave's share of the K and V tile loads (keys n0 .. n0+63) into
-// the LDS stage at `stage`.
+// Issue this wave's share of the K and V tile copies (keys n0 .. n0+63) into
+// the LDS stage at byte address `stage`.
 template <int D>
-__device__ __forceinline__ void issue_tile(uint32_t stage, const i32x4& rk, const i32x4& rv, uint32_t pitch, int n0,
-                                           int wave, int lane) {
+__device__ __forceinline__ void issue_kv(uint32_t stage, const i32x4& rk, const i32x4& rv, uint32_t pitch, int n0,
+                                        int wave, int lane) {
   using T = FwdTile<D>;
 #pragma unroll
   for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-    const int qd = wave * T::DMA_PER_WAVE + i;  // which 1 KB block of the stage
-    const bool is_v = qd >= T::DMA_PER_TILE;
-    const int blk = is_v ? qd - T::DMA_PER_TILE : qd;
-    const int row = blk * T::ROWS_PER_DMA + lane / T::CPR;
-    const int pos = lane % T::CPR;
-    const int c = pos ^ swz<D>(row);
-    const uint32_t voff = (uint32_t)(n0 + row) * pitch + (uint32_t)c * 16u;
-    lds_dma16(is_v ? rv : rk, stage + (is_v ? T::TILE : 0) + blk * 1024, voff);
+    const int qd = wave * T::DMA_PER_WAVE + i;  // which 1 KB copy of the stage
+    const bool is_v = qd >= T::KV::DMAS;
+    tile_dma<D, 64>(stage + (is_v ? T::TILE : 0), is_v ? rv : rk, pitch, n0, is_v ? qd - T::KV::DMAS : qd, lane);
   }
 }
 
@@ -100,12 +94,10 @@ __device__ __forceinline__ void issue_tile(uint32_t stage, const i32x4& rk, cons
 template <int D, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void fwd_half(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
                                          float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk,
-                                         int qlim, const uint32_t* koff, const uint32_t* voff0,
-                                         const uint32_t* voff1, int half) {
-  using T = FwdTile<D>;
+                                         int qlim, const OperandOffsets<D>& off, int half) {
   f32x16 s = zero16();
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) s = mfma32x32x16(as_bf16x8(lds_ld16(Ks + koff[kk])), qf[kk], s);
+  for (int kk = 0; kk < D / 16; ++kk) s = mfma32x32x16(as_bf16x8(lds_ld16(Ks + off.row_off[kk])), qf[kk], s);
   // mask, max over the 32 keys (this lane's 16 and lane ^ 32's 16). Masked
   // scores are excluded by selects, never by -inf arithmetic, so that any
   // finite scale (0 included) is safe.
@@ -169,12 +161,10 @@ __device__ __forceinline__ void fwd_half(const lds_char* Ks, const lds_char* Vs,
       l_o = add_bf16x2(u.w, l_o);
       pb = as_bf16x8(u);
     }
-    const lds_char* vrow = Vs + 16 * ks * T::ROW;
+    const lds_char* vrow = Vs + 16 * ks * FwdTile<D>::ROW;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint2 lo = lds_read_tr4(vrow + voff0[db]);
-      const uint2 hi = lds_read_tr4(vrow + voff1[db]);
-      const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const bf16x8 va = tr_operand<D>(vrow, off, db);
       o[db] = mfma32x32x16(va, pb, o[db]);
       if (MASK) o[db] = mfma32x32x16(va, pl, o[db]);
     }
@@ -185,13 +175,12 @@ __device__ __forceinline__ void fwd_half(const lds_char* Ks, const lds_char* Vs,
 template <int D, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
                                          float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk,
-                                         int qlim, const uint32_t* koff, const uint32_t* voff0,
-                                         const uint32_t* voff1, int half) {
+                                         int qlim, const OperandOffsets<D>& off, int half) {
   using T = FwdTile<D>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
     fwd_half<D, MASK, CAUSAL>(Ks + kb * 32 * T::ROW, Vs + kb * 32 * T::ROW, qf, o, m_ref, l_run, l_o, c,
-                              n0 + kb * 32, Lk, qlim, koff, voff0, voff1, half);
+                              n0 + kb * 32, Lk, qlim, off, half);
 }
 
 template <int D, bool CAUSAL, bool WRITE_LSE>
@@ -231,13 +220,12 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
 
   // K / V buffer resources for this (sequence, KV head): rows past Lk read as 0
   const uint32_t pitch = (uint32_t)p.Hkv * D * 2;
-  const uint32_t nbytes = (Lk > 0) ? (uint32_t)(Lk - 1) * pitch + D * 2 : 0u;
   const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
-  const i32x4 rk = make_rsrc(p.k + kvoff, nbytes);
-  const i32x4 rv = make_rsrc(p.v + kvoff, nbytes);
+  const i32x4 rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
+  const i32x4 rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
   const uint32_t lds0 = lds_addr(lds);
 
-  if (ntiles > 0) issue_tile<D>(lds0, rk, rv, pitch, 0, wave, lane);
+  if (ntiles > 0) issue_kv<D>(lds0, rk, rv, pitch, 0, wave, lane);
 
   // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
   // (sign-flipped when the scale is negative, so the scale applied is positive).
@@ -256,29 +244,9 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
     }
   }
 
-  // per-lane LDS byte offsets of the MFMA operand reads (the swizzle depends on
-  // the row mod 16, which is the same for every 32-key half and every tile)
-  uint32_t koff[D / 16];
-  {
-    const int row = kperm(col);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) koff[kk] = row * T::ROW + (((2 * kk + half) ^ swz<D>(row)) << 4);
-  }
-  uint32_t voff0[D / 32], voff1[D / 32];
-  {
-    const int grp = lane >> 4;  // 16-lane group: head-dim half (grp & 1) and key half (grp >> 1)
-    const int i = lane & 15;
-    const int j = i >> 2;   // key within the 4-key read
-    const int cc = i & 3;   // 4-column piece
-    const int key0 = 8 * half + j;
-    const int key1 = key0 + 4;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int chunk = db * 4 + 2 * (grp & 1) + (cc >> 1);
-      voff0[db] = key0 * T::ROW + ((chunk ^ swz<D>(key0)) << 4) + (cc & 1) * 8;
-      voff1[db] = key1 * T::ROW + ((chunk ^ swz<D>(key1)) << 4) + (cc & 1) * 8;
-    }
-  }
+  // per-lane LDS byte offsets of the MFMA operand reads
+  OperandOffsets<D> off;
+  operand_offsets<D>(off, lane);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -292,18 +260,16 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
   for (int n = 0; n < ntiles; ++n) {
     lds_char* cur = lds + (n & 1) * T::STAGE;
     if (n + 1 < ntiles) {
-      issue_tile<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
+      issue_kv<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
       wait_vmcnt<T::DMA_PER_WAVE>();  // this wave's copies of tile n have landed
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();  // ... and every other wave's
     if (n < nfull)
-      fwd_tile<D, false, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, koff, voff0, voff1,
-                                 half);
+      fwd_tile<D, false, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
     else
-      fwd_tile<D, true, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, koff, voff0, voff1,
-                                half);
+      fwd_tile<D, true, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
     lds_barrier();  // stage (n & 1) is free for tile n + 2
   }
 
@@ -314,15 +280,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
     const float inv = (lo_tot > 0.f) ? 1.f / lo_tot : 0.f;
     uint16_t* orow = p.out + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * half;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        uint2 w;
-        w.x = pack_bf16x2(o[db][4 * gq + 0] * inv, o[db][4 * gq + 1] * inv);
-        w.y = pack_bf16x2(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * gq) = w;
-      }
-    }
+    for (int db = 0; db < D / 32; ++db) store_acc_row(orow + db * 32, o[db], inv);
     if (WRITE_LSE && half == 0) {
       p.lse[(int64_t)h * p.total_q + cq + qi] =
           (l_tot > 0.f && m_ref != -INFINITY) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
