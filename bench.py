@@ -62,10 +62,38 @@ def kernel_bytes(name: str, wl) -> float:
     rows = 4 * tq * hq
     return {
         "attn_fwd": q + 2 * kv + q + rows,
-        "attn_bwd_delta": 2 * q + rows,
+        "attn_bwd_prep": 2 * q + 3 * rows,
         "attn_bwd_dkdv": 2 * q + 2 * kv + 2 * rows + 2 * kv,
         "attn_bwd_dq": 2 * q + 2 * kv + 2 * rows + q,
     }.get(name, 0.0)
+
+
+# library event name -> kernel symbol stem used in the profiler summaries
+KERNEL_SYMBOL = {"attn_fwd": "fwd_kernel", "attn_bwd_prep": "bwd_prep_kernel", "attn_bwd_dkdv": "bwd_dkdv_kernel",
+                 "attn_bwd_dq": "bwd_dq_kernel"}
+
+
+def measured_traffic(kernel: str, workload_tag: str):
+    """HBM bytes per launch (read + write) of `kernel` from the committed
+    FETCH_SIZE / WRITE_SIZE summary in profiles/, only if that summary was taken
+    with the library binary loaded now; otherwise None."""
+    import hashlib
+
+    import exact_attention_varlen_amd._lib as L
+
+    path = os.path.join(ROOT, "profiles", f"attn_kernels_{workload_tag}_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(L.LIB_PATH, "rb").read()).hexdigest()
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+            if rec.get("lib_sha256") != sha:
+                return None
+            k = rec["kernels"].get(KERNEL_SYMBOL.get(kernel, ""))
+            return None if k is None else k["read_bytes"] + k["write_bytes"]
+    return None
 
 
 def time_steps(fn, steps: int, warmup: int):
@@ -85,6 +113,24 @@ def time_steps(fn, steps: int, warmup: int):
     wall = (time.perf_counter() - t0) * 1e3 / max(1, steps)
     per = [s.elapsed_time(e) for s, e in evs]
     return wall, per
+
+
+def time_graph(fn, steps: int, warmup: int):
+    """Capture fn into a HIP graph (after eager warm-up) and time `steps` replays.
+
+    Returns (ms per replay over the bracketed region, per-replay event ms)."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return time_steps(g.replay, steps, warmup)
 
 
 def run_workload(wl, steps, warmup, profile=True):
@@ -115,23 +161,27 @@ def run_workload(wl, steps, warmup, profile=True):
                           wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     res = {}
-    fwd_ms, fwd_per = time_steps(fwd, steps, warmup)
+    fwd_flop = wl.accounted_fwd_flop()
+    # 1) eager calls with per-launch event timing inside the library
     if profile:
         A.attn_varlen_profile_enable(True)
-    step_ms, step_per = time_steps(step, steps, warmup)
+    eager_step_ms, _ = time_steps(step, steps, warmup)
     recs = []
     if profile:
         A.attn_varlen_profile_enable(False)
         recs = A.attn_varlen_profile_records()
-    fwd_flop = wl.accounted_fwd_flop()
+    # 2) the same work replayed from HIP graphs: no host launch overhead
+    fwd_ms, fwd_per = time_graph(fwd, steps, warmup)
+    step_ms, step_per = time_graph(step, steps, warmup)
     res["fwd_ms"] = fwd_ms
     res["fwd_ms_median"] = statistics.median(fwd_per)
     res["fwd_tflops"] = fwd_flop / (fwd_ms * 1e-3) / 1e12
     res["step_ms"] = step_ms
     res["step_ms_median"] = statistics.median(step_per)
     res["fwdbwd_tflops"] = 3.5 * fwd_flop / (step_ms * 1e-3) / 1e12
-    # per-kernel averages over the timed steps (the warm-up launches are not recorded
-    # because warm-up runs before the session starts... they are: drop the first `warmup`)
+    res["eager_step_ms"] = eager_step_ms
+    # per-kernel averages over the timed eager steps (the session also saw the
+    # warm-up steps: drop their launches)
     per_kernel = {}
     if recs:
         n_per_step = len(recs) // (steps + warmup)
@@ -196,6 +246,41 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     }
 
 
+def eager_only(wl, steps: int, warmup: int):
+    """warmup + steps eager forward+backward steps, no graphs and no extra timing
+    machinery: the command profilers wrap."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+    for i in range(warmup + steps):
+        out, lse = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                                     wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=True)
+        A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                          wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": wl.name, "eager_steps": warmup + steps}), flush=True)
+    return 0
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device copy of known size, for scaling the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) of a profiler run: each launch reads and writes
+    `nbytes`."""
+    import torch
+
+    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,7 +288,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the extra workloads")
-    ap.add_argument("--workload", default="packed16k", help="packed16k (default) or any name in workloads")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="only run warmup + steps eager fwd+bwd steps of the main workload (for profilers) and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this attention path has no multi-GPU mode",
@@ -216,6 +304,10 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if a.copy_calibration:
+        return copy_calibration()
+    if a.eager_only:
+        return eager_only(W.packed_16k(), a.steps, a.warmup)
     primary = W.packed_16k()
     log(f"device {torch.cuda.get_device_name(0)}; warming up")
     warm_gpu(1.0)
@@ -244,7 +336,8 @@ def main(argv=None):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": flop / (dom_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "traffic": None,
+        "traffic": measured_traffic(dom, "packed16k-causal-d128"),
+        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "avg_ms": dom_ms,
         "flop_per_launch": flop,
     }
@@ -272,6 +365,8 @@ def main(argv=None):
         "frac_of_peak_fwdbwd": res["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
         "step_ms_median": res["step_ms_median"],
         "fwd_ms_median": res["fwd_ms_median"],
+        "eager_step_ms": res["eager_step_ms"],
+        "timing": "HIP graph replay per step (value); per-kernel times from eager steps with library events",
         "kernels": kern,
         "roofline": roofline,
         "secondary": secondary,
