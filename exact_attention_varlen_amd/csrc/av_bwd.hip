@@ -181,32 +181,28 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
       s = mfma32x32x16(as_bf16x8(lds_ld16(qblk + off.row_off[kk])), kf[kk], s);
       dp = mfma32x32x16(as_bf16x8(lds_ld16(dblk + off.row_off[kk])), vf[kk], dp);
     }
-    // register v <-> query qb*32 + 16*(v/8) + 8*half + (v%8) of the step
-    float pv[16], dsv[16];
+    // register v <-> query qb*32 + 16*(v/8) + 8*half + (v%8) of the step; the
+    // 8 registers of k-step ks are the 8 consecutive queries 16 ks + 8 half + e
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int qo = qb * 32 + 16 * hh + 8 * half;
+    for (int ks = 0; ks < 2; ++ks) {
+      const int qo = qb * 32 + 16 * ks + 8 * half;
       const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
       const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
       const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
       const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
       const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float pv[8], dsv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int v = 8 * hh + e;
+        const int v = 8 * ks + e;
         float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
         if (MASK) pe = (m0 + qo + e >= klim) ? pe : 0.f;
-        pv[v] = pe;
-        dsv[v] = pe * (dp[v] - dl[e]);
+        pv[e] = pe;
+        dsv[e] = pe * (dp[v] - dl[e]);
       }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = to_bf16x8(pv[8 * ks + 0], pv[8 * ks + 1], pv[8 * ks + 2], pv[8 * ks + 3], pv[8 * ks + 4],
-                                  pv[8 * ks + 5], pv[8 * ks + 6], pv[8 * ks + 7]);
-      const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3],
-                                  dsv[8 * ks + 4], dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
+      const bf16x8 pb = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      const bf16x8 sb = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       const lds_char* qrows = qblk + 16 * ks * T::ROW;
       const lds_char* drows = dblk + 16 * ks * T::ROW;
 #pragma unroll
@@ -296,8 +292,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const float c = p.scale_log2;
   const int klim = kj - (Lk - Lq);  // query rows i >= klim see this lane's key (causal)
 
-  for (int it = 0; it < total; ++it) {
-    const uint32_t cur = lds0 + (it & 1) * T::STAGE;
+  // Per query head of the group: the steps that need the causal mask (their
+  // first row is below mask_end) come first, then the unmasked ones; two loops
+  // so the accumulators keep their registers from step to step. `it` counts
+  // steps over all heads for the double-buffer and copy pipeline.
+  const int nmask = CAUSAL ? min(nsteps, max(0, ceil_div(mask_end, T::BMQ) - sfirst)) : 0;
+  auto stage_in = [&](int it) {
     if (it + 1 < total) {
       issue(it + 1, lds0 + ((it + 1) & 1) * T::STAGE);
       wait_qdo_stage<D>(wave);
@@ -305,15 +305,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    const int m0 = (sfirst + it % nsteps) * T::BMQ;
-    const lds_char* st = lds + (it & 1) * T::STAGE;
-    const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-    if (CAUSAL && m0 < mask_end)
-      dkdv_step<D, true>(st, st + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
-    else
-      dkdv_step<D, false>(st, st + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
-    lds_barrier();
-    (void)cur;
+  };
+  int it = 0;
+  for (int hg = 0; hg < (total > 0 ? r : 0); ++hg) {
+    for (int st = 0; st < nmask; ++st, ++it) {
+      stage_in(it);
+      const int m0 = (sfirst + st) * T::BMQ;
+      const lds_char* stg = lds + (it & 1) * T::STAGE;
+      const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
+      dkdv_step<D, true>(stg, stg + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
+      lds_barrier();
+    }
+    for (int st = nmask; st < nsteps; ++st, ++it) {
+      stage_in(it);
+      const int m0 = (sfirst + st) * T::BMQ;
+      const lds_char* stg = lds + (it & 1) * T::STAGE;
+      const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
+      dkdv_step<D, false>(stg, stg + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
+      lds_barrier();
+    }
   }
 
   if (kvalid) {
@@ -341,7 +351,7 @@ struct DqCfg {
   static constexpr int STAGE = 2 * TILE;
   static constexpr size_t LDS_BYTES = 2 * STAGE;
   static constexpr int DMA_PER_WAVE = 2 * KV::DMAS / 4;
-  static constexpr int WAVES_PER_SIMD = (D <= 64) ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
 };
 
 template <int D>
@@ -449,7 +459,9 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   const float c = p.scale_log2;
   const int qlim = qi + (Lk - Lq);
 
-  for (int n = 0; n < ntiles; ++n) {
+  // full tiles, then the masked ones: two loops so the accumulators keep their
+  // registers across iterations
+  auto stage_in = [&](int n) {
     if (n + 1 < ntiles) {
       issue_kv_dq<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
       wait_vmcnt<T::DMA_PER_WAVE>();
@@ -457,16 +469,23 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
       wait_vmcnt<0>();
     }
     lds_barrier();
+  };
+  for (int n = 0; n < nfull; ++n) {
+    stage_in(n);
     const lds_char* cur = lds + (n & 1) * T::STAGE;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const lds_char* Ks = cur + kb * 32 * T::ROW;
-      const lds_char* Vs = cur + T::TILE + kb * 32 * T::ROW;
-      if (n < nfull)
-        dq_half<D, false, CAUSAL>(Ks, Vs, qf, df, dq, c, lse2, dlt, n * T::BN + kb * 32, Lk, qlim, off, half);
-      else
-        dq_half<D, true, CAUSAL>(Ks, Vs, qf, df, dq, c, lse2, dlt, n * T::BN + kb * 32, Lk, qlim, off, half);
-    }
+    for (int kb = 0; kb < 2; ++kb)
+      dq_half<D, false, CAUSAL>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c, lse2, dlt,
+                                n * T::BN + kb * 32, Lk, qlim, off, half);
+    lds_barrier();
+  }
+  for (int n = nfull; n < ntiles; ++n) {
+    stage_in(n);
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      dq_half<D, true, CAUSAL>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c, lse2, dlt,
+                               n * T::BN + kb * 32, Lk, qlim, off, half);
     lds_barrier();
   }
 

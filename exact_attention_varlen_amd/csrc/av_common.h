@@ -47,11 +47,13 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Round-to-nearest-even float -> bf16 of two values, packed (lo in bits 0..15).
+// Round-to-nearest-even float -> bf16 of two values, packed (lo in bits 0..15):
+// one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
 
 // Eight fp32 values -> one bf16x8 MFMA operand.

@@ -89,25 +89,32 @@ __device__ __forceinline__ void issue_kv(uint32_t stage, const i32x4& rk, const 
   }
 }
 
-// 32 keys (one half of a key tile) of the online softmax for one wave (32
-// query columns): S^T = K Q^T, running max / sum update, O^T += V^T P^T.
+// One 64-key tile of the online softmax for one wave (32 query columns):
+// S^T = K Q^T for both 32-key halves (two independent MFMA chains, interleaved),
+// one running-max update for the tile, then per half P = exp2(S c - m) and
+// O^T += V^T P^T. Keeping the rescale decision per tile leaves the exp /
+// convert work of one half and the PV products of the other in one basic block.
 template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void fwd_half(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
-                                         float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk,
-                                         int qlim, const OperandOffsets<D>& off, int half) {
-  f32x16 s = zero16();
+__device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
+                                         float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk, int qlim,
+                                         const OperandOffsets<D>& off, int half) {
+  using T = FwdTile<D>;
+  f32x16 s0 = zero16(), s1 = zero16();
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) s = mfma32x32x16(as_bf16x8(lds_ld16(Ks + off.row_off[kk])), qf[kk], s);
-  // mask, max over the 32 keys (this lane's 16 and lane ^ 32's 16). Masked
+  for (int kk = 0; kk < D / 16; ++kk) {
+    s0 = mfma32x32x16(as_bf16x8(lds_ld16(Ks + off.row_off[kk])), qf[kk], s0);
+    s1 = mfma32x32x16(as_bf16x8(lds_ld16(Ks + 32 * T::ROW + off.row_off[kk])), qf[kk], s1);
+  }
+  // mask, max over the 64 keys (this lane's 32 and lane ^ 32's 32). Masked
   // scores are excluded by selects, never by -inf arithmetic, so that any
   // finite scale (0 included) is safe.
+  uint32_t vis_bits = 0xffffffffu;
   float mx = -INFINITY;
-  uint32_t vis_bits = 0xffffu;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = s[v];
+  for (int v = 0; v < 32; ++v) {
+    float x = (v < 16) ? s0[v] : s1[v - 16];
     if (MASK) {
-      const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
+      const int key = n0 + 32 * (v >> 4) + 16 * ((v >> 3) & 1) + 8 * half + (v & 7);
       const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
       vis_bits = vis ? vis_bits : (vis_bits & ~(1u << v));
       x = vis ? x : -INFINITY;
@@ -132,55 +139,45 @@ __device__ __forceinline__ void fwd_half(const lds_char* Ks, const lds_char* Vs,
   }
   const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float e = fast_exp2(__builtin_fmaf(s[v], c, -msub));
-    if (MASK) e = ((vis_bits >> v) & 1u) ? e : 0.f;
-    s[v] = e;
-    l_run += e;
-  }
-  // O^T += V^T P^T; V^T operand rows are head-dims (transposing reads)
+  for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    float pv[8];
+    for (int ks = 0; ks < 2; ++ks) {
+      float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = s[8 * ks + e];
-    bf16x8 pb, pl;
-    if (MASK) {
-      split_bf16x8(pv, pb, pl);
+      for (int e = 0; e < 8; ++e) {
+        const int v = 16 * kb + 8 * ks + e;
+        const float sv = kb ? s1[8 * ks + e] : s0[8 * ks + e];
+        float p = fast_exp2(__builtin_fmaf(sv, c, -msub));
+        if (MASK) p = ((vis_bits >> v) & 1u) ? p : 0.f;
+        pv[e] = p;
+        l_run += p;
+      }
+      bf16x8 pb, pl;
+      if (MASK) {
+        split_bf16x8(pv, pb, pl);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) l_o += pv[e];
-    } else {
-      uint4 u;
-      u.x = pack_bf16x2(pv[0], pv[1]);
-      u.y = pack_bf16x2(pv[2], pv[3]);
-      u.z = pack_bf16x2(pv[4], pv[5]);
-      u.w = pack_bf16x2(pv[6], pv[7]);
-      l_o = add_bf16x2(u.x, l_o);
-      l_o = add_bf16x2(u.y, l_o);
-      l_o = add_bf16x2(u.z, l_o);
-      l_o = add_bf16x2(u.w, l_o);
-      pb = as_bf16x8(u);
+        for (int e = 0; e < 8; ++e) l_o += pv[e];
+      } else {
+        uint4 u;
+        u.x = pack_bf16x2(pv[0], pv[1]);
+        u.y = pack_bf16x2(pv[2], pv[3]);
+        u.z = pack_bf16x2(pv[4], pv[5]);
+        u.w = pack_bf16x2(pv[6], pv[7]);
+        l_o = add_bf16x2(u.x, l_o);
+        l_o = add_bf16x2(u.y, l_o);
+        l_o = add_bf16x2(u.z, l_o);
+        l_o = add_bf16x2(u.w, l_o);
+        pb = as_bf16x8(u);
+      }
+      const lds_char* vrow = Vs + (32 * kb + 16 * ks) * T::ROW;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 va = tr_operand<D>(vrow, off, db);
+        o[db] = mfma32x32x16(va, pb, o[db]);
+        if (MASK) o[db] = mfma32x32x16(va, pl, o[db]);
+      }
     }
-    const lds_char* vrow = Vs + 16 * ks * FwdTile<D>::ROW;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 va = tr_operand<D>(vrow, off, db);
-      o[db] = mfma32x32x16(va, pb, o[db]);
-      if (MASK) o[db] = mfma32x32x16(va, pl, o[db]);
-    }
   }
-}
-
-// One key tile (64 keys = two halves).
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
-                                         float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk,
-                                         int qlim, const OperandOffsets<D>& off, int half) {
-  using T = FwdTile<D>;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-    fwd_half<D, MASK, CAUSAL>(Ks + kb * 32 * T::ROW, Vs + kb * 32 * T::ROW, qf, o, m_ref, l_run, l_o, c,
-                              n0 + kb * 32, Lk, qlim, off, half);
 }
 
 template <int D, bool CAUSAL, bool WRITE_LSE>
@@ -257,8 +254,9 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
   const float c = p.scale_log2;
   const int qlim = qi + (Lk - Lq);  // last visible key of this lane's query (causal)
 
-  for (int n = 0; n < ntiles; ++n) {
-    lds_char* cur = lds + (n & 1) * T::STAGE;
+  // Full tiles first, then the masked ones (causal diagonal, sequence tail), as
+  // two loops so that the accumulators keep their registers across iterations.
+  auto stage_in = [&](int n) {
     if (n + 1 < ntiles) {
       issue_kv<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
       wait_vmcnt<T::DMA_PER_WAVE>();  // this wave's copies of tile n have landed
@@ -266,11 +264,18 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
       wait_vmcnt<0>();
     }
     lds_barrier();  // ... and every other wave's
-    if (n < nfull)
-      fwd_tile<D, false, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
-    else
-      fwd_tile<D, true, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
+  };
+  for (int n = 0; n < nfull; ++n) {
+    stage_in(n);
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+    fwd_tile<D, false, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
     lds_barrier();  // stage (n & 1) is free for tile n + 2
+  }
+  for (int n = nfull; n < ntiles; ++n) {
+    stage_in(n);
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+    fwd_tile<D, true, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
+    lds_barrier();
   }
 
   // epilogue: O = O / l, LSE = ln(2) * (m + log2 l)
