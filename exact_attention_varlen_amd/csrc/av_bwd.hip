@@ -129,16 +129,17 @@ __device__ __forceinline__ void rows64_f32_dma(uint32_t dst, const i32x4& rsrc, 
 
 template <int D>
 struct DkdvCfg {
-  using QT = RowTile<D, 64>;
   static constexpr int NT = 256;
-  static constexpr int BNK = 128;  // keys per workgroup (32 per wave)
-  static constexpr int BMQ = 64;   // query rows per step
+  static constexpr int BNK = 128;                 // keys per workgroup (32 per wave)
+  static constexpr int BMQ = (D <= 128) ? 128 : 64;  // query rows per step
+  using QT = RowTile<D, BMQ>;
   static constexpr int ROW = QT::ROW;
   static constexpr int TILE = QT::BYTES;
-  static constexpr int F32 = 2 * TILE;        // lse2[64] then Delta[64]
-  static constexpr int STAGE = 2 * TILE + 512;
+  static constexpr int F32 = 2 * TILE;            // lse2[BMQ] then Delta[BMQ]
+  static constexpr int STAGE = 2 * TILE + 8 * BMQ;
   static constexpr size_t LDS_BYTES = 2 * STAGE;
   static constexpr int DMA_PER_WAVE = 2 * QT::DMAS / 4;  // Q and dO copies
+  static constexpr int F32_DMAS = BMQ / 64;              // 64-row fp32 copies per array
 };
 
 template <int D>
@@ -149,67 +150,122 @@ __device__ __forceinline__ void issue_qdo(uint32_t stage, const i32x4& rq, const
   for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
     const int qd = wave * T::DMA_PER_WAVE + i;
     const bool is_do = qd >= T::QT::DMAS;
-    tile_dma<D, 64>(stage + (is_do ? T::TILE : 0), is_do ? rdo : rq, pitch, m0, is_do ? qd - T::QT::DMAS : qd, lane);
+    tile_dma<D, T::BMQ>(stage + (is_do ? T::TILE : 0), is_do ? rdo : rq, pitch, m0, is_do ? qd - T::QT::DMAS : qd,
+                        lane);
   }
-  if (wave == 0) rows64_f32_dma(stage + T::F32, rl, m0, lane);
-  if (wave == 1) rows64_f32_dma(stage + T::F32 + 256, rd, m0, lane);
+  // lse2 rows on wave 0, Delta rows on wave 1 (64 rows per copy)
+#pragma unroll
+  for (int j = 0; j < T::F32_DMAS; ++j) {
+    if (wave == 0) rows64_f32_dma(stage + T::F32 + 256 * j, rl, m0 + 64 * j, lane);
+    if (wave == 1) rows64_f32_dma(stage + T::F32 + 4 * T::BMQ + 256 * j, rd, m0 + 64 * j, lane);
+  }
 }
 
-// waves 0 and 1 have one more copy per stage in flight than waves 2 and 3
+// waves 0 and 1 have F32_DMAS more copies per stage in flight than waves 2 and 3
 template <int D>
 __device__ __forceinline__ void wait_qdo_stage(int wave) {
   using T = DkdvCfg<D>;
   if (wave < 2)
-    wait_vmcnt<T::DMA_PER_WAVE + 1>();
+    wait_vmcnt<T::DMA_PER_WAVE + T::F32_DMAS>();
   else
     wait_vmcnt<T::DMA_PER_WAVE>();
 }
 
+// Scheduling hints (instruction classes for __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002;
+
+// dV += P^T dO and dK += dS^T Q for one k-step (16 queries) of a 32-query
+// block whose S and dP are done. The transposed operands and the rows'
+// lse2 / Delta are read from LDS before the exp / convert work, so that work
+// covers their latency.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_kstep(const f32x16& s, const f32x16& dp, int ks, const lds_char* qblk,
+                                           const lds_char* dblk, const float* lse2_s, const float* dlt_s, f32x16* dk,
+                                           f32x16* dv, float c, int qrow0, int klim, const OperandOffsets<D>& off,
+                                           int half) {
+  using T = DkdvCfg<D>;
+  const lds_char* qrows = qblk + 16 * ks * T::ROW;
+  const lds_char* drows = dblk + 16 * ks * T::ROW;
+  bf16x8 at_do[D / 32], at_q[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    at_do[db] = tr_operand<D>(drows, off, db);
+    at_q[db] = tr_operand<D>(qrows, off, db);
+  }
+  // register v <-> query row (qrow0 + 16*(v/8) + 8*half + (v%8)) of the step; the 8
+  // registers of k-step ks are the 8 consecutive queries 16 ks + 8 half + e
+  const int qo = qrow0 + 16 * ks + 8 * half;
+  const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
+  const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
+  const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
+  const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
+  const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  __builtin_amdgcn_sched_barrier(0);  // all of this k-step's LDS reads are in flight
+  float pv[8], dsv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int v = 8 * ks + e;
+    float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
+    if (MASK) pe = (qo + e >= klim) ? pe : 0.f;
+    pv[e] = pe;
+    dsv[e] = pe * (dp[v] - dl[e]);
+  }
+  const bf16x8 pb = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+  const bf16x8 sb = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dv[db] = mfma32x32x16(at_do[db], pb, dv[db]);
+    dk[db] = mfma32x32x16(at_q[db], sb, dk[db]);
+  }
+}
+
+// One step: BMQ query rows (starting at sequence row m0) against this wave's
+// 32 keys. For each pair of 32-query blocks the S and dP products (four
+// independent MFMA chains) run with their LDS operands fetched two k-steps
+// ahead; then each block's dV / dK updates.
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
                                           const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
                                           f32x16* dv, float c, int m0, int klim, const OperandOffsets<D>& off,
                                           int half) {
   using T = DkdvCfg<D>;
+  constexpr int KK = D / 16;
+  constexpr int PF = 2;  // prefetch distance in k-steps
 #pragma unroll
-  for (int qb = 0; qb < T::BMQ / 32; ++qb) {
-    const lds_char* qblk = Qs + qb * 32 * T::ROW;
-    const lds_char* dblk = dOs + qb * 32 * T::ROW;
-    f32x16 s = zero16(), dp = zero16();
+  for (int qp = 0; qp < T::BMQ / 64; ++qp) {
+    const lds_char* src[4] = {Qs + (64 * qp) * T::ROW, dOs + (64 * qp) * T::ROW, Qs + (64 * qp + 32) * T::ROW,
+                              dOs + (64 * qp + 32) * T::ROW};
+    f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};  // s0, dp0, s1, dp1
+    uint4 fr[PF + 1][4];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = mfma32x32x16(as_bf16x8(lds_ld16(qblk + off.row_off[kk])), kf[kk], s);
-      dp = mfma32x32x16(as_bf16x8(lds_ld16(dblk + off.row_off[kk])), vf[kk], dp);
+    for (int kk = 0; kk < PF; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fr[kk][j] = lds_ld16(src[j] + off.row_off[kk]);
     }
-    // register v <-> query qb*32 + 16*(v/8) + 8*half + (v%8) of the step; the
-    // 8 registers of k-step ks are the 8 consecutive queries 16 ks + 8 half + e
+    // The fences keep the compiler from sinking each load to just before its
+    // MFMA: the loads of k-step kk + PF are issued ahead of the MFMAs of kk.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int qo = qb * 32 + 16 * ks + 8 * half;
-      const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
-      const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
-      const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
-      const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
-      const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      float pv[8], dsv[8];
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + PF < KK) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = 8 * ks + e;
-        float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
-        if (MASK) pe = (m0 + qo + e >= klim) ? pe : 0.f;
-        pv[e] = pe;
-        dsv[e] = pe * (dp[v] - dl[e]);
+        for (int j = 0; j < 4; ++j) fr[(kk + PF) % (PF + 1)][j] = lds_ld16(src[j] + off.row_off[kk + PF]);
       }
-      const bf16x8 pb = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      const bf16x8 sb = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-      const lds_char* qrows = qblk + 16 * ks * T::ROW;
-      const lds_char* drows = dblk + 16 * ks * T::ROW;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dv[db] = mfma32x32x16(tr_operand<D>(drows, off, db), pb, dv[db]);
-        dk[db] = mfma32x32x16(tr_operand<D>(qrows, off, db), sb, dk[db]);
-      }
+      for (int j = 0; j < 4; ++j)
+        acc[j] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][j]), (j & 1) ? vf[kk] : kf[kk], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        dkdv_kstep<D, MASK>(acc[2 * b], acc[2 * b + 1], ks, src[2 * b], src[2 * b + 1], lse2_s, dlt_s, dk, dv, c,
+                            64 * qp + 32 * b, klim - m0, off, half);
     }
   }
 }
@@ -313,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int m0 = (sfirst + st) * T::BMQ;
       const lds_char* stg = lds + (it & 1) * T::STAGE;
       const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-      dkdv_step<D, true>(stg, stg + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
+      dkdv_step<D, true>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, klim, off, half);
       lds_barrier();
     }
     for (int st = nmask; st < nsteps; ++st, ++it) {
@@ -321,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       const int m0 = (sfirst + st) * T::BMQ;
       const lds_char* stg = lds + (it & 1) * T::STAGE;
       const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-      dkdv_step<D, false>(stg, stg + T::TILE, f32, f32 + 64, kf, vf, dk, dv, c, m0, klim, off, half);
+      dkdv_step<D, false>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, klim, off, half);
       lds_barrier();
     }
   }
