@@ -427,12 +427,32 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
                                         f32x16* dq, float c, float lse2, float dlt, int n0, int Lk, int qlim,
                                         const OperandOffsets<D>& off, int half) {
   using T = DqCfg<D>;
+  constexpr int KK = D / 16;
+  constexpr int PF = 2;  // K / V operands are fetched PF k-steps ahead of their MFMAs
   f32x16 s = zero16(), dp = zero16();
+  uint4 fr[PF + 1][2];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    s = mfma32x32x16(as_bf16x8(lds_ld16(Ks + off.row_off[kk])), qf[kk], s);
-    dp = mfma32x32x16(as_bf16x8(lds_ld16(Vs + off.row_off[kk])), df[kk], dp);
+  for (int kk = 0; kk < PF; ++kk) {
+    fr[kk][0] = lds_ld16(Ks + off.row_off[kk]);
+    fr[kk][1] = lds_ld16(Vs + off.row_off[kk]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + PF < KK) {
+      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Ks + off.row_off[kk + PF]);
+      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Vs + off.row_off[kk + PF]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][0]), qf[kk], s);
+    dp = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][1]), df[kk], dp);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // K^T operands of the first k-step of dQ are read before the exp work
+  bf16x8 ka[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) ka[db] = tr_operand<D>(Ks, off, db);
+  __builtin_amdgcn_sched_barrier(0);
   float dsv[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -448,9 +468,12 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
   for (int ks = 0; ks < 2; ++ks) {
     const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3], dsv[8 * ks + 4],
                                 dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
-    const lds_char* krows = Ks + 16 * ks * T::ROW;
+    if (ks == 1) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(tr_operand<D>(krows, off, db), sb, dq[db]);
+      for (int db = 0; db < D / 32; ++db) ka[db] = tr_operand<D>(Ks + 16 * T::ROW, off, db);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(ka[db], sb, dq[db]);
   }
 }
 

@@ -99,11 +99,27 @@ __device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs,
                                          float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk, int qlim,
                                          const OperandOffsets<D>& off, int half) {
   using T = FwdTile<D>;
+  constexpr int KK = D / 16;
+  constexpr int PF = 2;  // K operands are fetched PF k-steps ahead of their MFMAs
   f32x16 s0 = zero16(), s1 = zero16();
+  uint4 fr[PF + 1][2];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    s0 = mfma32x32x16(as_bf16x8(lds_ld16(Ks + off.row_off[kk])), qf[kk], s0);
-    s1 = mfma32x32x16(as_bf16x8(lds_ld16(Ks + 32 * T::ROW + off.row_off[kk])), qf[kk], s1);
+  for (int kk = 0; kk < PF; ++kk) {
+    fr[kk][0] = lds_ld16(Ks + off.row_off[kk]);
+    fr[kk][1] = lds_ld16(Ks + 32 * T::ROW + off.row_off[kk]);
+  }
+  // fences keep the compiler from sinking each load to just before its MFMA
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + PF < KK) {
+      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Ks + off.row_off[kk + PF]);
+      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Ks + 32 * T::ROW + off.row_off[kk + PF]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s0 = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][0]), qf[kk], s0);
+    s1 = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][1]), qf[kk], s1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // mask, max over the 64 keys (this lane's 32 and lane ^ 32's 32). Masked
   // scores are excluded by selects, never by -inf arithmetic, so that any
@@ -142,6 +158,12 @@ __device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs,
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // V^T operands of this k-step are read before the exp / convert work
+      const lds_char* vrow = Vs + (32 * kb + 16 * ks) * T::ROW;
+      bf16x8 va[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) va[db] = tr_operand<D>(vrow, off, db);
+      __builtin_amdgcn_sched_barrier(0);
       float pv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -169,12 +191,10 @@ __device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs,
         l_o = add_bf16x2(u.w, l_o);
         pb = as_bf16x8(u);
       }
-      const lds_char* vrow = Vs + (32 * kb + 16 * ks) * T::ROW;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 va = tr_operand<D>(vrow, off, db);
-        o[db] = mfma32x32x16(va, pb, o[db]);
-        if (MASK) o[db] = mfma32x32x16(va, pl, o[db]);
+        o[db] = mfma32x32x16(va[db], pb, o[db]);
+        if (MASK) o[db] = mfma32x32x16(va[db], pl, o[db]);
       }
     }
   }
