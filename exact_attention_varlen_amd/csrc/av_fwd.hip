@@ -7,15 +7,22 @@
 // Abstractions (online softmax; causal block ranges; varlen offsets). The
 // result is the exact softmax(QK^T * scale + mask) V of each packed sequence.
 //
-// gfx950 design (one workgroup = 4 waves = one query block of 128 rows of one
-// query head; each wave owns 32 query rows):
+// gfx950 design (one workgroup = BM / 32 waves = one query block of BM rows of
+// one query head; each wave owns 32 query rows):
 //  * Q^T stays in VGPRs for the whole item as the B operand of S^T = K Q^T.
 //  * K and V tiles of 64 keys go HBM -> LDS with buffer_load ... lds (no VGPR
-//    staging, out-of-range rows read as zero), double-buffered: the loads of
-//    tile n+1 are in flight while tile n is computed. Rows are stored
-//    row-major with an XOR swizzle of 16-byte chunks (swz<D>).
-//  * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16. V^T comes
-//    from the row-major V tile through transposing LDS reads
+//    staging, out-of-range rows read as zero) into separate double buffers.
+//    Rows are stored row-major with an XOR swizzle of 16-byte chunks (swz<D>).
+//    The tile's first row is folded into the buffer descriptor (scalar ops),
+//    so the per-lane copy offsets never change.
+//  * Software pipeline inside each wave. Iteration n holds the scores of tile
+//    n and runs two phases: (B) the MFMAs of S(n+1) = K(n+1) Q^T interleaved
+//    with the exp / row-sum / bf16 packing of most of P(n); (C) the MFMAs of
+//    O^T += V(n)^T P(n)^T interleaved with the rest of P(n) and the row max of
+//    S(n+1). The vector ALU work of the softmax thus issues while the matrix
+//    cores run, instead of between MFMA bursts. K(n+1) and V(n) are resident
+//    together, and the copies of K(n+2) and V(n+1) are in flight meanwhile.
+//  * V^T comes from the row-major V tile through transposing LDS reads
 //    (ds_read_b64_tr_b16); the key permutation kperm makes the fp32 score
 //    registers the B operand of the PV product after a bf16 conversion.
 //  * Each lane owns one query column: running max, running sum and rescale
@@ -29,11 +36,14 @@
 //    the LSE, and the sum of the bf16-rounded P that enter the PV product
 //    normalises O, so the rounding of P cancels in O's weighted average even
 //    when one key carries almost all of a row's weight.
-//  * Masking code runs only on key tiles that cross the causal diagonal or the
-//    end of the sequence (a separate instantiation of the tile step); tiles
-//    past the causal range are never visited. On masked tiles P is split into
-//    bf16 hi + lo parts so rows with very few visible keys stay accurate.
+//  * Masking runs only on key tiles that cross the causal diagonal or the end
+//    of the sequence: their invisible scores are set to -inf once, when the
+//    tile's scores are formed (the scale factor is always > 0, so exp2 maps
+//    them to exactly 0). Tiles past the causal range are never visited. On
+//    masked tiles P is split into bf16 hi + lo parts so rows with very few
+//    visible keys stay accurate.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 #include "av_common.h"
@@ -44,18 +54,29 @@ namespace av {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D>
-struct FwdTile {
+template <int D, int BM_>
+struct FwdCfg {
   using KV = RowTile<D, 64>;
-  static constexpr int BM = 128;                      // query rows per workgroup
+  static constexpr int BM = BM_;                      // query rows per workgroup
+  static constexpr int WAVES = BM / 32;               // one wave per 32 rows
   static constexpr int BN = 64;                       // keys per tile
-  static constexpr int NT = 256;                      // threads per workgroup
+  static constexpr int NT = 64 * WAVES;               // threads per workgroup
   static constexpr int ROW = KV::ROW;                 // bytes per key row in LDS
   static constexpr int TILE = KV::BYTES;              // bytes of one K or V tile
-  static constexpr int STAGE = 2 * TILE;              // K then V
-  static constexpr size_t LDS_BYTES = 2 * STAGE;      // two stages
-  static constexpr int DMA_PER_WAVE = 2 * KV::DMAS / 4;
-  static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
+  static constexpr int VBASE = 2 * TILE;              // K0 K1 | V0 V1
+  static constexpr size_t LDS_BYTES = 4 * TILE;
+  static constexpr int DMA = KV::DMAS / WAVES;        // copies per wave per tile
+  static constexpr int KK = D / 16;                   // k-steps of S = K Q^T
+  static constexpr int DB = D / 32;                   // 32-wide head-dim blocks of O
+  static constexpr int PF = 2;                        // K operand prefetch distance
+  static constexpr int WAVES_PER_SIMD = 2;
+  static_assert(KV::DMAS % WAVES == 0, "tile copies must split evenly over the waves");
+};
+
+// The forward kernel's tile size for a head_dim (the grid depends on it).
+template <int D>
+struct FwdBlock {
+  static constexpr int BM = 128;
 };
 
 struct FwdParams {
@@ -71,140 +92,284 @@ struct FwdParams {
   int Hq;
   int Hkv;
   int levels;        // ceil(max_seqlen_q / BM)
-  float scale_log2;  // |softmax_scale| * log2(e)
+  float scale_log2;  // |softmax_scale| * log2(e), at least FLT_MIN
   int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
 };
 
-// Issue this wave's share of the K and V tile copies (keys n0 .. n0+63) into
-// the LDS stage at byte address `stage`.
-template <int D>
-__device__ __forceinline__ void issue_kv(uint32_t stage, const i32x4& rk, const i32x4& rv, uint32_t pitch, int n0,
-                                        int wave, int lane) {
-  using T = FwdTile<D>;
+// Descriptor of the same rows starting `bytes` further on.
+__device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, uint32_t bytes) {
+  const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + bytes;
+  i32x4 o;
+  o[0] = (int)(uint32_t)base;
+  o[1] = (int)((uint32_t)(base >> 32) & 0xffffu);
+  o[2] = (int)((uint32_t)r[2] - bytes);
+  o[3] = r[3];
+  return o;
+}
+
+// Per-wave state of the forward item that the pipeline steps share.
+template <int D, int BM>
+struct FwdCtx {
+  using T = FwdCfg<D, BM>;
+  const lds_char* lds;
+  uint32_t lds0;
+  i32x4 rk, rv;          // K / V rows of this (sequence, KV head), from key 0
+  uint32_t tile_bytes;   // BN rows of the K / V tensor
+  uint32_t voff[T::DMA]; // this lane's source offset within a tile, per copy
+  int wave, half;
+  int ntiles;
+  int kvis_end;          // first key invisible to this lane's query row
+  float c;               // exp2 scale factor
+  OperandOffsets<D> off;
+  bf16x8 qf[T::KK];
+};
+
+// Copy this wave's share of a 64-row tile (rows row0 ..) into LDS at `dst`.
+template <int D, int BM>
+__device__ __forceinline__ void issue_tile(const FwdCtx<D, BM>& x, uint32_t dst, const i32x4& rsrc, int row0) {
+  using T = FwdCfg<D, BM>;
+  const i32x4 r = rsrc_advance(rsrc, (uint32_t)row0 * (x.tile_bytes / T::BN));
 #pragma unroll
-  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-    const int qd = wave * T::DMA_PER_WAVE + i;  // which 1 KB copy of the stage
-    const bool is_v = qd >= T::KV::DMAS;
-    tile_dma<D, 64>(stage + (is_v ? T::TILE : 0), is_v ? rv : rk, pitch, n0, is_v ? qd - T::KV::DMAS : qd, lane);
+  for (int i = 0; i < T::DMA; ++i) lds_dma16(r, dst + (x.wave * T::DMA + i) * 1024, x.voff[i]);
+}
+
+// Score register v of accumulator a (a = 0: keys 0..31 of the tile, a = 1:
+// keys 32..63) is key 32 a + 16 (v / 8) + 8 half + v % 8.
+template <int D, int BM>
+__device__ __forceinline__ void mask_scores(const FwdCtx<D, BM>& x, f32x16& s, int first_key) {
+  const int t = x.kvis_end - first_key - 8 * x.half;  // visible iff 16 (v / 8) + v % 8 < t
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s[v] = (16 * (v >> 3) + (v & 7) < t) ? s[v] : -INFINITY;
+}
+
+__device__ __forceinline__ float max16(const f32x16& s, float m) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) m = fmaxf(m, s[v]);
+  return m;
+}
+
+// P for score i (0 .. 31) of the tile: register i % 16 of accumulator i / 16,
+// i.e. PV k-step i / 8, slot i % 8. Scores are exponentiated one at a time so
+// the work can be spread evenly between MFMAs, in two stages: exp_issue forms
+// p = exp2(s c - m); exp_finish adds it to the row sums and, with the second
+// score of a pair, packs the pair to bf16 (and, on masked tiles, splits it
+// into hi / lo parts). Issuing the exponentials one MFMA ahead of their use
+// hides the latency of the transcendental unit.
+__device__ __forceinline__ void exp_issue(const f32x16 (&sc)[2], int i, float c, float nm, float* pe) {
+  pe[i] = fast_exp2(__builtin_fmaf(sc[i >> 4][i & 15], c, nm));
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void exp_finish(int i, float& l_run, float& l_o, const float* pe, uint32_t* ph,
+                                           uint32_t* pl) {
+  const float p = pe[i];
+  l_run += p;
+  if (i & 1) {
+    const float p0 = pe[i - 1];
+    const uint32_t h = pack_bf16x2(p0, p);
+    ph[i >> 1] = h;
+    if (SPLIT) {
+      pl[i >> 1] = pack_bf16x2(p0 - bf16_lo(h), p - bf16_hi(h));
+      l_o += p0;
+      l_o += p;
+    } else {
+      l_o = add_bf16x2(h, l_o);
+    }
   }
 }
 
-// One 64-key tile of the online softmax for one wave (32 query columns):
-// S^T = K Q^T for both 32-key halves (two independent MFMA chains, interleaved),
-// one running-max update for the tile, then per half P = exp2(S c - m) and
-// O^T += V^T P^T. Keeping the rescale decision per tile leaves the exp /
-// convert work of one half and the PV products of the other in one basic block.
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, f32x16* o,
-                                         float& m_ref, float& l_run, float& l_o, float c, int n0, int Lk, int qlim,
-                                         const OperandOffsets<D>& off, int half) {
-  using T = FwdTile<D>;
-  constexpr int KK = D / 16;
-  constexpr int PF = 2;  // K operands are fetched PF k-steps ahead of their MFMAs
-  f32x16 s0 = zero16(), s1 = zero16();
-  uint4 fr[PF + 1][2];
+template <bool SPLIT>
+__device__ __forceinline__ void exp_score(const f32x16 (&sc)[2], int i, float c, float nm, float& l_run, float& l_o,
+                                          float* pe, uint32_t* ph, uint32_t* pl) {
+  exp_issue(sc, i, c, nm, pe);
+  exp_finish<SPLIT>(i, l_run, l_o, pe, ph, pl);
+}
+
+// S^T of one 64-key tile (both 32-key halves) for this wave's 32 queries.
+template <int D, int BM>
+__device__ __forceinline__ void qk_tile(const FwdCtx<D, BM>& x, const lds_char* Ks, f32x16 (&s)[2]) {
+  using T = FwdCfg<D, BM>;
+  uint4 fr[T::PF + 1][2];
 #pragma unroll
-  for (int kk = 0; kk < PF; ++kk) {
-    fr[kk][0] = lds_ld16(Ks + off.row_off[kk]);
-    fr[kk][1] = lds_ld16(Ks + 32 * T::ROW + off.row_off[kk]);
+  for (int kk = 0; kk < T::PF; ++kk) {
+    fr[kk][0] = lds_ld16(Ks + x.off.row_off[kk]);
+    fr[kk][1] = lds_ld16(Ks + 32 * T::ROW + x.off.row_off[kk]);
   }
-  // fences keep the compiler from sinking each load to just before its MFMA
+  s[0] = zero16();
+  s[1] = zero16();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    if (kk + PF < KK) {
-      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Ks + off.row_off[kk + PF]);
-      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Ks + 32 * T::ROW + off.row_off[kk + PF]);
+  for (int kk = 0; kk < T::KK; ++kk) {
+    if (kk + T::PF < T::KK) {
+      fr[(kk + T::PF) % (T::PF + 1)][0] = lds_ld16(Ks + x.off.row_off[kk + T::PF]);
+      fr[(kk + T::PF) % (T::PF + 1)][1] = lds_ld16(Ks + 32 * T::ROW + x.off.row_off[kk + T::PF]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    s0 = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][0]), qf[kk], s0);
-    s1 = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][1]), qf[kk], s1);
+    s[0] = mfma32x32x16(as_bf16x8(fr[kk % (T::PF + 1)][0]), x.qf[kk], s[0]);
+    s[1] = mfma32x32x16(as_bf16x8(fr[kk % (T::PF + 1)][1]), x.qf[kk], s[1]);
     __builtin_amdgcn_sched_barrier(0);
-  }
-  // mask, max over the 64 keys (this lane's 32 and lane ^ 32's 32). Masked
-  // scores are excluded by selects, never by -inf arithmetic, so that any
-  // finite scale (0 included) is safe.
-  uint32_t vis_bits = 0xffffffffu;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < 32; ++v) {
-    float x = (v < 16) ? s0[v] : s1[v - 16];
-    if (MASK) {
-      const int key = n0 + 32 * (v >> 4) + 16 * ((v >> 3) & 1) + 8 * half + (v & 7);
-      const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
-      vis_bits = vis ? vis_bits : (vis_bits & ~(1u << v));
-      x = vis ? x : -INFINITY;
-    }
-    mx = fmaxf(mx, x);
-  }
-  mx = max_xor32(mx);
-  const float cand = (mx == -INFINITY) ? -INFINITY : mx * c;
-  if (__ballot(cand > m_ref + kRescaleSlack)) {
-    const float mn = fmaxf(m_ref, cand);
-    // 0 when m_ref = -inf (O and l are still 0); rows that have seen no visible
-    // key yet keep mn = -inf and must not form exp2(-inf - -inf)
-    const float alpha = fast_exp2(m_ref - (mn == -INFINITY ? 0.f : mn));
-    m_ref = mn;
-    l_run *= alpha;
-    l_o *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-    }
-  }
-  const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      // V^T operands of this k-step are read before the exp / convert work
-      const lds_char* vrow = Vs + (32 * kb + 16 * ks) * T::ROW;
-      bf16x8 va[D / 32];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) va[db] = tr_operand<D>(vrow, off, db);
-      __builtin_amdgcn_sched_barrier(0);
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = 16 * kb + 8 * ks + e;
-        const float sv = kb ? s1[8 * ks + e] : s0[8 * ks + e];
-        float p = fast_exp2(__builtin_fmaf(sv, c, -msub));
-        if (MASK) p = ((vis_bits >> v) & 1u) ? p : 0.f;
-        pv[e] = p;
-        l_run += p;
-      }
-      bf16x8 pb, pl;
-      if (MASK) {
-        split_bf16x8(pv, pb, pl);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l_o += pv[e];
-      } else {
-        uint4 u;
-        u.x = pack_bf16x2(pv[0], pv[1]);
-        u.y = pack_bf16x2(pv[2], pv[3]);
-        u.z = pack_bf16x2(pv[4], pv[5]);
-        u.w = pack_bf16x2(pv[6], pv[7]);
-        l_o = add_bf16x2(u.x, l_o);
-        l_o = add_bf16x2(u.y, l_o);
-        l_o = add_bf16x2(u.z, l_o);
-        l_o = add_bf16x2(u.w, l_o);
-        pb = as_bf16x8(u);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        o[db] = mfma32x32x16(va[db], pb, o[db]);
-        if (MASK) o[db] = mfma32x32x16(va[db], pl, o[db]);
-      }
-    }
   }
 }
 
-template <int D, bool CAUSAL, bool WRITE_LSE>
-__global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(FwdParams p) {
-  using T = FwdTile<D>;
+// One pipeline step: tile n's softmax and PV product, tile n + 1's scores.
+//  PAR   buffer parity of n;
+//  MC    tile n is masked (its scores in sc already hold -inf where invisible);
+//  NX    1: tile n + 1 exists and is unmasked; -1: tile n + 1, if there is
+//        one, is masked (tiles treated as masked may well be full).
+// On entry sc holds S(n) and mx this lane's max over it; on return sn holds
+// S(n + 1) and mx its max (when tile n + 1 exists).
+template <int D, int BM, int PAR, bool MC, int NX>
+__device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f32x16 (&sc)[2], f32x16 (&sn)[2],
+                                         f32x16 (&o)[FwdCfg<D, BM>::DB], float& m_ref, float& l_run, float& l_o,
+                                         float& mx) {
+  using T = FwdCfg<D, BM>;
+  constexpr int KK = T::KK, PF = T::PF, DB = T::DB;
+  constexpr int par = PAR;
+  const bool next = NX > 0 || n + 1 < x.ntiles;
+
+  // every wave is done with tile n - 1; V(n) and K(n + 1) have landed
+  wait_vmcnt<0>();
+  lds_barrier();
+  if (next) {
+    if (n + 2 < x.ntiles) issue_tile(x, x.lds0 + par * T::TILE, x.rk, (n + 2) * T::BN);
+    issue_tile(x, x.lds0 + T::VBASE + (par ^ 1) * T::TILE, x.rv, (n + 1) * T::BN);
+  }
+  const lds_char* Kn = x.lds + (par ^ 1) * T::TILE;         // K(n + 1)
+  const lds_char* Vc = x.lds + T::VBASE + par * T::TILE;    // V(n)
+
+  uint4 fr[PF + 1][2];
+  if (next) {
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) {
+      fr[kk][0] = lds_ld16(Kn + x.off.row_off[kk]);
+      fr[kk][1] = lds_ld16(Kn + 32 * T::ROW + x.off.row_off[kk]);
+    }
+  }
+
+  // running max: move the reference (and rescale O) only when the tile's max
+  // exceeds it by more than the slack, for any lane of the wave
+  {
+    const float mt = max_xor32(mx);
+    const float cand = (mt == -INFINITY) ? -INFINITY : mt * x.c;
+    if (__ballot(cand > m_ref + kRescaleSlack)) {
+      const float mn = fmaxf(m_ref, cand);
+      // 0 when m_ref = -inf (O and l are still 0); rows that have seen no
+      // visible key yet keep mn = -inf and must not form exp2(-inf - -inf)
+      const float alpha = fast_exp2(m_ref - (mn == -INFINITY ? 0.f : mn));
+      m_ref = mn;
+      l_run *= alpha;
+      l_o *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      }
+    }
+  }
+  const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
+
+  // The matrix core runs one MFMA at a time and a wave issues in order, so the
+  // VALU work is spread in small shares between consecutive MFMAs: each share
+  // issues while the MFMA before it executes.
+  //
+  // phase B: S(n + 1) on the matrix cores (2 KK MFMAs); on the VALU, P(n)
+  // scores 0 .. SB - 1 (unmasked tile) or 0 .. 7 (masked tile: its hi / lo
+  // parts are formed one PV k-step ahead in phase C instead, which keeps fewer
+  // registers live)
+  constexpr int SB = MC ? 8 : 18;
+  constexpr int NB = 2 * KK;
+  float pe[32];
+  uint32_t ph[16], pl[16];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int kk = m >> 1, a = m & 1;
+    if (next) {
+      if (a == 0 && kk + PF < KK) {
+        fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Kn + x.off.row_off[kk + PF]);
+        fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Kn + 32 * T::ROW + x.off.row_off[kk + PF]);
+      }
+      sn[a] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][a]), x.qf[kk], kk ? sn[a] : zero16());
+    }
+    if (MC) {
+#pragma unroll
+      for (int i = SB * m / NB; i < SB * (m + 1) / NB; ++i) exp_score<MC>(sc, i, x.c, nm, l_run, l_o, pe, ph, pl);
+    } else {
+      // this share's exponentials, and the sums / packing of the previous share's
+#pragma unroll
+      for (int i = SB * m / NB; i < SB * (m + 1) / NB; ++i) exp_issue(sc, i, x.c, nm, pe);
+      if (m > 0) {
+#pragma unroll
+        for (int i = SB * (m - 1) / NB; i < SB * m / NB; ++i) exp_finish<MC>(i, l_run, l_o, pe, ph, pl);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // phase C: O^T += V(n)^T P(n)^T on the matrix cores, one MFMA unit (PV
+  // k-step j, head-dim block db) at a time with the V^T operands read RV - 1
+  // units ahead. On the VALU: the units of k-steps 0 and 1 finish P(n)
+  // (scores SB .. 31), those of k-steps 2 and 3 take the max of S(n + 1); a
+  // masked tile instead forms the next k-step's P during each k-step.
+  constexpr int NU = 4 * DB, RV = 3;
+  bf16x8 va[RV];
+#pragma unroll
+  for (int u = 0; u < RV - 1; ++u) va[u] = tr_operand<D>(Vc + 16 * (u / DB) * T::ROW, x.off, u % DB);
+  float mxa = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int j = u / DB, db = u % DB;
+    if (u + RV - 1 < NU) {
+      const int w = u + RV - 1;
+      va[w % RV] = tr_operand<D>(Vc + 16 * (w / DB) * T::ROW, x.off, w % DB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 pb = as_bf16x8(make_uint4(ph[4 * j], ph[4 * j + 1], ph[4 * j + 2], ph[4 * j + 3]));
+    o[db] = mfma32x32x16(va[u % RV], pb, o[db]);
+    if (MC) {
+      const bf16x8 pq = as_bf16x8(make_uint4(pl[4 * j], pl[4 * j + 1], pl[4 * j + 2], pl[4 * j + 3]));
+      o[db] = mfma32x32x16(va[u % RV], pq, o[db]);
+      if (j + 1 < 4) {
+#pragma unroll
+        for (int i = 8 * (j + 1) + 8 * db / DB; i < 8 * (j + 1) + 8 * (db + 1) / DB; ++i)
+          exp_score<MC>(sc, i, x.c, nm, l_run, l_o, pe, ph, pl);
+      }
+    } else if (u <= 2 * DB) {
+      // scores SB .. 31 over the units of k-steps 0 and 1, each share finished
+      // one unit later (the first unit finishes phase B's last share)
+      if (u < 2 * DB) {
+#pragma unroll
+        for (int i = SB + (32 - SB) * u / (2 * DB); i < SB + (32 - SB) * (u + 1) / (2 * DB); ++i)
+          exp_issue(sc, i, x.c, nm, pe);
+      }
+      const int f0 = u ? SB + (32 - SB) * (u - 1) / (2 * DB) : SB * (NB - 1) / NB;
+      const int f1 = u ? SB + (32 - SB) * u / (2 * DB) : SB;
+#pragma unroll
+      for (int i = f0; i < f1; ++i) exp_finish<MC>(i, l_run, l_o, pe, ph, pl);
+    }
+    if (next && u >= 2 * DB) {
+      // mask and max of S(n + 1): 32 values spread over the last 2 DB units
+      const int e = u - 2 * DB;
+#pragma unroll
+      for (int i = 32 * e / (2 * DB); i < 32 * (e + 1) / (2 * DB); ++i) {
+        const int v = i & 15;
+        if (NX < 0) {
+          const int t = x.kvis_end - (n + 1) * T::BN - 32 * (i >> 4) - 8 * x.half;
+          sn[i >> 4][v] = (16 * (v >> 3) + (v & 7) < t) ? sn[i >> 4][v] : -INFINITY;
+        }
+        mxa = fmaxf(mxa, sn[i >> 4][v]);
+      }
+      asm volatile("" : "+v"(mxa));  // keep this unit's share of the max here
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  mx = mxa;  // meaningless when there is no tile n + 1
+}
+
+template <int D, int BM, bool CAUSAL, bool WRITE_LSE>
+__global__ __launch_bounds__((FwdCfg<D, BM>::NT), (FwdCfg<D, BM>::WAVES_PER_SIMD)) void fwd_kernel(FwdParams p) {
+  using T = FwdCfg<D, BM>;
   extern __shared__ __align__(16) uint16_t smem[];
-  lds_char* lds = (lds_char*)smem;
 
   const int r = p.Hq / p.Hkv;
   const int64_t L = xcd_logical(blockIdx.x, r);
@@ -219,83 +384,104 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
   const int ck = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - ck;
 
+  FwdCtx<D, BM> x;
+  x.lds = (const lds_char*)smem;
+  x.lds0 = lds_addr((lds_char*)smem);
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int col = lane & 31;
-  const int half = lane >> 5;
+  x.half = lane >> 5;
   const int q0 = mblk * T::BM;
-  const int qi = q0 + wave * 32 + col;  // this lane's query row (sequence-relative)
+  const int qi = q0 + x.wave * 32 + (lane & 31);  // this lane's query row (sequence-relative)
   const bool qvalid = qi < Lq;
 
   int kend = Lk;
   if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
-  const int ntiles = ceil_div(kend, T::BN);
+  x.ntiles = ceil_div(kend, T::BN);
   // tiles [0, nfull) need no mask: every key is below Lk and visible to every row
   const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
-  const int nfull = min(ntiles, kfull / T::BN);
+  const int nfull = min(x.ntiles, kfull / T::BN);
+  x.kvis_end = CAUSAL ? min(Lk, qi + (Lk - Lq) + 1) : Lk;
+  x.c = p.scale_log2;
 
   // K / V buffer resources for this (sequence, KV head): rows past Lk read as 0
   const uint32_t pitch = (uint32_t)p.Hkv * D * 2;
+  x.tile_bytes = pitch * T::BN;
   const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
-  const i32x4 rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
-  const i32x4 rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
-  const uint32_t lds0 = lds_addr(lds);
+  x.rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
+  x.rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
+#pragma unroll
+  for (int i = 0; i < T::DMA; ++i) {
+    const int row = (x.wave * T::DMA + i) * T::KV::ROWS_PER_DMA + lane / T::KV::CPR;
+    const int cidx = (lane % T::KV::CPR) ^ swz<D>(row);
+    x.voff[i] = (uint32_t)row * pitch + (uint32_t)cidx * 16u;
+  }
 
-  if (ntiles > 0) issue_kv<D>(lds0, rk, rv, pitch, 0, wave, lane);
-
-  // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
-  // (sign-flipped when the scale is negative, so the scale applied is positive).
-  bf16x8 qf[D / 16];
+  // prologue copies: K(0) -> K0, V(0) -> V0, K(1) -> K1; then Q^T into VGPRs
+  if (x.ntiles > 0) {
+    issue_tile(x, x.lds0, x.rk, 0);
+    issue_tile(x, x.lds0 + T::VBASE, x.rv, 0);
+    if (x.ntiles > 1) issue_tile(x, x.lds0 + T::TILE, x.rk, T::BN);
+  }
   {
-    const uint16_t* qrow = p.q + ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * half;
+    // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
+    // (sign-flipped when the scale is negative, so the scale applied is positive)
+    const uint16_t* qrow = p.q + ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * x.half;
     const uint32_t flip = p.neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < T::KK; ++kk) {
       uint4 u = qvalid ? ld16(qrow + 16 * kk) : zero_u4();
       u.x ^= flip;
       u.y ^= flip;
       u.z ^= flip;
       u.w ^= flip;
-      qf[kk] = as_bf16x8(u);
+      x.qf[kk] = as_bf16x8(u);
     }
   }
+  operand_offsets<D>(x.off, lane);
 
-  // per-lane LDS byte offsets of the MFMA operand reads
-  OperandOffsets<D> off;
-  operand_offsets<D>(off, lane);
-
-  f32x16 o[D / 32];
+  f32x16 o[T::DB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = zero16();
+  for (int db = 0; db < T::DB; ++db) o[db] = zero16();
   float m_ref = -INFINITY;
   float l_run = 0.f;  // sum of P (fp32): the LSE
   float l_o = 0.f;    // sum of the P values as they enter the PV product: normalises O
-  const float c = p.scale_log2;
-  const int qlim = qi + (Lk - Lq);  // last visible key of this lane's query (causal)
+  float mx = -INFINITY;
+  f32x16 sa[2], sb[2];
 
-  // Full tiles first, then the masked ones (causal diagonal, sequence tail), as
-  // two loops so that the accumulators keep their registers across iterations.
-  auto stage_in = [&](int n) {
-    if (n + 1 < ntiles) {
-      issue_kv<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
-      wait_vmcnt<T::DMA_PER_WAVE>();  // this wave's copies of tile n have landed
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // ... and every other wave's
-  };
-  for (int n = 0; n < nfull; ++n) {
-    stage_in(n);
-    const lds_char* cur = lds + (n & 1) * T::STAGE;
-    fwd_tile<D, false, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
-    lds_barrier();  // stage (n & 1) is free for tile n + 2
-  }
-  for (int n = nfull; n < ntiles; ++n) {
-    stage_in(n);
-    const lds_char* cur = lds + (n & 1) * T::STAGE;
-    fwd_tile<D, true, CAUSAL>(cur, cur + T::TILE, qf, o, m_ref, l_run, l_o, c, n * T::BN, Lk, qlim, off, half);
+  if (x.ntiles > 0) {
+    wait_vmcnt<0>();
     lds_barrier();
+    qk_tile(x, x.lds, sa);
+    if (nfull == 0) {
+      mask_scores(x, sa[0], 0);
+      mask_scores(x, sa[1], 32);
+    }
+    mx = max16(sa[1], max16(sa[0], mx));
+  }
+
+  // Steady state, unrolled by two so the buffer parity is a constant: tile n
+  // and tile n + 1 both unmasked. S(n) lives in sa for even n, sb for odd n.
+  int n = 0;
+  if (nfull > 0) {
+    for (; n + 3 <= nfull; n += 2) {
+      fwd_step<D, BM, 0, false, 1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
+      fwd_step<D, BM, 1, false, 1>(x, n + 1, sb, sa, o, m_ref, l_run, l_o, mx);
+    }
+    // last unmasked step (n is even); the tiles after it are all treated as
+    // masked, which is exact for full tiles too
+    fwd_step<D, BM, 0, false, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
+    ++n;
+  } else if (x.ntiles > 0) {
+    fwd_step<D, BM, 0, true, -1>(x, 0, sa, sb, o, m_ref, l_run, l_o, mx);
+    n = 1;
+  }
+  // masked tail from an odd n, unrolled by two like the steady state
+  while (n < x.ntiles) {
+    fwd_step<D, BM, 1, true, -1>(x, n, sb, sa, o, m_ref, l_run, l_o, mx);
+    if (++n >= x.ntiles) break;
+    fwd_step<D, BM, 0, true, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
+    ++n;
   }
 
   // epilogue: O = O / l, LSE = ln(2) * (m + log2 l)
@@ -303,10 +489,10 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
   const float lo_tot = add_xor32(l_o);
   if (qvalid) {
     const float inv = (lo_tot > 0.f) ? 1.f / lo_tot : 0.f;
-    uint16_t* orow = p.out + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * half;
+    uint16_t* orow = p.out + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * x.half;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) store_acc_row(orow + db * 32, o[db], inv);
-    if (WRITE_LSE && half == 0) {
+    for (int db = 0; db < T::DB; ++db) store_acc_row(orow + db * 32, o[db], inv);
+    if (WRITE_LSE && x.half == 0) {
       p.lse[(int64_t)h * p.total_q + cq + qi] =
           (l_tot > 0.f && m_ref != -INFINITY) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     }
@@ -315,8 +501,9 @@ __global__ __launch_bounds__(256, FwdTile<D>::WAVES_PER_SIMD) void fwd_kernel(Fw
 
 template <int D, bool CAUSAL, bool WRITE_LSE>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  using T = FwdTile<D>;
-  auto kern = fwd_kernel<D, CAUSAL, WRITE_LSE>;
+  constexpr int BM = FwdBlock<D>::BM;
+  using T = FwdCfg<D, BM>;
+  auto kern = fwd_kernel<D, BM, CAUSAL, WRITE_LSE>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -337,7 +524,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.levels = ceil_div(a.max_q, T::BM);
-  p.scale_log2 = fabsf(a.scale) * kLog2e;
+  // a zero (or tiny) scale becomes the smallest normal float: the scores then
+  // all map to exp2(~0) = 1 as for scale 0, while masked scores (-inf) stay -inf
+  p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
   p.neg_scale = a.scale < 0.f ? 1 : 0;
   const int r = a.Hq / a.Hkv;
   const int64_t grid = grid_for(a.total_q, a.num_seqs, T::BM, a.Hq, r);
@@ -366,7 +555,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
 }
 
 int64_t fwd_grid_size(int64_t total_q, int num_seqs, int Hq, int Hkv) {
-  return grid_for(total_q, num_seqs, 128, Hq, Hq / Hkv);
+  return grid_for(total_q, num_seqs, FwdBlock<128>::BM, Hq, Hq / Hkv);
 }
 
 }  // namespace av
