@@ -133,6 +133,124 @@ def time_graph(fn, steps: int, warmup: int):
     return time_steps(g.replay, steps, warmup)
 
 
+def time_graph_steady(fn, reps: int = 10, rounds: int = 5):
+    """Per-call ms of `reps` back-to-back calls captured in one HIP graph (median
+    over rounds): the steady-state rate without per-launch dispatch gaps."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    return statistics.median(per)
+
+
+def read_clocks():
+    """One `amd-smi metric` sample: socket power (W) and the graphics clock of
+    each XCD (MHz). Returns None when the tool is unavailable."""
+    import re
+    import subprocess
+
+    try:
+        txt = subprocess.run(["amd-smi", "metric"], capture_output=True, text=True, timeout=20).stdout
+    except Exception:  # pragma: no cover
+        return None
+    power = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    clks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", txt)]
+    if not clks:
+        return None
+    return {"power_w": float(power[0]) if power else None, "gfx_mhz": clks}
+
+
+def power_phase(fn, seconds: float = 4.0):
+    """Run fn back to back for `seconds` and sample clocks / power from a side
+    thread in the second half: the sustained operating point of this work."""
+    import threading
+
+    import torch
+
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        if stop.wait(seconds * 0.4):
+            return
+        while not stop.is_set() and len(samples) < 3:
+            r = read_clocks()
+            if r is None:
+                return
+            samples.append(r)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n += 10
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return {"error": "amd-smi metric gave no clock readings"}
+    clks = [c for s in samples for c in s["gfx_mhz"]]
+    pw = [s["power_w"] for s in samples if s["power_w"] is not None]
+    return {
+        "sclk_mhz_mean": sum(clks) / len(clks),
+        "sclk_mhz_min": min(clks),
+        "sclk_mhz_max": max(clks),
+        "sclk_mhz_nominal_max": 2400.0,
+        "socket_power_w": (sum(pw) / len(pw)) if pw else None,
+        "samples": len(samples),
+        "calls": n,
+        "source": "amd-smi metric (per-XCD GFX clocks, socket power) while the step runs back to back",
+    }
+
+
+def lse_ratio(wl, rounds: int = 5, reps: int = 10):
+    """Forward with and without the LSE output, timed in alternating rounds (the
+    pages' with / without LSE comparison); returns medians and their ratio."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl, with_dout=False).items()}
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+
+    def f(with_lse):
+        return lambda: A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                         wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal, out=out,
+                                         lse=lse if with_lse else None)
+
+    t_no, t_with = [], []
+    for _ in range(rounds):
+        t_no.append(time_graph_steady(f(False), reps, 1))
+        t_with.append(time_graph_steady(f(True), reps, 1))
+    no, wi = statistics.median(t_no), statistics.median(t_with)
+    fl = wl.accounted_fwd_flop()
+    return {"workload": wl.name, "no_lse_ms": no, "with_lse_ms": wi, "no_lse_over_with_lse": no / wi,
+            "no_lse_tflops": fl / (no * 1e-3) / 1e12, "with_lse_tflops": fl / (wi * 1e-3) / 1e12}
+
+
 def run_workload(wl, steps, warmup, profile=True):
     import torch
 
@@ -173,6 +291,9 @@ def run_workload(wl, steps, warmup, profile=True):
     # 2) the same work replayed from HIP graphs: no host launch overhead
     fwd_ms, fwd_per = time_graph(fwd, steps, warmup)
     step_ms, step_per = time_graph(step, steps, warmup)
+    res["fwd_ms_steady"] = time_graph_steady(fwd)
+    res["fwd_tflops_steady"] = fwd_flop / (res["fwd_ms_steady"] * 1e-3) / 1e12
+    res["_step_fn"] = step
     res["fwd_ms"] = fwd_ms
     res["fwd_ms_median"] = statistics.median(fwd_per)
     res["fwd_tflops"] = fwd_flop / (fwd_ms * 1e-3) / 1e12
@@ -320,10 +441,15 @@ def main(argv=None):
             r = run_workload(wl, max(3, a.steps // 4), 2, profile=True)
             secondary[wl.name] = {
                 "fwd_tflops": r["fwd_tflops"], "fwdbwd_tflops": r["fwdbwd_tflops"], "fwd_ms": r["fwd_ms"],
+                "fwd_ms_steady": r["fwd_ms_steady"], "fwd_tflops_steady": r["fwd_tflops_steady"],
                 "step_ms": r["step_ms"], "frac_fwd": r["fwd_tflops"] / PEAK_BF16_TFLOPS,
                 "frac_fwdbwd": r["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
                 "kernels": r["kernels"],
             }
+        log("forward with / without LSE, head_dim 64")
+        secondary["lse_ratio"] = lse_ratio(W.hd64_mha())
+    log("sustained clocks and power of the primary step")
+    clocks = power_phase(res.pop("_step_fn"))
     # dominant kernel of the step: the one with the largest total time
     kern = res["kernels"]
     dom = max(kern, key=lambda k: kern[k]["avg_ms"]) if kern else "attn_fwd"
@@ -363,6 +489,13 @@ def main(argv=None):
         "fwd_ms": res["fwd_ms"],
         "frac_of_peak_fwd": res["fwd_tflops"] / PEAK_BF16_TFLOPS,
         "frac_of_peak_fwdbwd": res["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
+        "fwd_ms_steady": res["fwd_ms_steady"],
+        "fwd_tflops_steady": res["fwd_tflops_steady"],
+        "clocks": clocks,
+        # the published peak assumes 2400 MHz; this is the peak at the clock the
+        # chip held (power-limited) while running the step
+        "frac_of_peak_fwdbwd_at_sclk": (res["fwdbwd_tflops"] / (PEAK_BF16_TFLOPS * clocks["sclk_mhz_mean"] / 2400.0)
+                                        if "sclk_mhz_mean" in clocks else None),
         "step_ms_median": res["step_ms_median"],
         "fwd_ms_median": res["fwd_ms_median"],
         "eager_step_ms": res["eager_step_ms"],
