@@ -402,6 +402,50 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
     return 0
 
 
+def all_configs_table(include_long: bool):
+    """Forward and forward+backward time of every config (fwd with LSE; steady
+    state, several calls per HIP graph): one JSON object per config on stdout."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    rows = []
+    for wl in W.all_configs():
+        if not include_long and wl.total_q > 40000:
+            continue
+        log(f"config {wl.name}")
+        d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+        mq, mk = wl.max_seqlen_q, wl.max_seqlen_k
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        ws = torch.empty(max(16, A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k,
+                                                                  wl.n_q_heads, wl.n_kv_heads, wl.head_dim)),
+                         dtype=torch.uint8, device="cuda:0")
+
+        def fwd():
+            A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
+                              wl.softmax_scale, wl.causal, out=out, lse=lse)
+
+        def step():
+            fwd()
+            A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"], mq,
+                              mk, wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        fl = wl.accounted_fwd_flop()
+        reps = max(1, min(10, int(2e13 / max(fl, 1.0))))
+        f_ms = time_graph_steady(fwd, reps, 3)
+        s_ms = time_graph_steady(step, reps, 3) if wl.backward else None
+        row = {"config": wl.name, **wl.describe(), "fwd_ms": f_ms, "fwd_tflops": fl / (f_ms * 1e-3) / 1e12,
+               "fwdbwd_ms": s_ms, "fwdbwd_tflops": (3.5 * fl / (s_ms * 1e-3) / 1e12) if s_ms else None}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del d, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -411,6 +455,9 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true", help="skip the extra workloads")
     ap.add_argument("--eager-only", action="store_true",
                     help="only run warmup + steps eager fwd+bwd steps of the main workload (for profilers) and exit")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="only time forward and forward+backward of every config (one JSON line each) and exit")
+    ap.add_argument("--long", action="store_true", help="with --all-configs: include the 64K and 128K sequences")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
@@ -427,6 +474,9 @@ def main(argv=None):
         return 1
     if a.copy_calibration:
         return copy_calibration()
+    if a.all_configs:
+        warm_gpu(1.0)
+        return all_configs_table(a.long)
     if a.eager_only:
         return eager_only(W.packed_16k(), a.steps, a.warmup)
     primary = W.packed_16k()

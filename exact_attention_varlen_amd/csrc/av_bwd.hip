@@ -243,7 +243,7 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fr[kk][j] = lds_ld16(src[j] + off.row_off[kk]);
+      for (int j = 0; j < 4; ++j) fr[kk][j] = lds_ld16(src[j] + off.row(kk));
     }
     // The fences keep the compiler from sinking each load to just before its
     // MFMA: the loads of k-step kk + PF are issued ahead of the MFMAs of kk.
@@ -252,7 +252,7 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + PF < KK) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fr[(kk + PF) % (PF + 1)][j] = lds_ld16(src[j] + off.row_off[kk + PF]);
+        for (int j = 0; j < 4; ++j) fr[(kk + PF) % (PF + 1)][j] = lds_ld16(src[j] + off.row(kk + PF));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -433,15 +433,15 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
   uint4 fr[PF + 1][2];
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    fr[kk][0] = lds_ld16(Ks + off.row_off[kk]);
-    fr[kk][1] = lds_ld16(Vs + off.row_off[kk]);
+    fr[kk][0] = lds_ld16(Ks + off.row(kk));
+    fr[kk][1] = lds_ld16(Vs + off.row(kk));
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (kk + PF < KK) {
-      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Ks + off.row_off[kk + PF]);
-      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Vs + off.row_off[kk + PF]);
+      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Ks + off.row(kk + PF));
+      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Vs + off.row(kk + PF));
     }
     __builtin_amdgcn_sched_barrier(0);
     s = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][0]), qf[kk], s);

@@ -54,12 +54,15 @@ namespace av {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int BM_>
+template <int D, int BM_, int BN_>
 struct FwdCfg {
-  using KV = RowTile<D, 64>;
+  using KV = RowTile<D, BN_>;
   static constexpr int BM = BM_;                      // query rows per workgroup
   static constexpr int WAVES = BM / 32;               // one wave per 32 rows
-  static constexpr int BN = 64;                       // keys per tile
+  static constexpr int BN = BN_;                      // keys per tile (32 or 64)
+  static constexpr int NA = BN / 32;                  // 32-key score accumulators per wave
+  static constexpr int NS = BN / 2;                   // scores per lane per tile
+  static constexpr int NJ = BN / 16;                  // 16-key k-steps of the PV product
   static constexpr int NT = 64 * WAVES;               // threads per workgroup
   static constexpr int ROW = KV::ROW;                 // bytes per key row in LDS
   static constexpr int TILE = KV::BYTES;              // bytes of one K or V tile
@@ -69,14 +72,22 @@ struct FwdCfg {
   static constexpr int KK = D / 16;                   // k-steps of S = K Q^T
   static constexpr int DB = D / 32;                   // 32-wide head-dim blocks of O
   static constexpr int PF = 2;                        // K operand prefetch distance
-  static constexpr int WAVES_PER_SIMD = 2;
+  // head_dim 256 needs more than 256 registers per lane (O alone is 128): one
+  // wave per SIMD, with the accumulators free to use AGPRs
+  static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
+  static constexpr int MIN_BLOCKS_PER_CU = WAVES_PER_SIMD * 4 / WAVES;
   static_assert(KV::DMAS % WAVES == 0, "tile copies must split evenly over the waves");
+  static_assert(LDS_BYTES * MIN_BLOCKS_PER_CU <= 160 * 1024, "LDS budget");
 };
 
-// The forward kernel's tile size for a head_dim (the grid depends on it).
+// The forward kernel's tile sizes for a head_dim (the grid depends on BM).
+// head_dim 256 uses 32-key tiles: the four K / V buffers then take 64 KB, so
+// every LDS operand address is a register plus a 16-bit immediate, and the
+// score state of the pipeline halves.
 template <int D>
 struct FwdBlock {
   static constexpr int BM = 128;
+  static constexpr int BN = (D <= 128) ? 64 : 32;
 };
 
 struct FwdParams {
@@ -96,6 +107,33 @@ struct FwdParams {
   int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
 };
 
+// O^T accumulation. At head_dim 256 (one wave per SIMD, O = 128 registers per
+// lane) the accumulators are pinned to AGPRs through an inline-asm MFMA: left
+// to itself the register allocator gives the loop-carried O different register
+// files in the two unrolled steps and copies all of it every step. The asm is
+// opaque to the compiler's hazard checks, so it carries its own: s_nop 1 before
+// the MFMA covers a VALU-written P operand, and o_fence() separates MFMA writes
+// of O from VALU accesses (rescale, epilogue) in both directions.
+template <int D>
+__device__ __forceinline__ void pv_mfma(f32x16& o, const bf16x8& v, const bf16x8& p) {
+  if constexpr (D == 256) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+  } else {
+    o = mfma32x32x16(v, p, o);
+  }
+}
+
+template <int D, int DB>
+__device__ __forceinline__ void o_fence(f32x16 (&o)[DB]) {
+  if constexpr (D == 256) {
+    static_assert(DB == 8, "fence written for 8 accumulators");
+    // 24 wait states: more than an MFMA result needs before a VALU read, and
+    // than a VALU write needs before an MFMA reads it as the accumulator
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+  }
+}
+
 // Descriptor of the same rows starting `bytes` further on.
 __device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, uint32_t bytes) {
   const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + bytes;
@@ -108,9 +146,9 @@ __device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, uint32_t bytes) {
 }
 
 // Per-wave state of the forward item that the pipeline steps share.
-template <int D, int BM>
+template <int D, int BM, int BN>
 struct FwdCtx {
-  using T = FwdCfg<D, BM>;
+  using T = FwdCfg<D, BM, BN>;
   const lds_char* lds;
   uint32_t lds0;
   i32x4 rk, rv;          // K / V rows of this (sequence, KV head), from key 0
@@ -125,9 +163,9 @@ struct FwdCtx {
 };
 
 // Copy this wave's share of a 64-row tile (rows row0 ..) into LDS at `dst`.
-template <int D, int BM>
-__device__ __forceinline__ void issue_tile(const FwdCtx<D, BM>& x, uint32_t dst, const i32x4& rsrc, int row0) {
-  using T = FwdCfg<D, BM>;
+template <int D, int BM, int BN>
+__device__ __forceinline__ void issue_tile(const FwdCtx<D, BM, BN>& x, uint32_t dst, const i32x4& rsrc, int row0) {
+  using T = FwdCfg<D, BM, BN>;
   const i32x4 r = rsrc_advance(rsrc, (uint32_t)row0 * (x.tile_bytes / T::BN));
 #pragma unroll
   for (int i = 0; i < T::DMA; ++i) lds_dma16(r, dst + (x.wave * T::DMA + i) * 1024, x.voff[i]);
@@ -135,8 +173,8 @@ __device__ __forceinline__ void issue_tile(const FwdCtx<D, BM>& x, uint32_t dst,
 
 // Score register v of accumulator a (a = 0: keys 0..31 of the tile, a = 1:
 // keys 32..63) is key 32 a + 16 (v / 8) + 8 half + v % 8.
-template <int D, int BM>
-__device__ __forceinline__ void mask_scores(const FwdCtx<D, BM>& x, f32x16& s, int first_key) {
+template <int D, int BM, int BN>
+__device__ __forceinline__ void mask_scores(const FwdCtx<D, BM, BN>& x, f32x16& s, int first_key) {
   const int t = x.kvis_end - first_key - 8 * x.half;  // visible iff 16 (v / 8) + v % 8 < t
 #pragma unroll
   for (int v = 0; v < 16; ++v) s[v] = (16 * (v >> 3) + (v & 7) < t) ? s[v] : -INFINITY;
@@ -155,7 +193,7 @@ __device__ __forceinline__ float max16(const f32x16& s, float m) {
 // score of a pair, packs the pair to bf16 (and, on masked tiles, splits it
 // into hi / lo parts). Issuing the exponentials one MFMA ahead of their use
 // hides the latency of the transcendental unit.
-__device__ __forceinline__ void exp_issue(const f32x16 (&sc)[2], int i, float c, float nm, float* pe) {
+__device__ __forceinline__ void exp_issue(const f32x16* sc, int i, float c, float nm, float* pe) {
   pe[i] = fast_exp2(__builtin_fmaf(sc[i >> 4][i & 15], c, nm));
 }
 
@@ -179,34 +217,35 @@ __device__ __forceinline__ void exp_finish(int i, float& l_run, float& l_o, cons
 }
 
 template <bool SPLIT>
-__device__ __forceinline__ void exp_score(const f32x16 (&sc)[2], int i, float c, float nm, float& l_run, float& l_o,
+__device__ __forceinline__ void exp_score(const f32x16* sc, int i, float c, float nm, float& l_run, float& l_o,
                                           float* pe, uint32_t* ph, uint32_t* pl) {
   exp_issue(sc, i, c, nm, pe);
   exp_finish<SPLIT>(i, l_run, l_o, pe, ph, pl);
 }
 
-// S^T of one 64-key tile (both 32-key halves) for this wave's 32 queries.
-template <int D, int BM>
-__device__ __forceinline__ void qk_tile(const FwdCtx<D, BM>& x, const lds_char* Ks, f32x16 (&s)[2]) {
-  using T = FwdCfg<D, BM>;
-  uint4 fr[T::PF + 1][2];
+// S^T of one key tile (NA accumulators of 32 keys) for this wave's 32 queries.
+template <int D, int BM, int BN>
+__device__ __forceinline__ void qk_tile(const FwdCtx<D, BM, BN>& x, const lds_char* Ks,
+                                        f32x16 (&s)[FwdCfg<D, BM, BN>::NA]) {
+  using T = FwdCfg<D, BM, BN>;
+  constexpr int NA = T::NA, PF = T::PF;
+  uint4 fr[PF + 1][NA];
 #pragma unroll
-  for (int kk = 0; kk < T::PF; ++kk) {
-    fr[kk][0] = lds_ld16(Ks + x.off.row_off[kk]);
-    fr[kk][1] = lds_ld16(Ks + 32 * T::ROW + x.off.row_off[kk]);
+  for (int kk = 0; kk < PF; ++kk) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a) fr[kk][a] = lds_ld16(Ks + 32 * a * T::ROW + x.off.row(kk));
   }
-  s[0] = zero16();
-  s[1] = zero16();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < T::KK; ++kk) {
-    if (kk + T::PF < T::KK) {
-      fr[(kk + T::PF) % (T::PF + 1)][0] = lds_ld16(Ks + x.off.row_off[kk + T::PF]);
-      fr[(kk + T::PF) % (T::PF + 1)][1] = lds_ld16(Ks + 32 * T::ROW + x.off.row_off[kk + T::PF]);
+    if (kk + PF < T::KK) {
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        fr[(kk + PF) % (PF + 1)][a] = lds_ld16(Ks + 32 * a * T::ROW + x.off.row(kk + PF));
     }
     __builtin_amdgcn_sched_barrier(0);
-    s[0] = mfma32x32x16(as_bf16x8(fr[kk % (T::PF + 1)][0]), x.qf[kk], s[0]);
-    s[1] = mfma32x32x16(as_bf16x8(fr[kk % (T::PF + 1)][1]), x.qf[kk], s[1]);
+#pragma unroll
+    for (int a = 0; a < NA; ++a) s[a] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][a]), x.qf[kk], kk ? s[a] : zero16());
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -218,12 +257,12 @@ __device__ __forceinline__ void qk_tile(const FwdCtx<D, BM>& x, const lds_char* 
 //        one, is masked (tiles treated as masked may well be full).
 // On entry sc holds S(n) and mx this lane's max over it; on return sn holds
 // S(n + 1) and mx its max (when tile n + 1 exists).
-template <int D, int BM, int PAR, bool MC, int NX>
-__device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f32x16 (&sc)[2], f32x16 (&sn)[2],
-                                         f32x16 (&o)[FwdCfg<D, BM>::DB], float& m_ref, float& l_run, float& l_o,
-                                         float& mx) {
-  using T = FwdCfg<D, BM>;
-  constexpr int KK = T::KK, PF = T::PF, DB = T::DB;
+template <int D, int BM, int BN, int PAR, bool MC, int NX>
+__device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN>& x, int n, const f32x16 (&sc)[FwdCfg<D, BM, BN>::NA],
+                                         f32x16 (&sn)[FwdCfg<D, BM, BN>::NA], f32x16 (&o)[FwdCfg<D, BM, BN>::DB],
+                                         float& m_ref, float& l_run, float& l_o, float& mx) {
+  using T = FwdCfg<D, BM, BN>;
+  constexpr int KK = T::KK, PF = T::PF, DB = T::DB, NA = T::NA, NS = T::NS, NJ = T::NJ;
   constexpr int par = PAR;
   const bool next = NX > 0 || n + 1 < x.ntiles;
 
@@ -237,12 +276,12 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f3
   const lds_char* Kn = x.lds + (par ^ 1) * T::TILE;         // K(n + 1)
   const lds_char* Vc = x.lds + T::VBASE + par * T::TILE;    // V(n)
 
-  uint4 fr[PF + 1][2];
+  uint4 fr[PF + 1][NA];
   if (next) {
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      fr[kk][0] = lds_ld16(Kn + x.off.row_off[kk]);
-      fr[kk][1] = lds_ld16(Kn + 32 * T::ROW + x.off.row_off[kk]);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) fr[kk][a] = lds_ld16(Kn + 32 * a * T::ROW + x.off.row(kk));
     }
   }
 
@@ -259,11 +298,13 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f3
       m_ref = mn;
       l_run *= alpha;
       l_o *= alpha;
+      o_fence<D>(o);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
       }
+      o_fence<D>(o);
     }
   }
   const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
@@ -272,22 +313,24 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f3
   // VALU work is spread in small shares between consecutive MFMAs: each share
   // issues while the MFMA before it executes.
   //
-  // phase B: S(n + 1) on the matrix cores (2 KK MFMAs); on the VALU, P(n)
+  // phase B: S(n + 1) on the matrix cores (NA KK MFMAs); on the VALU, P(n)
   // scores 0 .. SB - 1 (unmasked tile) or 0 .. 7 (masked tile: its hi / lo
   // parts are formed one PV k-step ahead in phase C instead, which keeps fewer
-  // registers live)
-  constexpr int SB = MC ? 8 : 18;
-  constexpr int NB = 2 * KK;
-  float pe[32];
-  uint32_t ph[16], pl[16];
+  // registers live). The last share of phase B holds no score of PV k-step 0.
+  constexpr int SB = MC ? 8 : NS * 9 / 16;
+  constexpr int NB = NA * KK;
+  static_assert(MC || SB * (NB - 1) / NB >= 8, "phase B's last share must not hold k-step 0");
+  float pe[NS];
+  uint32_t ph[NS / 2], pl[NS / 2];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
-    const int kk = m >> 1, a = m & 1;
+    const int kk = m / NA, a = m % NA;
     if (next) {
       if (a == 0 && kk + PF < KK) {
-        fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Kn + x.off.row_off[kk + PF]);
-        fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Kn + 32 * T::ROW + x.off.row_off[kk + PF]);
+#pragma unroll
+        for (int b = 0; b < NA; ++b)
+          fr[(kk + PF) % (PF + 1)][b] = lds_ld16(Kn + 32 * b * T::ROW + x.off.row(kk + PF));
       }
       sn[a] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][a]), x.qf[kk], kk ? sn[a] : zero16());
     }
@@ -308,10 +351,15 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f3
 
   // phase C: O^T += V(n)^T P(n)^T on the matrix cores, one MFMA unit (PV
   // k-step j, head-dim block db) at a time with the V^T operands read RV - 1
-  // units ahead. On the VALU: the units of k-steps 0 and 1 finish P(n)
-  // (scores SB .. 31), those of k-steps 2 and 3 take the max of S(n + 1); a
-  // masked tile instead forms the next k-step's P during each k-step.
-  constexpr int NU = 4 * DB, RV = 3;
+  // units ahead. On the VALU, unmasked tile: the first UC units finish P(n)
+  // (scores SB .. NS - 1, each share finished one unit later, the first unit
+  // finishing phase B's last share), all of it before the first unit of k-step
+  // NJ / 2; the units of the second half of the k-steps take the max of
+  // S(n + 1). A masked tile instead forms the next k-step's P during each k-step.
+  constexpr int NU = NJ * DB, RV = 3;
+  constexpr int UH = (NJ / 2) * DB;  // first unit of the second half
+  constexpr int UC = UH - 1;         // units that issue P(n) shares
+  static_assert(MC || SB >= 8 * (NJ / 2), "phase C's shares must belong to the second half of the k-steps");
   bf16x8 va[RV];
 #pragma unroll
   for (int u = 0; u < RV - 1; ++u) va[u] = tr_operand<D>(Vc + 16 * (u / DB) * T::ROW, x.off, u % DB);
@@ -325,33 +373,31 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f3
     }
     __builtin_amdgcn_sched_barrier(0);
     const bf16x8 pb = as_bf16x8(make_uint4(ph[4 * j], ph[4 * j + 1], ph[4 * j + 2], ph[4 * j + 3]));
-    o[db] = mfma32x32x16(va[u % RV], pb, o[db]);
+    pv_mfma<D>(o[db], va[u % RV], pb);
     if (MC) {
       const bf16x8 pq = as_bf16x8(make_uint4(pl[4 * j], pl[4 * j + 1], pl[4 * j + 2], pl[4 * j + 3]));
-      o[db] = mfma32x32x16(va[u % RV], pq, o[db]);
-      if (j + 1 < 4) {
+      pv_mfma<D>(o[db], va[u % RV], pq);
+      if (j + 1 < NJ) {
 #pragma unroll
         for (int i = 8 * (j + 1) + 8 * db / DB; i < 8 * (j + 1) + 8 * (db + 1) / DB; ++i)
           exp_score<MC>(sc, i, x.c, nm, l_run, l_o, pe, ph, pl);
       }
-    } else if (u <= 2 * DB) {
-      // scores SB .. 31 over the units of k-steps 0 and 1, each share finished
-      // one unit later (the first unit finishes phase B's last share)
-      if (u < 2 * DB) {
+    } else if (u <= UC) {
+      if (u < UC) {
 #pragma unroll
-        for (int i = SB + (32 - SB) * u / (2 * DB); i < SB + (32 - SB) * (u + 1) / (2 * DB); ++i)
-          exp_issue(sc, i, x.c, nm, pe);
+        for (int i = SB + (NS - SB) * u / UC; i < SB + (NS - SB) * (u + 1) / UC; ++i) exp_issue(sc, i, x.c, nm, pe);
       }
-      const int f0 = u ? SB + (32 - SB) * (u - 1) / (2 * DB) : SB * (NB - 1) / NB;
-      const int f1 = u ? SB + (32 - SB) * u / (2 * DB) : SB;
+      const int f0 = u ? SB + (NS - SB) * (u - 1) / UC : SB * (NB - 1) / NB;
+      const int f1 = u ? SB + (NS - SB) * u / UC : SB;
 #pragma unroll
       for (int i = f0; i < f1; ++i) exp_finish<MC>(i, l_run, l_o, pe, ph, pl);
     }
-    if (next && u >= 2 * DB) {
-      // mask and max of S(n + 1): 32 values spread over the last 2 DB units
-      const int e = u - 2 * DB;
+    if (next && u >= UH) {
+      // mask and max of S(n + 1): NA x 16 values spread over the units of the
+      // second half of the k-steps
+      const int e = u - UH;
 #pragma unroll
-      for (int i = 32 * e / (2 * DB); i < 32 * (e + 1) / (2 * DB); ++i) {
+      for (int i = 16 * NA * e / (NU - UH); i < 16 * NA * (e + 1) / (NU - UH); ++i) {
         const int v = i & 15;
         if (NX < 0) {
           const int t = x.kvis_end - (n + 1) * T::BN - 32 * (i >> 4) - 8 * x.half;
@@ -366,9 +412,11 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM>& x, int n, const f3
   mx = mxa;  // meaningless when there is no tile n + 1
 }
 
-template <int D, int BM, bool CAUSAL, bool WRITE_LSE>
-__global__ __launch_bounds__((FwdCfg<D, BM>::NT), (FwdCfg<D, BM>::WAVES_PER_SIMD)) void fwd_kernel(FwdParams p) {
-  using T = FwdCfg<D, BM>;
+template <int D, int BM, int BN, bool CAUSAL, bool WRITE_LSE>
+__global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void fwd_kernel(
+    FwdParams p) {
+  using T = FwdCfg<D, BM, BN>;
+  constexpr int NA = T::NA;
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int r = p.Hq / p.Hkv;
@@ -384,7 +432,7 @@ __global__ __launch_bounds__((FwdCfg<D, BM>::NT), (FwdCfg<D, BM>::WAVES_PER_SIMD
   const int ck = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - ck;
 
-  FwdCtx<D, BM> x;
+  FwdCtx<D, BM, BN> x;
   x.lds = (const lds_char*)smem;
   x.lds0 = lds_addr((lds_char*)smem);
   const int tid = threadIdx.x;
@@ -447,17 +495,18 @@ __global__ __launch_bounds__((FwdCfg<D, BM>::NT), (FwdCfg<D, BM>::WAVES_PER_SIMD
   float l_run = 0.f;  // sum of P (fp32): the LSE
   float l_o = 0.f;    // sum of the P values as they enter the PV product: normalises O
   float mx = -INFINITY;
-  f32x16 sa[2], sb[2];
+  f32x16 sa[NA], sb[NA];
 
   if (x.ntiles > 0) {
     wait_vmcnt<0>();
     lds_barrier();
     qk_tile(x, x.lds, sa);
     if (nfull == 0) {
-      mask_scores(x, sa[0], 0);
-      mask_scores(x, sa[1], 32);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) mask_scores(x, sa[a], 32 * a);
     }
-    mx = max16(sa[1], max16(sa[0], mx));
+#pragma unroll
+    for (int a = 0; a < NA; ++a) mx = max16(sa[a], mx);
   }
 
   // Steady state, unrolled by two so the buffer parity is a constant: tile n
@@ -465,26 +514,27 @@ __global__ __launch_bounds__((FwdCfg<D, BM>::NT), (FwdCfg<D, BM>::WAVES_PER_SIMD
   int n = 0;
   if (nfull > 0) {
     for (; n + 3 <= nfull; n += 2) {
-      fwd_step<D, BM, 0, false, 1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
-      fwd_step<D, BM, 1, false, 1>(x, n + 1, sb, sa, o, m_ref, l_run, l_o, mx);
+      fwd_step<D, BM, BN, 0, false, 1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
+      fwd_step<D, BM, BN, 1, false, 1>(x, n + 1, sb, sa, o, m_ref, l_run, l_o, mx);
     }
     // last unmasked step (n is even); the tiles after it are all treated as
     // masked, which is exact for full tiles too
-    fwd_step<D, BM, 0, false, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
+    fwd_step<D, BM, BN, 0, false, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
     ++n;
   } else if (x.ntiles > 0) {
-    fwd_step<D, BM, 0, true, -1>(x, 0, sa, sb, o, m_ref, l_run, l_o, mx);
+    fwd_step<D, BM, BN, 0, true, -1>(x, 0, sa, sb, o, m_ref, l_run, l_o, mx);
     n = 1;
   }
   // masked tail from an odd n, unrolled by two like the steady state
   while (n < x.ntiles) {
-    fwd_step<D, BM, 1, true, -1>(x, n, sb, sa, o, m_ref, l_run, l_o, mx);
+    fwd_step<D, BM, BN, 1, true, -1>(x, n, sb, sa, o, m_ref, l_run, l_o, mx);
     if (++n >= x.ntiles) break;
-    fwd_step<D, BM, 0, true, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
+    fwd_step<D, BM, BN, 0, true, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
     ++n;
   }
 
   // epilogue: O = O / l, LSE = ln(2) * (m + log2 l)
+  o_fence<D>(o);
   const float l_tot = add_xor32(l_run);
   const float lo_tot = add_xor32(l_o);
   if (qvalid) {
@@ -501,9 +551,9 @@ __global__ __launch_bounds__((FwdCfg<D, BM>::NT), (FwdCfg<D, BM>::WAVES_PER_SIMD
 
 template <int D, bool CAUSAL, bool WRITE_LSE>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  constexpr int BM = FwdBlock<D>::BM;
-  using T = FwdCfg<D, BM>;
-  auto kern = fwd_kernel<D, BM, CAUSAL, WRITE_LSE>;
+  constexpr int BM = FwdBlock<D>::BM, BN = FwdBlock<D>::BN;
+  using T = FwdCfg<D, BM, BN>;
+  auto kern = fwd_kernel<D, BM, BN, CAUSAL, WRITE_LSE>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -549,7 +599,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
   switch (a.D) {
     case 64: return launch_fwd_d<64>(a);
     case 128: return launch_fwd_d<128>(a);
-    case 256: return launch_fwd_d256(a);
+    case 256: return launch_fwd_d<256>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -42,7 +42,6 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_fwd_d256(const FwdArgs& a);  // av_fwd_d256.hip
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_schedule_probe(const int32_t* cu_q, int num_seqs, int max_q, int block_m, int32_t* seq_out,
                                  int32_t* block_out, int count, void* stream);

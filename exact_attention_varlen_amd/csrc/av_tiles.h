@@ -50,11 +50,20 @@ __device__ __forceinline__ i32x4 head_rows_rsrc(const uint16_t* first_row_head, 
   return make_rsrc(first_row_head, nbytes);
 }
 
+// Only the offsets of the first 16 chunks of a row are stored: the swizzle
+// changes the low 4 bits of a chunk index only, so chunk c + 16 lies 256 bytes
+// after chunk c (head_dim 256 has 32 chunks per row). row(kk) and tr(db) add
+// that part as an immediate.
 template <int D>
 struct OperandOffsets {
-  uint32_t row_off[D / 16];
-  uint32_t tr_off0[D / 32];
-  uint32_t tr_off1[D / 32];
+  static constexpr int NR = (D / 16 < 8) ? D / 16 : 8;
+  static constexpr int NT = (D / 32 < 4) ? D / 32 : 4;
+  uint32_t row_off[NR];
+  uint32_t tr_off0[NT];
+  uint32_t tr_off1[NT];
+  __device__ __forceinline__ uint32_t row(int kk) const { return row_off[kk % NR] + 256u * (kk / NR); }
+  __device__ __forceinline__ uint32_t tr0(int db) const { return tr_off0[db % NT] + 256u * (db / NT); }
+  __device__ __forceinline__ uint32_t tr1(int db) const { return tr_off1[db % NT] + 256u * (db / NT); }
 };
 
 template <int D>
@@ -64,7 +73,7 @@ __device__ __forceinline__ void operand_offsets(OperandOffsets<D>& o, int lane) 
   const int half = lane >> 5;
   const int row = kperm(col);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) o.row_off[kk] = row * ROW + (((2 * kk + half) ^ swz<D>(row)) << 4);
+  for (int kk = 0; kk < OperandOffsets<D>::NR; ++kk) o.row_off[kk] = row * ROW + (((2 * kk + half) ^ swz<D>(row)) << 4);
   const int grp = lane >> 4;  // 16-lane group: head-dim half (grp & 1) and k-group (grp >> 1)
   const int i = lane & 15;
   const int j = i >> 2;  // row within the 4-row read
@@ -72,7 +81,7 @@ __device__ __forceinline__ void operand_offsets(OperandOffsets<D>& o, int lane) 
   const int r0 = 8 * half + j;
   const int r1 = r0 + 4;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < OperandOffsets<D>::NT; ++db) {
     const int chunk = db * 4 + 2 * (grp & 1) + (cc >> 1);
     o.tr_off0[db] = r0 * ROW + ((chunk ^ swz<D>(r0)) << 4) + (cc & 1) * 8;
     o.tr_off1[db] = r1 * ROW + ((chunk ^ swz<D>(r1)) << 4) + (cc & 1) * 8;
@@ -83,8 +92,8 @@ __device__ __forceinline__ void operand_offsets(OperandOffsets<D>& o, int lane) 
 // at `tile`, where rows0 = 16 s for k-step s of a 32-row block).
 template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const lds_char* rows0, const OperandOffsets<D>& o, int db) {
-  const uint2 lo = lds_read_tr4(rows0 + o.tr_off0[db]);
-  const uint2 hi = lds_read_tr4(rows0 + o.tr_off1[db]);
+  const uint2 lo = lds_read_tr4(rows0 + o.tr0(db));
+  const uint2 hi = lds_read_tr4(rows0 + o.tr1(db));
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
