@@ -93,11 +93,8 @@ int attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* 
 size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t head_dim) {
   (void)num_seqs;
-  (void)total_k;
-  (void)n_kv_heads;
-  (void)head_dim;
-  if (total_q < 0 || n_q_heads <= 0) return 0;
-  return av::bwd_workspace_bytes(total_q, n_q_heads);
+  if (total_q < 0 || total_k < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return 0;
+  return av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
 }
 
 int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -113,7 +110,7 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* 
   if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4))
     return ATTN_VARLEN_ERR_MISALIGNED;
-  const size_t need = av::bwd_workspace_bytes(total_q, n_q_heads);
+  const size_t need = av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
   if (!workspace || workspace_bytes < need) return ATTN_VARLEN_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
   if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;

@@ -21,7 +21,7 @@
 //                       head and loops over the visible 64-key tiles in
 //                       ascending order: dQ += dS K.
 // dQ and dK are scaled by softmax_scale at the end. Head dim 256 uses the
-// register-staged main kernels of av_bwd_d256.hip after the same preprocess.
+// main kernels of av_bwd_d256.hip after the same preprocess.
 //
 // gfx950 mapping (as in the forward): Q/dO tiles (dK/dV kernel) and K/V tiles
 // (dQ kernel) go HBM -> LDS by range-checked buffer-load DMA, double-buffered,
@@ -31,21 +31,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "av_bwd.h"
 #include "av_common.h"
 #include "av_launch.h"
 #include "av_tiles.h"
 
 namespace av {
 
-hipError_t launch_bwd_main_d256(const BwdArgs& a);  // av_bwd_d256.hip
+hipError_t launch_bwd_main_d256(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv,
+                                int splits);  // av_bwd_d256.hip
 
-// workspace layout: Delta [Hq][total_q] fp32, then lse2 [Hq][total_q] fp32
-static inline size_t ws_plane_bytes(int64_t total_q, int Hq) {
-  const size_t b = (size_t)total_q * (size_t)Hq * sizeof(float);
-  return (b + 255) / 256 * 256;
+size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D) {
+  const int splits = dkdv_splits(total_k, Hq, Hkv, D);
+  return 2 * ws_plane_bytes(total_q, Hq) + 2 * ws_part_bytes(total_k, Hkv, D, splits);
 }
-
-size_t bwd_workspace_bytes(int64_t total_q, int Hq) { return 2 * ws_plane_bytes(total_q, Hq); }
 
 // ---------------------------------------------------------------------------
 // 1. preprocess
@@ -88,39 +87,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
       lse2[idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
   }
-}
-
-struct BwdParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const uint16_t* dout;
-  const float* delta;
-  const float* lse2;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  uint16_t* dq;
-  uint16_t* dk;
-  uint16_t* dv;
-  int num_seqs;
-  int total_q;
-  int Hq;
-  int Hkv;
-  int levels;        // query-block or key-block levels, per kernel
-  float scale;       // softmax_scale
-  float scale_log2;  // softmax_scale * log2(e)
-};
-
-// Copy of 64 consecutive fp32 row values (rows row0 .. row0 + 63 of one head's
-// plane) into LDS at `dst`; rows past the sequence read as 0.
-__device__ __forceinline__ void rows64_f32_dma(uint32_t dst, const i32x4& rsrc, int row0, int lane) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds"
-      :
-      : "s"(dst), "v"((uint32_t)(row0 + lane) * 4u), "s"(rsrc)
-      : "memory", "m0");
 }
 
 // ---------------------------------------------------------------------------
@@ -620,10 +586,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
+  p.part_dk = nullptr;
+  p.part_dv = nullptr;
   p.num_seqs = f.num_seqs;
   p.total_q = (int)f.total_q;
+  p.total_k = (int)f.total_k;
   p.Hq = f.Hq;
   p.Hkv = f.Hkv;
+  p.splits = 1;
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
 
@@ -672,7 +642,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if constexpr (D == 256) {
-    return launch_bwd_main_d256(a);
+    const int splits = dkdv_splits(a.f.total_k, a.f.Hq, a.f.Hkv, D);
+    char* part = reinterpret_cast<char*>(a.delta) + 2 * ws_plane_bytes(a.f.total_q, a.f.Hq);
+    const size_t pb = ws_part_bytes(a.f.total_k, a.f.Hkv, D, splits);
+    return launch_bwd_main_d256(a, lse2, splits > 1 ? reinterpret_cast<float*>(part) : nullptr,
+                                splits > 1 ? reinterpret_cast<float*>(part + pb) : nullptr, splits);
   } else {
     return a.f.causal ? launch_bwd_t<D, true>(a, lse2) : launch_bwd_t<D, false>(a, lse2);
   }

@@ -1,251 +1,253 @@
-// av_bwd_d256.hip — backward kernels for head_dim 256: gradients of
-// sum(dout * out) for exact varlen GQA attention, deterministic (no atomics,
-// every sum in a fixed order). Register-staged variant: Q/dO (resp. K/V) tiles
-// go through VGPRs into LDS in row-major and transposed copies.
+// av_bwd_d256.hip — backward main kernels for head dim 256: the dK / dV and dQ
+// products of the FlashAttention repository guide's backward (Backward
+// Kernels), after the preprocess kernel of av_bwd.hip (Delta, lse2).
 //
-// The FlashAttention repository guide (Backward Kernels) splits the backward
-// into a preprocess kernel, a main kernel and a postprocess kernel. Here:
-//  1. bwd_delta_kernel   Delta_i = sum_d dO_id * O_id per query row and head
-//                        (fp32), written to the caller's workspace.
-//  2. bwd_dkdv_kernel    key-stationary: a workgroup owns 128 keys of one KV
-//                        head and loops over every query head of that head's
-//                        group and every query block that can see the keys,
-//                        recomputing P from the LSE:
-//                          S = Q K^T, P = exp(S*scale - LSE), dP = dO V^T,
-//                          dS = P * (dP - Delta), dV += P^T dO, dK += dS^T Q.
-//                        The sum over the group's query heads happens in fp32
-//                        registers in a fixed order: no atomics and no scratch.
-//  3. bwd_dq_kernel      query-stationary: a workgroup owns 128 query rows of
-//                        one head and loops over the visible key tiles in
-//                        ascending order: dQ += dS K (fixed order).
-// dQ and dK are scaled by softmax_scale at the end.
+// At head_dim 256 a wave's accumulators alone take 256 (dK + dV for 32 keys) or
+// 128 (dQ for 32 queries) registers per lane, so both kernels run one wave per
+// SIMD with the accumulators pinned to AGPRs (inline-asm MFMA: left to itself
+// the register allocator moves loop-carried accumulators between register
+// files). The asm is opaque to the compiler's hazard checks, so it carries its
+// own padding: s_nop 1 before each MFMA covers a VALU-written operand, and
+// acc_fence() separates MFMA writes of the accumulators from their VALU reads.
 //
-// MFMA lane maps and row permutations are those of av_common.h; the
-// transposed operands (Q^T, dO^T for the key-stationary kernel, K^T for the
-// query-stationary kernel) are written transposed into LDS at staging time.
+//  bwd_dkdv256_kernel  key-stationary: a workgroup owns 128 keys (32 per wave)
+//                      of one KV head and one split of that head's query
+//                      heads, and loops over every 32-row query block that can
+//                      see the keys: S = Q K^T, P = exp2(S scale log2 e - lse2),
+//                      dP = dO V^T, dS = P (dP - Delta), dV += P^T dO,
+//                      dK += dS^T Q. K^T stays in VGPRs, the item's V block is
+//                      copied to LDS once (64 KB; registers cannot hold it next
+//                      to the 256 accumulator registers); Q / dO tiles and the
+//                      rows' lse2 / Delta arrive by buffer-load DMA,
+//                      double-buffered. With one split the group sum is done in
+//                      registers and dK / dV are written directly; with more
+//                      (few key blocks per KV head, so too few work items to
+//                      fill the chip or to balance causal work), each split
+//                      writes fp32 partial sums that bwd_dkdv_reduce_kernel adds
+//                      in split order: deterministic, no atomics.
+//  bwd_dq256_kernel    query-stationary: a workgroup owns 128 query rows (32 per
+//                      wave) of one head and loops over the visible 32-key tiles
+//                      in ascending order: dQ += dS K. 32-key tiles keep the two
+//                      double-buffered K / V stages within 64 KB, so every LDS
+//                      operand address is a register plus an immediate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "av_bwd.h"
 #include "av_common.h"
 #include "av_launch.h"
+#include "av_tiles.h"
 
 namespace av {
 
-// ---------------------------------------------------------------------------
-// staging helpers: 4 consecutive rows x 16 bytes per unit
-// ---------------------------------------------------------------------------
+namespace {
 
-struct Rows4V {
-  uint4 r[4];
-};
+constexpr int kD = 256;
+constexpr int kKK = kD / 16;  // k-steps of a contraction over head_dim
+constexpr int kDB = kD / 32;  // 32-wide head-dim blocks of an accumulator
 
-__device__ __forceinline__ void rows4_load_v(Rows4V& x, const uint16_t* base, int64_t pitch, int row0, int nvalid,
-                                           int col8) {
+// acc += A B with the accumulator in AGPRs (see the file comment).
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// acc (+)= A B with the accumulator pinned to VGPRs (the S / dP products, which
+// the VALU reads next); the first k-step starts from zero. vgpr_fence() gives
+// an MFMA result the wait states it needs before the VALU reads it.
+__device__ __forceinline__ void mfma_vgpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void vgpr_fence(f32x16& a, f32x16& b) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
+
+// 24 wait states, with the accumulators as operands so that no read or write
+// of them moves across: more than an MFMA result needs before a VALU read.
+__device__ __forceinline__ void acc_fence(f32x16 (&a)[kDB]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]));
+}
+
+// fp32 twin of store_acc_row: register v of lane l is head-dim 8 (v / 4) +
+// 4 (l / 32) + v % 4 of the block; the caller adds 4 (l / 32).
+__device__ __forceinline__ void store_acc_row_f32(float* row_db, const f32x16& a) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) x.r[e] = (row0 + e < nvalid) ? ld16(base + (int64_t)(row0 + e) * pitch + col8) : zero_u4();
-}
-
-// rows (row0 .. row0+3) of 8 columns (col8 .. col8+7) -> dst[row][col] row-major
-__device__ __forceinline__ void rows4_store_v(const Rows4V& x, uint16_t* dst, int pitch, int row0, int col8) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) st16(dst + (row0 + e) * pitch + col8, x.r[e]);
-}
-
-// rows (row0 .. row0+3) of 8 columns -> dst[col][row] (transposed), 4 rows per 8-byte write
-__device__ __forceinline__ void rows4_store_t_v(const Rows4V& x, uint16_t* dst, int pitch, int row0, int col8) {
-  const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&x.r[0]);
-  const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&x.r[1]);
-  const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&x.r[2]);
-  const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&x.r[3]);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint2 lo, hi;
-    lo.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-    lo.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-    hi.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-    hi.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-    const int c = col8 + 2 * w;
-    *reinterpret_cast<uint2*>(dst + c * pitch + row0) = lo;
-    *reinterpret_cast<uint2*>(dst + (c + 1) * pitch + row0) = hi;
-  }
-}
-
-__device__ __forceinline__ float dot8_bf16_v(const uint4& a, const uint4& b) {
-  float acc = 0.f;
-  acc += bf16_lo(a.x) * bf16_lo(b.x);
-  acc += bf16_hi(a.x) * bf16_hi(b.x);
-  acc += bf16_lo(a.y) * bf16_lo(b.y);
-  acc += bf16_hi(a.y) * bf16_hi(b.y);
-  acc += bf16_lo(a.z) * bf16_lo(b.z);
-  acc += bf16_hi(a.z) * bf16_hi(b.z);
-  acc += bf16_lo(a.w) * bf16_lo(b.w);
-  acc += bf16_hi(a.w) * bf16_hi(b.w);
-  return acc;
+  for (int gq = 0; gq < 4; ++gq)
+    *reinterpret_cast<float4*>(row_db + 8 * gq) = make_float4(a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]);
 }
 
 // ---------------------------------------------------------------------------
-// common parameters
+// dK / dV
 // ---------------------------------------------------------------------------
 
-struct BwdParamsV {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const uint16_t* dout;
-  const float* lse;
-  const float* delta;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  uint16_t* dq;
-  uint16_t* dk;
-  uint16_t* dv;
-  int num_seqs;
-  int total_q;
-  int Hq;
-  int Hkv;
-  int levels;        // query-block or key-block levels, per kernel
-  float scale;       // softmax_scale
-  float scale_log2;  // softmax_scale * log2(e)
-};
-
-// LSE in base 2 for a query row; rows outside the sequence or without any
-// visible key get +inf so that exp2(s - lse2) is exactly 0 there.
-__device__ __forceinline__ float lse_log2_v(const float* lse, int64_t idx, bool valid) {
-  if (!valid) return INFINITY;
-  const float l = lse[idx];
-  return (l == -INFINITY) ? INFINITY : l * kLog2e;
-}
-
-// ---------------------------------------------------------------------------
-// 2. key-stationary dK / dV
-// ---------------------------------------------------------------------------
-
-template <int D>
-struct DkdvTileV {
+struct Dkdv256 {
   static constexpr int NT = 256;
-  static constexpr int BNK = 128;                  // keys per workgroup (32 per wave)
-  static constexpr int BMQ = (D <= 128) ? 64 : 32; // query rows per step
-  static constexpr int RP = D + 8;                 // row-major pitch (Q, dO)
-  static constexpr int TP = BMQ + 8;               // transposed pitch (Q^T, dO^T)
-  static constexpr int UNITS = (BMQ / 4) * (D / 8);  // Rows4V units per tensor per step
-  static constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread per tensor
-  static constexpr int OFF_DOS = BMQ * RP;
-  static constexpr int OFF_QT = 2 * BMQ * RP;
-  static constexpr int OFF_DOT = 2 * BMQ * RP + D * TP;
-  static constexpr int OFF_F32 = 2 * BMQ * RP + 2 * D * TP;  // in bf16 elements (even)
-  static constexpr size_t LDS_BYTES = (size_t)OFF_F32 * 2 + 2 * BMQ * sizeof(float);
+  static constexpr int BNK = 128;  // keys per workgroup (32 per wave)
+  static constexpr int BMQ = 32;   // query rows per step
+  using QT = RowTile<kD, BMQ>;
+  static constexpr int ROW = QT::ROW;
+  static constexpr int TILE = QT::BYTES;     // 16 KB
+  static constexpr int STAGE = 2 * TILE;     // Q tile, then dO tile
+  using VT = RowTile<kD, BNK>;
+  static constexpr int VBASE = 2 * STAGE;               // the item's V block (64 KB)
+  static constexpr int F32 = VBASE + VT::BYTES;         // lse2 / Delta of both stages
+  static constexpr int F32_STAGE = 512;                 // lse2[64] then Delta[64] (a copy moves 64 rows)
+  static constexpr size_t LDS_BYTES = F32 + 2 * F32_STAGE;
+  static constexpr int VDMA_PER_WAVE = VT::DMAS / 4;
+  static constexpr int DMA_PER_WAVE = 2 * QT::DMAS / 4;  // Q and dO copies
+  static constexpr int PF = 1;                           // operand prefetch distance (k-steps)
+  static constexpr int RV = 2;                           // ring of transposed operands
+  static_assert(2 * STAGE <= 65536, "tile offsets must fit the 16-bit LDS immediate");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D>
-struct QdoStageV {
-  Rows4V q[DkdvTileV<D>::UPT];
-  Rows4V d[DkdvTileV<D>::UPT];
-  float lse2;
-  float dlt;
-};
-
-template <int D>
-__device__ __forceinline__ void qdo_load_v(QdoStageV<D>& st, const BwdParamsV& p, int cq, int Lq, int h, int m0) {
-  using T = DkdvTileV<D>;
-  const int tid = threadIdx.x;
-  const int64_t pitch = (int64_t)p.Hq * D;
-  const uint16_t* qb = p.q + (int64_t)(cq + m0) * pitch + (int64_t)h * D;
-  const uint16_t* db = p.dout + (int64_t)(cq + m0) * pitch + (int64_t)h * D;
-  const int nvalid = Lq - m0;
+__device__ __forceinline__ void issue_qdo256(uint32_t lds0, int stage, const i32x4& rq, const i32x4& rdo,
+                                             const i32x4& rl, const i32x4& rd, uint32_t pitch, int m0, int wave,
+                                             int lane) {
+  using T = Dkdv256;
+  const uint32_t st = lds0 + stage * T::STAGE;
 #pragma unroll
-  for (int i = 0; i < T::UPT; ++i) {
-    const int u = tid + T::NT * i;
-    const int rg = u / (D / 8);
-    const int c8 = (u % (D / 8)) * 8;
-    if (u < T::UNITS) {
-      rows4_load_v(st.q[i], qb, pitch, 4 * rg, nvalid, c8);
-      rows4_load_v(st.d[i], db, pitch, 4 * rg, nvalid, c8);
-    }
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int qd = wave * T::DMA_PER_WAVE + i;
+    const bool is_do = qd >= T::QT::DMAS;
+    tile_dma<kD, T::BMQ>(st + (is_do ? T::TILE : 0), is_do ? rdo : rq, pitch, m0, is_do ? qd - T::QT::DMAS : qd,
+                         lane);
   }
-  if (tid < T::BMQ) {
-    const int i = m0 + tid;
-    const bool valid = i < Lq;
-    const int64_t idx = (int64_t)h * p.total_q + cq + i;
-    st.lse2 = lse_log2_v(p.lse, idx, valid);
-    st.dlt = valid ? p.delta[idx] : 0.f;
+  const uint32_t f = lds0 + T::F32 + stage * T::F32_STAGE;
+  if (wave == 0) rows64_f32_dma(f, rl, m0, lane);
+  if (wave == 1) rows64_f32_dma(f + 256, rd, m0, lane);
+}
+
+// One step: the 32 query rows at sequence row m0 against this wave's 32 keys.
+// B operand of dP = dO V^T for k-step kk: lane l holds head-dims 16 kk +
+// 8 (l / 32) .. + 7 of key row (wave's key l % 32) of the V block in LDS;
+// vrow[] holds the byte addresses of the first 16 chunks of that row (chunk
+// c + 16 lies 256 bytes after chunk c).
+__device__ __forceinline__ uint4 v_operand(const lds_char* lds, const uint32_t* vrow, int kk) {
+  return lds_ld16(lds + vrow[kk % 8] + 256 * (kk / 8));
+}
+
+template <bool MASK>
+__device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char* Qs, const lds_char* dOs,
+                                             const float* lse2_s, const float* dlt_s, const bf16x8* kf,
+                                             const uint32_t* vrow, f32x16 (&dk)[kDB], f32x16 (&dv)[kDB], float c,
+                                             int klim_rel, const OperandOffsets<kD>& off, int half) {
+  using T = Dkdv256;
+  constexpr int PF = T::PF, RV = T::RV;
+  // S (query rows x keys) and dP: two independent chains, LDS operands
+  // (Q and dO rows, V rows) fetched PF k-steps ahead
+  f32x16 s, dp;
+  uint4 fr[PF + 1][3];
+#pragma unroll
+  for (int kk = 0; kk < PF; ++kk) {
+    fr[kk][0] = lds_ld16(Qs + off.row(kk));
+    fr[kk][1] = lds_ld16(dOs + off.row(kk));
+    fr[kk][2] = v_operand(lds, vrow, kk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    if (kk + PF < kKK) {
+      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Qs + off.row(kk + PF));
+      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(dOs + off.row(kk + PF));
+      fr[(kk + PF) % (PF + 1)][2] = v_operand(lds, vrow, kk + PF);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kk == 0) {
+      mfma_vgpr0(s, as_bf16x8(fr[0][0]), kf[0]);
+      mfma_vgpr0(dp, as_bf16x8(fr[0][1]), as_bf16x8(fr[0][2]));
+    } else {
+      mfma_vgpr(s, as_bf16x8(fr[kk % (PF + 1)][0]), kf[kk]);
+      mfma_vgpr(dp, as_bf16x8(fr[kk % (PF + 1)][1]), as_bf16x8(fr[kk % (PF + 1)][2]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  vgpr_fence(s, dp);
+  // dV += P^T dO and dK += dS^T Q, one (k-step ks of 16 queries, head-dim
+  // block db) unit at a time; the transposed dO / Q operands are read RV - 1
+  // units ahead.
+  bf16x8 tdo[RV], tq[RV];
+#pragma unroll
+  for (int u = 0; u < RV - 1; ++u) {
+    tdo[u] = tr_operand<kD>(dOs + 16 * (u / kDB) * T::ROW, off, u % kDB);
+    tq[u] = tr_operand<kD>(Qs + 16 * (u / kDB) * T::ROW, off, u % kDB);
+  }
+  bf16x8 pb, sb;
+#pragma unroll
+  for (int u = 0; u < 2 * kDB; ++u) {
+    const int ks = u / kDB, db = u % kDB;
+    if (u + RV - 1 < 2 * kDB) {
+      const int w = u + RV - 1;
+      tdo[w % RV] = tr_operand<kD>(dOs + 16 * (w / kDB) * T::ROW, off, w % kDB);
+      tq[w % RV] = tr_operand<kD>(Qs + 16 * (w / kDB) * T::ROW, off, w % kDB);
+    }
+    if (db == 0) {
+      // register v <-> query row 16 (v / 8) + 8 half + v % 8 of the step; the
+      // 8 registers of k-step ks are queries 16 ks + 8 half + e
+      const int qo = 16 * ks + 8 * half;
+      const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
+      const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
+      const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
+      const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = 8 * ks + e;
+        float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
+        if (MASK) pe = (qo + e >= klim_rel) ? pe : 0.f;
+        pv[e] = pe;
+        dsv[e] = pe * (dp[v] - dl[e]);
+      }
+      pb = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      sb = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_agpr(dv[db], tdo[u % RV], pb);
+    mfma_agpr(dk[db], tq[u % RV], sb);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void qdo_store_v(const QdoStageV<D>& st, uint16_t* smem) {
-  using T = DkdvTileV<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < T::UPT; ++i) {
-    const int u = tid + T::NT * i;
-    const int rg = u / (D / 8);
-    const int c8 = (u % (D / 8)) * 8;
-    if (u < T::UNITS) {
-      rows4_store_v(st.q[i], smem, T::RP, 4 * rg, c8);
-      rows4_store_v(st.d[i], smem + T::OFF_DOS, T::RP, 4 * rg, c8);
-      rows4_store_t_v(st.q[i], smem + T::OFF_QT, T::TP, 4 * rg, c8);
-      rows4_store_t_v(st.d[i], smem + T::OFF_DOT, T::TP, 4 * rg, c8);
-    }
-  }
-  float* f = reinterpret_cast<float*>(smem + T::OFF_F32);
-  if (tid < T::BMQ) {
-    f[tid] = st.lse2;
-    f[T::BMQ + tid] = st.dlt;
-  }
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel_v(BwdParamsV p) {
-  using T = DkdvTileV<D>;
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
+  using T = Dkdv256;
   extern __shared__ __align__(16) uint16_t smem[];
-  const uint16_t* Qs = smem;
-  const uint16_t* dOs = smem + T::OFF_DOS;
-  const uint16_t* Qt = smem + T::OFF_QT;
-  const uint16_t* dOt = smem + T::OFF_DOT;
-  const float* lse2_s = reinterpret_cast<const float*>(smem + T::OFF_F32);
-  const float* dlt_s = lse2_s + T::BMQ;
+  lds_char* lds = (lds_char*)smem;
 
-  // work item: (sequence, key block) ranked by descending work, x KV heads
-  const int64_t L = xcd_logical(blockIdx.x, 1);
-  const int rank = (int)(L / p.Hkv);
-  const int g = (int)(L % p.Hkv);
+  // work item: (sequence, key block) ranked by descending work, x KV heads x
+  // query-head splits. The rank's level counts key blocks from the end of the
+  // sequence, so the blocks seen by the most query rows come first; the splits
+  // of one key block sit next to each other (same XCD).
+  const int S = p.splits;
+  const int64_t L = xcd_logical(blockIdx.x, S);
+  const int rank = (int)(L / ((int64_t)p.Hkv * S));
+  const int rem = (int)(L % ((int64_t)p.Hkv * S));
+  const int g = rem / S;
+  const int split = rem % S;
   int b, lvl;
   if (!decode_rank(p.cu_k, p.num_seqs, T::BNK, p.levels, rank, b, lvl)) return;
   const int cq = p.cu_q[b];
   const int Lq = p.cu_q[b + 1] - cq;
   const int ck = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - ck;
-  const int nblk = ceil_div(Lk, T::BNK) - 1 - lvl;  // the level counts key blocks from the end
-  const int n0 = nblk * T::BNK;
+  const int n0 = (ceil_div(Lk, T::BNK) - 1 - lvl) * T::BNK;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
   const int kj = n0 + wave * 32 + col;  // this lane's key (sequence-relative)
   const bool kvalid = kj < Lk;
   const int r = p.Hq / p.Hkv;
+  const int hper = r / S;  // query heads of this split: g r + split hper + [0, hper)
 
-  // K^T and V^T operands (B of S = Q K^T and of dP = dO V^T)
-  bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const int64_t off = ((int64_t)(ck + kj) * p.Hkv + g) * D + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = as_bf16x8(kvalid ? ld16(p.k + off + 16 * kk) : zero_u4());
-      vf[kk] = as_bf16x8(kvalid ? ld16(p.v + off + 16 * kk) : zero_u4());
-    }
-  }
-
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dk[db] = zero16();
-    dv[db] = zero16();
-  }
-
-  // query blocks that can see a key of this block
+  // query steps that can see a key of this block
   int mfirst = 0;
   if (CAUSAL) {
     mfirst = n0 - (Lk - Lq);
@@ -253,188 +255,250 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel_v(BwdParamsV p) {
   }
   const int sfirst = mfirst / T::BMQ;
   const int nsteps = ceil_div(Lq, T::BMQ) - sfirst;
-  const int total = (nsteps > 0) ? nsteps * r : 0;
+  const int total = (nsteps > 0) ? nsteps * hper : 0;
+  // steps whose first row is at or past this bound need no causal mask
+  const int mask_end = CAUSAL ? (n0 + T::BNK - 1) - (Lk - Lq) : 0;
 
-  const int qrow = kperm(col);
-  const int drow = dperm(col);
-  const int klim = kj - (Lk - Lq);  // queries i >= klim see this lane's key (causal)
-
-  QdoStageV<D> st;
-  if (total > 0) {
-    qdo_load_v<D>(st, p, cq, Lq, g * r, sfirst * T::BMQ);
-    qdo_store_v<D>(st, smem);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < total; ++it) {
+  const uint32_t pitch = (uint32_t)p.Hq * kD * 2;
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int it, int stage) {
+    const int h = g * r + split * hper + it / nsteps;
     const int m0 = (sfirst + it % nsteps) * T::BMQ;
-    if (it + 1 < total) {
-      const int h1 = g * r + (it + 1) / nsteps;
-      const int m1 = (sfirst + (it + 1) % nsteps) * T::BMQ;
-      qdo_load_v<D>(st, p, cq, Lq, h1, m1);
-    }
-    const bool need_mask = CAUSAL && (n0 + T::BNK - 1 - m0 > Lk - Lq);
+    const int64_t qoff = ((int64_t)cq * p.Hq + h) * kD;
+    const i32x4 rq = head_rows_rsrc<kD>(p.q + qoff, Lq, pitch);
+    const i32x4 rdo = head_rows_rsrc<kD>(p.dout + qoff, Lq, pitch);
+    const int64_t roff = (int64_t)h * p.total_q + cq;
+    const i32x4 rl = make_rsrc(p.lse2 + roff, (uint32_t)Lq * 4u);
+    const i32x4 rd = make_rsrc(p.delta + roff, (uint32_t)Lq * 4u);
+    issue_qdo256(lds0, stage, rq, rdo, rl, rd, pitch, m0, wave, lane);
+  };
+  if (total > 0) {
+    // the item's V block (rows n0 .. n0 + 127; rows past Lk read as 0), once
+    const uint32_t kvpitch = (uint32_t)p.Hkv * kD * 2;
+    const i32x4 rv = head_rows_rsrc<kD>(p.v + ((int64_t)ck * p.Hkv + g) * kD, Lk, kvpitch);
+#pragma unroll
+    for (int i = 0; i < T::VDMA_PER_WAVE; ++i)
+      tile_dma<kD, T::BNK>(lds0 + T::VBASE, rv, kvpitch, n0, wave * T::VDMA_PER_WAVE + i, lane);
+    issue(0, 0);
+  }
 
+  // K^T operand (B of S = Q K^T) in VGPRs
+  bf16x8 kf[kKK];
+  {
+    const int64_t off = ((int64_t)(ck + kj) * p.Hkv + g) * kD + 8 * half;
 #pragma unroll
-    for (int qb = 0; qb < T::BMQ / 32; ++qb) {
-      f32x16 s = zero16(), dp = zero16();
-      const uint16_t* qr = Qs + (qb * 32 + qrow) * T::RP + 8 * half;
-      const uint16_t* dr = dOs + (qb * 32 + qrow) * T::RP + 8 * half;
+    for (int kk = 0; kk < kKK; ++kk) kf[kk] = as_bf16x8(kvalid ? ld16(p.k + off + 16 * kk) : zero_u4());
+  }
+  // addresses of this lane's V row (key wave * 32 + col of the block) in LDS
+  uint32_t vrow[8];
+  {
+    const int vr = wave * 32 + col;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32x32x16(as_bf16x8(ld16(qr + 16 * kk)), kf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(ld16(dr + 16 * kk)), vf[kk], dp);
-      }
-      // register v <-> query qb*32 + 16*(v/8) + 8*half + (v%8)
-      float l2[16], dl[16];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int qo = qb * 32 + 16 * hh + 8 * half;
-        const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
-        const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
-        const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
-        const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
-        l2[8 * hh + 0] = a0.x; l2[8 * hh + 1] = a0.y; l2[8 * hh + 2] = a0.z; l2[8 * hh + 3] = a0.w;
-        l2[8 * hh + 4] = a1.x; l2[8 * hh + 5] = a1.y; l2[8 * hh + 6] = a1.z; l2[8 * hh + 7] = a1.w;
-        dl[8 * hh + 0] = b0.x; dl[8 * hh + 1] = b0.y; dl[8 * hh + 2] = b0.z; dl[8 * hh + 3] = b0.w;
-        dl[8 * hh + 4] = b1.x; dl[8 * hh + 5] = b1.y; dl[8 * hh + 6] = b1.z; dl[8 * hh + 7] = b1.w;
-      }
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pe = fast_exp2(s[v] * p.scale_log2 - l2[v]);
-        if (need_mask) {
-          const int qi = m0 + qb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-          pe = (qi >= klim) ? pe : 0.f;
-        }
-        pv[v] = pe;
-        dsv[v] = pe * (dp[v] - dl[v]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pb = to_bf16x8(pv[8 * ks + 0], pv[8 * ks + 1], pv[8 * ks + 2], pv[8 * ks + 3], pv[8 * ks + 4],
-                                    pv[8 * ks + 5], pv[8 * ks + 6], pv[8 * ks + 7]);
-        const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3],
-                                    dsv[8 * ks + 4], dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
-        const int qo = qb * 32 + 16 * ks + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int d = db * 32 + drow;
-          dv[db] = mfma32x32x16(as_bf16x8(ld16(dOt + d * T::TP + qo)), pb, dv[db]);
-          dk[db] = mfma32x32x16(as_bf16x8(ld16(Qt + d * T::TP + qo)), sb, dk[db]);
-        }
-      }
-    }
+    for (int kk = 0; kk < 8; ++kk) vrow[kk] = T::VBASE + vr * T::ROW + (((2 * kk + half) ^ swz<kD>(vr)) << 4);
+  }
+  OperandOffsets<kD> off;
+  operand_offsets<kD>(off, lane);
 
-    __syncthreads();
+  f32x16 dk[kDB], dv[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+  acc_fence(dk);
+  acc_fence(dv);
+  const float c = p.scale_log2;
+  const int klim = kj - (Lk - Lq);  // query rows i >= klim see this lane's key (causal)
+
+  // waves 0 and 1 have one more copy (lse2 / Delta) per stage in flight
+  auto stage_in = [&](int it) {
     if (it + 1 < total) {
-      qdo_store_v<D>(st, smem);
-      __syncthreads();
+      issue(it + 1, (it + 1) & 1);
+      if (wave < 2)
+        wait_vmcnt<T::DMA_PER_WAVE + 1>();
+      else
+        wait_vmcnt<T::DMA_PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+  };
+  // Per query head of the split: the steps that need the causal mask come
+  // first, then the unmasked ones (two loops, so the accumulators keep their
+  // registers). `it` counts steps over all heads for the copy pipeline.
+  const int nmask = CAUSAL ? min(nsteps, max(0, ceil_div(mask_end, T::BMQ) - sfirst)) : 0;
+  int it = 0;
+  for (int hg = 0; hg < (total > 0 ? hper : 0); ++hg) {
+    for (int st = 0; st < nmask; ++st, ++it) {
+      stage_in(it);
+      const int m0 = (sfirst + st) * T::BMQ;
+      const lds_char* stg = lds + (it & 1) * T::STAGE;
+      const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
+      dkdv256_step<true>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, klim - m0, off, half);
+      lds_barrier();
+    }
+    for (int st = nmask; st < nsteps; ++st, ++it) {
+      stage_in(it);
+      const lds_char* stg = lds + (it & 1) * T::STAGE;
+      const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
+      dkdv256_step<false>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, 0, off, half);
+      lds_barrier();
     }
   }
 
+  acc_fence(dk);
+  acc_fence(dv);
   if (kvalid) {
-    const int64_t off = ((int64_t)(ck + kj) * p.Hkv + g) * D + 16 * half;
+    const int64_t row = ((int64_t)(ck + kj) * p.Hkv + g) * kD + 4 * half;
+    if (S == 1) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      uint4 a, c, e, f;
-      a.x = pack_bf16x2(dk[db][0] * p.scale, dk[db][1] * p.scale);
-      a.y = pack_bf16x2(dk[db][2] * p.scale, dk[db][3] * p.scale);
-      a.z = pack_bf16x2(dk[db][4] * p.scale, dk[db][5] * p.scale);
-      a.w = pack_bf16x2(dk[db][6] * p.scale, dk[db][7] * p.scale);
-      c.x = pack_bf16x2(dk[db][8] * p.scale, dk[db][9] * p.scale);
-      c.y = pack_bf16x2(dk[db][10] * p.scale, dk[db][11] * p.scale);
-      c.z = pack_bf16x2(dk[db][12] * p.scale, dk[db][13] * p.scale);
-      c.w = pack_bf16x2(dk[db][14] * p.scale, dk[db][15] * p.scale);
-      e.x = pack_bf16x2(dv[db][0], dv[db][1]);
-      e.y = pack_bf16x2(dv[db][2], dv[db][3]);
-      e.z = pack_bf16x2(dv[db][4], dv[db][5]);
-      e.w = pack_bf16x2(dv[db][6], dv[db][7]);
-      f.x = pack_bf16x2(dv[db][8], dv[db][9]);
-      f.y = pack_bf16x2(dv[db][10], dv[db][11]);
-      f.z = pack_bf16x2(dv[db][12], dv[db][13]);
-      f.w = pack_bf16x2(dv[db][14], dv[db][15]);
-      st16(p.dk + off + db * 32, a);
-      st16(p.dk + off + db * 32 + 8, c);
-      st16(p.dv + off + db * 32, e);
-      st16(p.dv + off + db * 32 + 8, f);
+      for (int db = 0; db < kDB; ++db) {
+        store_acc_row(p.dk + row + db * 32, dk[db], p.scale);
+        store_acc_row(p.dv + row + db * 32, dv[db], 1.f);
+      }
+    } else {
+      const int64_t part = (int64_t)split * p.total_k * p.Hkv * kD;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        store_acc_row_f32(p.part_dk + part + row + db * 32, dk[db]);
+        store_acc_row_f32(p.part_dv + part + row + db * 32, dv[db]);
+      }
     }
   }
 }
 
+// dK = scale * sum_s part_dk[s], dV = sum_s part_dv[s], in split order; 8
+// consecutive values per thread.
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part_dk,
+                                                              const float* __restrict__ part_dv,
+                                                              uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                                              int64_t n8, int splits, float scale) {
+  const int64_t plane = n8 * 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) {
+      const float4* pk = reinterpret_cast<const float4*>(part_dk + s * plane + 8 * i);
+      const float4* pv = reinterpret_cast<const float4*>(part_dv + s * plane + 8 * i);
+      const float4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+      a[0] += k0.x; a[1] += k0.y; a[2] += k0.z; a[3] += k0.w;
+      a[4] += k1.x; a[5] += k1.y; a[6] += k1.z; a[7] += k1.w;
+      v[0] += v0.x; v[1] += v0.y; v[2] += v0.z; v[3] += v0.w;
+      v[4] += v1.x; v[5] += v1.y; v[6] += v1.z; v[7] += v1.w;
+    }
+    uint4 ok, ov;
+    ok.x = pack_bf16x2(a[0] * scale, a[1] * scale);
+    ok.y = pack_bf16x2(a[2] * scale, a[3] * scale);
+    ok.z = pack_bf16x2(a[4] * scale, a[5] * scale);
+    ok.w = pack_bf16x2(a[6] * scale, a[7] * scale);
+    ov.x = pack_bf16x2(v[0], v[1]);
+    ov.y = pack_bf16x2(v[2], v[3]);
+    ov.z = pack_bf16x2(v[4], v[5]);
+    ov.w = pack_bf16x2(v[6], v[7]);
+    st16(dk + 8 * i, ok);
+    st16(dv + 8 * i, ov);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// 3. query-stationary dQ
+// dQ
 // ---------------------------------------------------------------------------
 
-template <int D>
-struct DqTileV {
+struct Dq256 {
   static constexpr int NT = 256;
-  static constexpr int BM = 128;   // query rows per workgroup (32 per wave)
-  static constexpr int BN = 64;    // keys per tile
-  static constexpr int RP = D + 8;
-  static constexpr int TP = BN + 8;
-  static constexpr int K_UNITS = (BN / 4) * (D / 8);
-  static constexpr int K_UPT = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_CHUNKS = BN * D / 8 / NT;
-  static constexpr int OFF_VS = BN * RP;
-  static constexpr int OFF_KT = 2 * BN * RP;
-  static constexpr size_t LDS_BYTES = (size_t)(2 * BN * RP + D * TP) * 2;
+  static constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+  static constexpr int BN = 32;   // keys per tile
+  using KV = RowTile<kD, BN>;
+  static constexpr int ROW = KV::ROW;
+  static constexpr int TILE = KV::BYTES;  // 16 KB
+  static constexpr int STAGE = 2 * TILE;  // K tile, then V tile
+  static constexpr size_t LDS_BYTES = 2 * STAGE;
+  static constexpr int DMA_PER_WAVE = 2 * KV::DMAS / 4;
+  static constexpr int PF = 2;
+  static constexpr int RV = 3;
+  static_assert(LDS_BYTES <= 65536, "tile offsets must fit the 16-bit LDS immediate");
 };
 
-template <int D>
-struct KvdStageV {
-  Rows4V k[DqTileV<D>::K_UPT];
-  uint4 v[DqTileV<D>::V_CHUNKS];
-};
-
-template <int D>
-__device__ __forceinline__ void kvd_load_v(KvdStageV<D>& st, const uint16_t* kbase, const uint16_t* vbase,
-                                         int64_t pitch, int n0, int Lk) {
-  using T = DqTileV<D>;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void issue_kv_dq256(uint32_t stage, const i32x4& rk, const i32x4& rv, uint32_t pitch,
+                                               int n0, int wave, int lane) {
+  using T = Dq256;
 #pragma unroll
-  for (int i = 0; i < T::K_UPT; ++i) {
-    const int u = tid + T::NT * i;
-    if (u < T::K_UNITS) rows4_load_v(st.k[i], kbase + (int64_t)n0 * pitch, pitch, 4 * (u / (D / 8)), Lk - n0,
-                                   (u % (D / 8)) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < T::V_CHUNKS; ++i) {
-    const int c = tid + T::NT * i;
-    const int key = c / (D / 8);
-    const int kg = n0 + key;
-    st.v[i] = (kg < Lk) ? ld16(vbase + (int64_t)kg * pitch + (c % (D / 8)) * 8) : zero_u4();
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int qd = wave * T::DMA_PER_WAVE + i;
+    const bool is_v = qd >= T::KV::DMAS;
+    tile_dma<kD, T::BN>(stage + (is_v ? T::TILE : 0), is_v ? rv : rk, pitch, n0, is_v ? qd - T::KV::DMAS : qd, lane);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void kvd_store_v(const KvdStageV<D>& st, uint16_t* smem) {
-  using T = DqTileV<D>;
-  const int tid = threadIdx.x;
+// One 32-key tile: S^T = K Q^T and dP^T = V dO^T (two chains), dS, then
+// dQ^T += K^T dS^T one (k-step, head-dim block) unit at a time.
+template <bool MASK, bool CAUSAL>
+__device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf,
+                                           const bf16x8* df, f32x16 (&dq)[kDB], float c, float lse2, float dlt,
+                                           int n0, int Lk, int qlim, const OperandOffsets<kD>& off, int half) {
+  using T = Dq256;
+  constexpr int PF = T::PF, RV = T::RV;
+  f32x16 s, dp;
+  uint4 fr[PF + 1][2];
 #pragma unroll
-  for (int i = 0; i < T::K_UPT; ++i) {
-    const int u = tid + T::NT * i;
-    if (u < T::K_UNITS) {
-      const int rg = u / (D / 8);
-      const int c8 = (u % (D / 8)) * 8;
-      rows4_store_v(st.k[i], smem, T::RP, 4 * rg, c8);
-      rows4_store_t_v(st.k[i], smem + T::OFF_KT, T::TP, 4 * rg, c8);
+  for (int kk = 0; kk < PF; ++kk) {
+    fr[kk][0] = lds_ld16(Ks + off.row(kk));
+    fr[kk][1] = lds_ld16(Vs + off.row(kk));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    if (kk + PF < kKK) {
+      fr[(kk + PF) % (PF + 1)][0] = lds_ld16(Ks + off.row(kk + PF));
+      fr[(kk + PF) % (PF + 1)][1] = lds_ld16(Vs + off.row(kk + PF));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kk == 0) {
+      mfma_vgpr0(s, as_bf16x8(fr[0][0]), qf[0]);
+      mfma_vgpr0(dp, as_bf16x8(fr[0][1]), df[0]);
+    } else {
+      mfma_vgpr(s, as_bf16x8(fr[kk % (PF + 1)][0]), qf[kk]);
+      mfma_vgpr(dp, as_bf16x8(fr[kk % (PF + 1)][1]), df[kk]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  vgpr_fence(s, dp);
+  bf16x8 ka[RV];
 #pragma unroll
-  for (int i = 0; i < T::V_CHUNKS; ++i) {
-    const int c = tid + T::NT * i;
-    st16(smem + T::OFF_VS + (c / (D / 8)) * T::RP + (c % (D / 8)) * 8, st.v[i]);
+  for (int u = 0; u < RV - 1; ++u) ka[u] = tr_operand<kD>(Ks + 16 * (u / kDB) * T::ROW, off, u % kDB);
+  __builtin_amdgcn_sched_barrier(0);
+  float dsv[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float pe = fast_exp2(__builtin_fmaf(s[v], c, -lse2));
+    if (MASK) {
+      const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
+      const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
+      pe = vis ? pe : 0.f;
+    }
+    dsv[v] = pe * (dp[v] - dlt);
+  }
+  bf16x8 sb;
+#pragma unroll
+  for (int u = 0; u < 2 * kDB; ++u) {
+    const int ks = u / kDB, db = u % kDB;
+    if (u + RV - 1 < 2 * kDB) {
+      const int w = u + RV - 1;
+      ka[w % RV] = tr_operand<kD>(Ks + 16 * (w / kDB) * T::ROW, off, w % kDB);
+    }
+    if (db == 0)
+      sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3], dsv[8 * ks + 4],
+                     dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_agpr(dq[db], ka[u % RV], sb);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel_v(BwdParamsV p) {
-  using T = DqTileV<D>;
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
+  using T = Dq256;
   extern __shared__ __align__(16) uint16_t smem[];
-  const uint16_t* Ks = smem;
-  const uint16_t* Vs = smem + T::OFF_VS;
-  const uint16_t* Kt = smem + T::OFF_KT;
+  lds_char* lds = (lds_char*)smem;
 
   const int r = p.Hq / p.Hkv;
   const int64_t L = xcd_logical(blockIdx.x, r);
@@ -449,7 +513,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel_v(BwdParamsV p) {
   const int Lk = p.cu_k[b + 1] - ck;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -461,107 +525,69 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel_v(BwdParamsV p) {
   if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
   const int ntiles = ceil_div(kend, T::BN);
   const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
+  const int nfull = min(ntiles, kfull / T::BN);
 
-  bf16x8 qf[D / 16], df[D / 16];
+  const uint32_t pitch = (uint32_t)p.Hkv * kD * 2;
+  const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * kD;
+  const i32x4 rk = head_rows_rsrc<kD>(p.k + kvoff, Lk, pitch);
+  const i32x4 rv = head_rows_rsrc<kD>(p.v + kvoff, Lk, pitch);
+  const uint32_t lds0 = lds_addr(lds);
+  if (ntiles > 0) issue_kv_dq256(lds0, rk, rv, pitch, 0, wave, lane);
+
+  bf16x8 qf[kKK], df[kKK];
   {
-    const int64_t off = ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * half;
+    const int64_t off = ((int64_t)(cq + qi) * p.Hq + h) * kD + 8 * half;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < kKK; ++kk) {
       qf[kk] = as_bf16x8(qvalid ? ld16(p.q + off + 16 * kk) : zero_u4());
       df[kk] = as_bf16x8(qvalid ? ld16(p.dout + off + 16 * kk) : zero_u4());
     }
   }
   const int64_t lidx = (int64_t)h * p.total_q + cq + qi;
-  const float lse2 = lse_log2_v(p.lse, lidx, qvalid);
+  const float lse2 = qvalid ? p.lse2[lidx] : INFINITY;
   const float dlt = qvalid ? p.delta[lidx] : 0.f;
+  OperandOffsets<kD> off;
+  operand_offsets<kD>(off, lane);
 
-  f32x16 dq[D / 32];
+  f32x16 dq[kDB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dq[db] = zero16();
-
-  const int64_t kvpitch = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + (int64_t)ck * kvpitch + (int64_t)g * D;
-  const uint16_t* vbase = p.v + (int64_t)ck * kvpitch + (int64_t)g * D;
-
-  KvdStageV<D> st;
-  if (ntiles > 0) {
-    kvd_load_v<D>(st, kbase, vbase, kvpitch, 0, Lk);
-    kvd_store_v<D>(st, smem);
-  }
-  __syncthreads();
-
-  const int krow = kperm(col);
-  const int drow = dperm(col);
+  for (int db = 0; db < kDB; ++db) dq[db] = zero16();
+  acc_fence(dq);
+  const float c = p.scale_log2;
   const int qlim = qi + (Lk - Lq);
 
-  for (int n = 0; n < ntiles; ++n) {
-    const int n0 = n * T::BN;
-    if (n + 1 < ntiles) kvd_load_v<D>(st, kbase, vbase, kvpitch, n0 + T::BN, Lk);
-    const bool need_mask = (n0 + T::BN > kfull);
-
-#pragma unroll
-    for (int kb = 0; kb < T::BN / 32; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
-      const uint16_t* kr = Ks + (kb * 32 + krow) * T::RP + 8 * half;
-      const uint16_t* vr = Vs + (kb * 32 + krow) * T::RP + 8 * half;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma32x32x16(as_bf16x8(ld16(kr + 16 * kk)), qf[kk], s);
-        dp = mfma32x32x16(as_bf16x8(ld16(vr + 16 * kk)), df[kk], dp);
-      }
-      float dsv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pe = fast_exp2(s[v] * p.scale_log2 - lse2);
-        if (need_mask) {
-          const int key = n0 + kb * 32 + 16 * (v >> 3) + 8 * half + (v & 7);
-          const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
-          pe = vis ? pe : 0.f;
-        }
-        dsv[v] = pe * (dp[v] - dlt);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3],
-                                    dsv[8 * ks + 4], dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
-        const uint16_t* kt = Kt + drow * T::TP + kb * 32 + 16 * ks + 8 * half;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(as_bf16x8(ld16(kt + db * 32 * T::TP)), sb, dq[db]);
-      }
-    }
-
-    __syncthreads();
+  auto stage_in = [&](int n) {
     if (n + 1 < ntiles) {
-      kvd_store_v<D>(st, smem);
-      __syncthreads();
+      issue_kv_dq256(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
+      wait_vmcnt<T::DMA_PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
     }
+    lds_barrier();
+  };
+  for (int n = 0; n < nfull; ++n) {
+    stage_in(n);
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+    dq256_tile<false, CAUSAL>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, Lk, qlim, off, half);
+    lds_barrier();
+  }
+  for (int n = nfull; n < ntiles; ++n) {
+    stage_in(n);
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+    dq256_tile<true, CAUSAL>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, Lk, qlim, off, half);
+    lds_barrier();
   }
 
+  acc_fence(dq);
   if (qvalid) {
-    uint16_t* row = p.dq + ((int64_t)(cq + qi) * p.Hq + h) * D + 16 * half;
+    uint16_t* row = p.dq + ((int64_t)(cq + qi) * p.Hq + h) * kD + 4 * half;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      uint4 a, c;
-      a.x = pack_bf16x2(dq[db][0] * p.scale, dq[db][1] * p.scale);
-      a.y = pack_bf16x2(dq[db][2] * p.scale, dq[db][3] * p.scale);
-      a.z = pack_bf16x2(dq[db][4] * p.scale, dq[db][5] * p.scale);
-      a.w = pack_bf16x2(dq[db][6] * p.scale, dq[db][7] * p.scale);
-      c.x = pack_bf16x2(dq[db][8] * p.scale, dq[db][9] * p.scale);
-      c.y = pack_bf16x2(dq[db][10] * p.scale, dq[db][11] * p.scale);
-      c.z = pack_bf16x2(dq[db][12] * p.scale, dq[db][13] * p.scale);
-      c.w = pack_bf16x2(dq[db][14] * p.scale, dq[db][15] * p.scale);
-      st16(row + db * 32, a);
-      st16(row + db * 32 + 8, c);
-    }
+    for (int db = 0; db < kDB; ++db) store_acc_row(row + db * 32, dq[db], p.scale);
   }
 }
 
-// ---------------------------------------------------------------------------
-// launchers (Delta has been computed by the caller)
-// ---------------------------------------------------------------------------
-
 template <typename K>
-static hipError_t set_lds_limit_v(K kern, size_t bytes, bool& done) {
+hipError_t set_lds_limit256(K kern, size_t bytes, bool& done) {
   if (done) return hipSuccess;
   hipError_t e =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -569,37 +595,42 @@ static hipError_t set_lds_limit_v(K kern, size_t bytes, bool& done) {
   return e;
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch_bwd_v_t(const BwdArgs& a) {
+template <bool CAUSAL>
+hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
-  BwdParamsV p;
+  BwdParams p;
   p.q = static_cast<const uint16_t*>(f.q);
   p.k = static_cast<const uint16_t*>(f.k);
   p.v = static_cast<const uint16_t*>(f.v);
   p.dout = static_cast<const uint16_t*>(a.dout);
-  p.lse = a.lse;
   p.delta = a.delta;
+  p.lse2 = lse2;
   p.cu_q = f.cu_q;
   p.cu_k = f.cu_k;
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
+  p.part_dk = part_dk;
+  p.part_dv = part_dv;
   p.num_seqs = f.num_seqs;
   p.total_q = (int)f.total_q;
+  p.total_k = (int)f.total_k;
   p.Hq = f.Hq;
   p.Hkv = f.Hkv;
+  p.splits = splits;
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
+
   if (f.total_k > 0) {
-    using T = DkdvTileV<D>;
-    auto kern = bwd_dkdv_kernel_v<D, CAUSAL>;
+    using T = Dkdv256;
+    auto kern = bwd_dkdv256_kernel<CAUSAL>;
     static bool done = false;
-    hipError_t e = set_lds_limit_v(kern, T::LDS_BYTES, done);
+    hipError_t e = set_lds_limit256(kern, T::LDS_BYTES, done);
     if (e != hipSuccess) return e;
-    BwdParamsV pk = p;
+    BwdParams pk = p;
     pk.levels = ceil_div(f.max_k, T::BNK);
-    const int64_t grid = grid_for(f.total_k, f.num_seqs, T::BNK, f.Hkv, 1);
+    const int64_t grid = grid_for(f.total_k, f.num_seqs, T::BNK, f.Hkv * splits, splits);
     if (grid > 0 && pk.levels > 0) {
       prof_begin("attn_bwd_dkdv", stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
@@ -607,14 +638,25 @@ static hipError_t launch_bwd_v_t(const BwdArgs& a) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    if (splits > 1) {
+      const int64_t n8 = f.total_k * f.Hkv * kD / 8;
+      int64_t rgrid = (n8 + 255) / 256;
+      if (rgrid > 8192) rgrid = 8192;
+      prof_begin("attn_bwd_dkdv_reduce", stream);
+      hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)rgrid), dim3(256), 0, stream, part_dk, part_dv,
+                         p.dk, p.dv, n8, splits, f.scale);
+      prof_end(stream);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (f.total_q > 0) {
-    using T = DqTileV<D>;
-    auto kern = bwd_dq_kernel_v<D, CAUSAL>;
+    using T = Dq256;
+    auto kern = bwd_dq256_kernel<CAUSAL>;
     static bool done = false;
-    hipError_t e = set_lds_limit_v(kern, T::LDS_BYTES, done);
+    hipError_t e = set_lds_limit256(kern, T::LDS_BYTES, done);
     if (e != hipSuccess) return e;
-    BwdParamsV pq = p;
+    BwdParams pq = p;
     pq.levels = ceil_div(f.max_q, T::BM);
     const int64_t grid = grid_for(f.total_q, f.num_seqs, T::BM, f.Hq, f.Hq / f.Hkv);
     if (grid > 0 && pq.levels > 0) {
@@ -628,8 +670,11 @@ static hipError_t launch_bwd_v_t(const BwdArgs& a) {
   return hipSuccess;
 }
 
-hipError_t launch_bwd_main_d256(const BwdArgs& a) {
-  return a.f.causal ? launch_bwd_v_t<256, true>(a) : launch_bwd_v_t<256, false>(a);
+}  // namespace
+
+hipError_t launch_bwd_main_d256(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
+  return a.f.causal ? launch_main_t<true>(a, lse2, part_dk, part_dv, splits)
+                    : launch_main_t<false>(a, lse2, part_dk, part_dv, splits);
 }
 
 }  // namespace av

@@ -38,7 +38,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: fp32 [Hq][total_q]
+  float* delta;  // workspace (Delta, lse2, partial dK / dV): see av_bwd.h
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
@@ -54,7 +54,7 @@ int prof_count();
 int prof_get(int i, char* name, int cap, float* ms);
 
 int64_t fwd_grid_size(int64_t total_q, int num_seqs, int Hq, int Hkv);
-size_t bwd_workspace_bytes(int64_t total_q, int Hq);
+size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D);
 
 }  // namespace av
 

@@ -97,9 +97,13 @@ int attn_varlen_fwd(const void* q, const void* k, const void* v,
                     void* out, float* lse, void* stream);
 
 /*
- * Bytes of device workspace attn_varlen_bwd needs for these sizes: the fp32 row
- * term Delta_i = sum_d dout_id * out_id per query row and head ([GUIDE] Backward
- * Kernels: the preprocess kernel), [n_q_heads][total_q], rounded up to 256 bytes.
+ * Bytes of device workspace attn_varlen_bwd needs for these sizes. It holds the
+ * fp32 row term Delta_i = sum_d dout_id * out_id per query row and head ([GUIDE]
+ * Backward Kernels: the preprocess kernel) and the LSE in base 2, each
+ * [n_q_heads][total_q]. At head_dim 256 with few key blocks per KV head, it
+ * also holds fp32 partial dK / dV sums, [s][total_k][n_kv_heads][256] each,
+ * where s divides n_q_heads / n_kv_heads. Each part is rounded up to 256 bytes.
+ * Returns 0 for negative sizes or non-positive head counts.
  */
 size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k,
                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim);

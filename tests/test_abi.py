@@ -123,6 +123,26 @@ def test_bwd_workspace_size():
     assert A.attn_varlen_bwd_workspace_size(1, 0, 0, 4, 2, 64) == 0
 
 
+def _pad(b):
+    return -(-b // 256) * 256
+
+
+@pytest.mark.parametrize("total, hq, hkv, d, splits", [
+    (1000, 32, 8, 128, 1),        # head dims 64 / 128 never split the dK / dV work
+    (32768, 8, 1, 256, 8),        # 256 key blocks x 1 KV head: 8 splits reach 2048 items
+    (131072, 8, 1, 256, 2),       # 1024 key blocks: 2 splits
+    (16384, 16, 2, 256, 8),       # 128 blocks x 2 heads = 256 items: 8 of the 8 heads
+    (300000, 8, 1, 256, 1),       # >= 2048 key blocks: no split
+    (1000, 6, 1, 256, 6),         # too few items for any divisor: all 6 heads
+])
+def test_bwd_workspace_size_splits(total, hq, hkv, d, splits):
+    """Two fp32 row planes [Hq][total_q], plus (head dim 256) two fp32 partial
+    dK / dV blocks of [splits][total_k][Hkv][D] when the split count exceeds 1."""
+    planes = 2 * _pad(total * hq * 4)
+    parts = 2 * _pad(splits * total * hkv * d * 4) if splits > 1 else 0
+    assert A.attn_varlen_bwd_workspace_size(1, total, total, hq, hkv, d) == planes + parts
+
+
 def test_schedule_device_argument_errors():
     l = _lib.lib()
     assert l.attn_varlen_schedule_device(None, 1, 16, 128, FAKE, FAKE, 4, None) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
