@@ -28,8 +28,16 @@ out in float64 NumPy, one packed sequence and one query head at a time:
   the repository guide's Core Abstractions list causal masks). Reading: key ``j``
   of a sequence is visible to query ``i`` when ``j <= i + Lk - Lq`` (aligned at the
   bottom-right; with ``Lq == Lk`` this is the lower triangle with the diagonal).
-* A query row with no visible key (possible only when causal with ``Lq > Lk``, or
-  ``Lk == 0``) has output 0, LSE ``-inf`` and contributes no gradient.
+* Local (sliding-window) attention: the repository guide's Public API lists
+  ``window_size_left/right`` among the key parameters and Core Abstractions list a
+  local / sliding-window mask (``mask.py``); the pages define neither. Reading: with
+  ``window = (left, right)``, key ``j`` is visible to query ``i`` when
+  ``i + Lk - Lq - left <= j <= i + Lk - Lq + right``, a negative bound meaning
+  unbounded on that side; ``causal`` is the window's right bound 0, and the two
+  masks combine by intersection. ``(-1, -1)`` is full attention.
+* A query row with no visible key (possible when causal with ``Lq > Lk``, with a
+  window that leaves it no key, or ``Lk == 0``) has output 0, LSE ``-inf`` and
+  contributes no gradient.
 
 The backward is the analytic gradient of the same definition, given ``dout``:
 ``dP = dO V^T``; ``Delta_i = sum_j P_ij dP_ij``; ``dS = P * (dP - Delta)``;
@@ -70,13 +78,23 @@ def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
     return h // (n_q_heads // n_kv_heads)
 
 
-def visible(Lq: int, Lk: int, causal: bool, rows: Optional[np.ndarray] = None) -> np.ndarray:
+Window = Optional[Tuple[int, int]]
+
+
+def visible(Lq: int, Lk: int, causal: bool, rows: Optional[np.ndarray] = None, window: Window = None) -> np.ndarray:
     """Boolean ``(len(rows), Lk)`` matrix: may query ``i`` of the sequence see key ``j``?"""
     i = np.arange(Lq) if rows is None else np.asarray(rows)
     j = np.arange(Lk)
-    if not causal:
-        return np.ones((i.shape[0], Lk), dtype=bool)
-    return j[None, :] <= (i[:, None] + (Lk - Lq))
+    left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    diag = i[:, None] + (Lk - Lq)  # the key aligned with query i (bottom-right)
+    ok = np.ones((i.shape[0], Lk), dtype=bool)
+    if causal:
+        ok &= j[None, :] <= diag
+    if right >= 0:
+        ok &= j[None, :] <= diag + right
+    if left >= 0:
+        ok &= j[None, :] >= diag - left
+    return ok
 
 
 def _check(q, k, v, cu_q, cu_k):
@@ -115,7 +133,7 @@ def _chunks(n: int, chunk: int) -> Iterable[Tuple[int, int]]:
 
 
 def forward(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int], scale: float, causal: bool,
-            chunk: int = 2048) -> Tuple[np.ndarray, np.ndarray]:
+            chunk: int = 2048, window: Window = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention output ``(total_q, Hq, D)`` and LSE ``(Hq, total_q)``, both float64."""
     q, k, v, cu_q, cu_k = _check(q, k, v, cu_q, cu_k)
     Tq, Hq, D = q.shape
@@ -133,13 +151,13 @@ def forward(q, k, v, cu_q: Sequence[int], cu_k: Sequence[int], scale: float, cau
             vb = v[ck:ck + Lk, g, :]
             for r0, r1 in _chunks(Lq, chunk):
                 s = scale * (q[cq + r0:cq + r1, h, :] @ kb.T)
-                p, l = _row_softmax(s, visible(Lq, Lk, causal, np.arange(r0, r1)))
+                p, l = _row_softmax(s, visible(Lq, Lk, causal, np.arange(r0, r1), window))
                 out[cq + r0:cq + r1, h, :] = p @ vb
                 lse[h, cq + r0:cq + r1] = l
     return out, lse
 
 
-def probabilities(q, k, cu_q, cu_k, scale: float, causal: bool, b: int, h: int) -> np.ndarray:
+def probabilities(q, k, cu_q, cu_k, scale: float, causal: bool, b: int, h: int, window: Window = None) -> np.ndarray:
     """The full ``(Lq, Lk)`` attention matrix P of sequence ``b``, query head ``h`` (small cases)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -148,12 +166,12 @@ def probabilities(q, k, cu_q, cu_k, scale: float, causal: bool, b: int, h: int) 
     ck, Lk = int(cu_k[b]), int(cu_k[b + 1]) - int(cu_k[b])
     g = kv_head_of(h, Hq, Hkv)
     s = scale * (q[cq:cq + Lq, h, :] @ k[ck:ck + Lk, g, :].T)
-    p, _ = _row_softmax(s, visible(Lq, Lk, causal))
+    p, _ = _row_softmax(s, visible(Lq, Lk, causal, None, window))
     return p
 
 
 def backward(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout,
-             chunk: int = 2048) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+             chunk: int = 2048, window: Window = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients ``(dq, dk, dv)`` of ``sum(dout * out)`` with respect to q, k, v (float64)."""
     q, k, v, cu_q, cu_k = _check(q, k, v, cu_q, cu_k)
     dout = np.asarray(dout, dtype=np.float64)
@@ -176,7 +194,7 @@ def backward(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout,
                 qr = q[cq + r0:cq + r1, h, :]
                 dor = dout[cq + r0:cq + r1, h, :]
                 s = scale * (qr @ kb.T)
-                p, _ = _row_softmax(s, visible(Lq, Lk, causal, np.arange(r0, r1)))
+                p, _ = _row_softmax(s, visible(Lq, Lk, causal, np.arange(r0, r1), window))
                 dp = dor @ vb.T
                 delta = (p * dp).sum(axis=1)
                 ds = p * (dp - delta[:, None])
@@ -205,7 +223,8 @@ def _rows_by_sequence(cu_q, rows):
         yield int(b), rows[seq == b]
 
 
-def forward_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, rows) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+def forward_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, rows,
+                 window: Window = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Output and LSE of the given global query rows only.
 
     Returns ``(rows_sorted, out_rows (n, Hq, D), lse_rows (Hq, n))``.
@@ -223,7 +242,7 @@ def forward_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, rows) -> Tuple
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             s = scale * (q[rws, h, :] @ k[ck:ck + Lk, g, :].T)
-            p, lh = _row_softmax(s, visible(Lq, Lk, causal, local))
+            p, lh = _row_softmax(s, visible(Lq, Lk, causal, local, window))
             o[:, h, :] = p @ v[ck:ck + Lk, g, :]
             l[h] = lh
         all_rows.append(rws)
@@ -232,7 +251,8 @@ def forward_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, rows) -> Tuple
     return np.concatenate(all_rows), np.concatenate(outs, axis=0), np.concatenate(lses, axis=1)
 
 
-def backward_dq_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, rows) -> Tuple[np.ndarray, np.ndarray]:
+def backward_dq_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, rows,
+                     window: Window = None) -> Tuple[np.ndarray, np.ndarray]:
     """dQ of the given global query rows only. Returns ``(rows_sorted, dq_rows (n, Hq, D))``."""
     q, k, v, cu_q, cu_k = _check(q, k, v, cu_q, cu_k)
     dout = np.asarray(dout, dtype=np.float64)
@@ -248,7 +268,7 @@ def backward_dq_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, rows
             g = kv_head_of(h, Hq, Hkv)
             kb = k[ck:ck + Lk, g, :]
             s = scale * (q[rws, h, :] @ kb.T)
-            p, _ = _row_softmax(s, visible(Lq, Lk, causal, local))
+            p, _ = _row_softmax(s, visible(Lq, Lk, causal, local, window))
             dp = dout[rws, h, :] @ v[ck:ck + Lk, g, :].T
             delta = (p * dp).sum(axis=1)
             dq[:, h, :] = scale * ((p * (dp - delta[:, None])) @ kb)
@@ -258,7 +278,7 @@ def backward_dq_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, rows
 
 
 def backward_dkdv_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, key_rows,
-                       chunk: int = 1024) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                       chunk: int = 1024, window: Window = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """dK and dV of the given global key rows only.
 
     Every query row that can see one of the keys is visited with its full key row
@@ -277,8 +297,11 @@ def backward_dkdv_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, ke
         kloc = krws - ck
         dk = np.zeros((len(krws), Hkv, D))
         dv = np.zeros((len(krws), Hkv, D))
-        # first query row that can see the earliest requested key
-        i0 = max(0, int(kloc.min()) - (Lk - Lq)) if causal else 0
+        # first query row that can see the earliest requested key (rows before it
+        # see none of them: key j needs i >= j - (Lk - Lq) - right)
+        bounds = ([0] if causal else []) + ([int(window[1])] if window is not None and int(window[1]) >= 0 else [])
+        right = min(bounds) if bounds else -1
+        i0 = max(0, int(kloc.min()) - (Lk - Lq) - right) if right >= 0 else 0
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             kb = k[ck:ck + Lk, g, :]
@@ -288,7 +311,7 @@ def backward_dkdv_rows(q, k, v, cu_q, cu_k, scale: float, causal: bool, dout, ke
                 qr = q[cq + rr, h, :]
                 dor = dout[cq + rr, h, :]
                 s = scale * (qr @ kb.T)
-                p, _ = _row_softmax(s, visible(Lq, Lk, causal, rr))
+                p, _ = _row_softmax(s, visible(Lq, Lk, causal, rr, window))
                 dp = dor @ vb.T
                 delta = (p * dp).sum(axis=1)
                 ds = p * (dp - delta[:, None])

@@ -183,14 +183,15 @@ def check_against_sdpa(mod, causal):
         np.testing.assert_allclose(dv[sl], vb.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
 
 
-def check_finite_differences(mod, causal, seqlens_q=(3, 5), seqlens_k=None):
+def check_finite_differences(mod, causal, seqlens_q=(3, 5), seqlens_k=None, window=None):
     q, k, v, do, cu_q, cu_k = rand_problem(list(seqlens_q), 4, 2, 4, seed=9,
                                            seqlens_k=None if seqlens_k is None else list(seqlens_k))
     scale = 0.6
-    dq, dk, dv = mod.backward(q, k, v, cu_q, cu_k, scale, causal, do)
+    kw = {} if window is None else {"window": window}
+    dq, dk, dv = mod.backward(q, k, v, cu_q, cu_k, scale, causal, do, **kw)
 
     def loss(qq, kk, vv):
-        o, _ = mod.forward(qq, kk, vv, cu_q, cu_k, scale, causal)
+        o, _ = mod.forward(qq, kk, vv, cu_q, cu_k, scale, causal, **kw)
         return float((o * do).sum())
 
     eps = 1e-6
@@ -288,6 +289,101 @@ def check_empty_rows(mod):
     np.testing.assert_allclose(out[3, :], np.broadcast_to(v[0, 0], (2, 4)), atol=1e-14)
     dq, dk, dv = mod.backward(q, k, v, cu_q, cu_k, 1.0, True, do)
     assert np.all(dq[:3] == 0)
+
+
+# Local (sliding-window) attention. The band is built here with torch.tril /
+# torch.triu diagonals, independently of the oracle's own mask code.
+WINDOWS = [(3, 1), (0, 0), (2, -1), (-1, 2), (5, 0), (1, 3)]
+
+
+def band_mask(Lq, Lk, causal, window):
+    """Visible (query, key) pairs: diagonals relative to the bottom-right-aligned one."""
+    off = Lk - Lq
+    left, right = window
+    ones = torch.ones(Lq, Lk, dtype=torch.bool)
+    m = ones.clone()
+    if causal:
+        m &= torch.tril(ones, diagonal=off)
+    if right >= 0:
+        m &= torch.tril(ones, diagonal=off + right)
+    if left >= 0:
+        m &= torch.triu(ones, diagonal=off - left)
+    return m
+
+
+def check_window_against_sdpa(mod, causal, window):
+    # torch float64 SDPA with the band as a boolean mask, per sequence; rows whose
+    # band is empty must give O = 0 and LSE = -inf (SDPA itself gives NaN there).
+    seqlens_q, seqlens_k = [9, 4, 12], [9, 7, 5]
+    Hq, Hkv, scale = 4, 2, 0.45
+    q, k, v, do, cu_q, cu_k = rand_problem(seqlens_q, Hq, Hkv, 8, seed=21, seqlens_k=seqlens_k)
+    out, lse = mod.forward(q, k, v, cu_q, cu_k, scale, causal, window=window)
+    dq, dk, dv = mod.backward(q, k, v, cu_q, cu_k, scale, causal, do, window=window)
+    for b in range(3):
+        sq, sk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        Lq, Lk = seqlens_q[b], seqlens_k[b]
+        m = band_mask(Lq, Lk, causal, window)
+        rows = m.any(dim=1).numpy()
+        qb = torch.tensor(q[sq]).permute(1, 0, 2).contiguous().requires_grad_(True)
+        kb = torch.tensor(k[sk]).permute(1, 0, 2).contiguous().requires_grad_(True)
+        vb = torch.tensor(v[sk]).permute(1, 0, 2).contiguous().requires_grad_(True)
+        kr, vr = kb.repeat_interleave(Hq // Hkv, dim=0), vb.repeat_interleave(Hq // Hkv, dim=0)
+        ob = F.scaled_dot_product_attention(qb[None], kr[None], vr[None], attn_mask=m, scale=scale)[0]
+        ob = torch.where(torch.tensor(rows)[None, :, None], ob, torch.zeros_like(ob))
+        sc = (scale * (qb @ kr.transpose(1, 2))).masked_fill(~m, -math.inf)
+        lref = torch.logsumexp(sc, dim=-1).detach().numpy()
+        o_ref = ob.permute(1, 0, 2).detach().numpy()
+        np.testing.assert_allclose(out[sq][rows], o_ref[rows], rtol=0, atol=1e-12)
+        assert np.all(out[sq][~rows] == 0)
+        np.testing.assert_allclose(lse[:, sq][:, rows], lref[:, rows], rtol=0, atol=1e-12)
+        assert np.all(np.isneginf(lse[:, sq][:, ~rows]))
+        (ob * torch.tensor(do[sq]).permute(1, 0, 2)).sum().backward()
+        np.testing.assert_allclose(dq[sq], qb.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dk[sk], kb.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dv[sk], vb.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+
+
+def check_window_zero_query(mod, causal, window):
+    # Q = 0: O_i is the mean of v over the keys lo .. hi of row i's band, with
+    # lo = i + off - left and hi = i + off + right clipped to the sequence; LSE_i is
+    # log of the band's size; an empty band gives O = 0, LSE = -inf.
+    seqlens_q, seqlens_k = [7, 10], [11, 4]
+    q, k, v, do, cu_q, cu_k = rand_problem(seqlens_q, 2, 1, 4, seed=22, seqlens_k=seqlens_k)
+    q[:] = 0.0
+    out, lse = mod.forward(q, k, v, cu_q, cu_k, 0.8, causal, window=window)
+    left, right = window
+    if causal:
+        right = 0 if right < 0 else min(right, 0)
+    for b in range(2):
+        Lq, Lk = seqlens_q[b], seqlens_k[b]
+        off = Lk - Lq
+        for i in range(Lq):
+            lo = max(0, i + off - left) if left >= 0 else 0
+            hi = min(Lk - 1, i + off + right) if right >= 0 else Lk - 1
+            for h in range(2):
+                if lo > hi:
+                    assert np.all(out[cu_q[b] + i, h] == 0) and np.isneginf(lse[h, cu_q[b] + i])
+                else:
+                    exp_o = v[cu_k[b] + lo:cu_k[b] + hi + 1, 0].mean(axis=0)
+                    np.testing.assert_allclose(out[cu_q[b] + i, h], exp_o, rtol=0, atol=1e-13)
+                    assert abs(lse[h, cu_q[b] + i] - math.log(hi - lo + 1)) < 1e-13
+
+
+def check_window_rows(mod, causal, window):
+    # the row-sampled forms agree with the full oracle under a window
+    seqlens = [13, 6]
+    q, k, v, do, cu, _ = rand_problem(seqlens, 4, 2, 8, seed=23)
+    out, lse = mod.forward(q, k, v, cu, cu, 0.5, causal, window=window)
+    dq, dk, dv = mod.backward(q, k, v, cu, cu, 0.5, causal, do, window=window)
+    rows = [0, 3, 7, 12, 13, 18]
+    r, o, l = mod.forward_rows(q, k, v, cu, cu, 0.5, causal, rows, window=window)
+    np.testing.assert_allclose(o, out[r], atol=1e-13)
+    np.testing.assert_allclose(l, lse[:, r], atol=1e-13)
+    r, g = mod.backward_dq_rows(q, k, v, cu, cu, 0.5, causal, do, rows, window=window)
+    np.testing.assert_allclose(g, dq[r], atol=1e-12)
+    r, gk, gv = mod.backward_dkdv_rows(q, k, v, cu, cu, 0.5, causal, do, [1, 5, 12, 14, 18], window=window)
+    np.testing.assert_allclose(gk, dk[r], atol=1e-12)
+    np.testing.assert_allclose(gv, dv[r], atol=1e-12)
 
 
 # ---------------------------------------------------------------------------
@@ -417,6 +513,55 @@ def _mutant(**overrides):
     return m
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", WINDOWS)
+def test_window_against_torch_sdpa_f64(causal, window):
+    check_window_against_sdpa(O, causal, window)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", WINDOWS)
+def test_window_zero_query_closed_form(causal, window):
+    check_window_zero_query(O, causal, window)
+
+
+@pytest.mark.parametrize("causal, window", [(False, (2, 1)), (True, (1, -1)), (False, (0, 0))])
+def test_window_finite_differences(causal, window):
+    check_finite_differences(O, causal, (5, 4), None, window)
+
+
+@pytest.mark.parametrize("causal, window", [(False, (3, 2)), (True, (4, -1)), (False, (-1, 1))])
+def test_window_row_sampled_forms(causal, window):
+    check_window_rows(O, causal, window)
+
+
+def test_window_unbounded_is_plain_attention():
+    # (-1, -1) is full attention and (-1, 0) is causal: the same masks as the
+    # causal flag, so the results are identical
+    q, k, v, do, cu, _ = rand_problem([9, 5], 4, 2, 8, seed=24)
+    for causal in (False, True):
+        a = O.forward(q, k, v, cu, cu, 0.5, causal)
+        b = O.forward(q, k, v, cu, cu, 0.5, causal, window=(-1, -1))
+        np.testing.assert_array_equal(a[0], b[0])
+    a = O.forward(q, k, v, cu, cu, 0.5, True)
+    b = O.forward(q, k, v, cu, cu, 0.5, False, window=(-1, 0))
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_mutation_window_off_by_one_is_caught():
+    good = O.visible
+
+    def vis(Lq, Lk, causal, rows=None, window=None):
+        m = good(Lq, Lk, causal, rows, window)
+        if window is not None and window[0] >= 0:
+            m = m & good(Lq, Lk, causal, rows, (window[0] - 1 if window[0] > 0 else 0, window[1]))
+        return m
+    bad = _mutant(visible=vis)
+    assert _fails(check_window_zero_query, bad, False, (3, 1))
+    assert _fails(check_window_against_sdpa, bad, False, (3, 1))
+
+
 def _fails(check, *args):
     try:
         check(*args)
@@ -432,7 +577,7 @@ def test_mutation_wrong_gqa_grouping_is_caught():
 
 
 def test_mutation_strict_causal_mask_is_caught():
-    def vis(Lq, Lk, causal, rows=None):
+    def vis(Lq, Lk, causal, rows=None, window=None):
         i = np.arange(Lq) if rows is None else np.asarray(rows)
         j = np.arange(Lk)
         if not causal:
@@ -444,7 +589,7 @@ def test_mutation_strict_causal_mask_is_caught():
 
 
 def test_mutation_top_left_causal_alignment_is_caught():
-    def vis(Lq, Lk, causal, rows=None):
+    def vis(Lq, Lk, causal, rows=None, window=None):
         i = np.arange(Lq) if rows is None else np.asarray(rows)
         j = np.arange(Lk)
         if not causal:
