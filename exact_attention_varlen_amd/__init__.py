@@ -31,6 +31,8 @@ from ._lib import LibraryMissing, lib
 __all__ = [
     "attn_varlen_fwd",
     "attn_varlen_bwd",
+    "attn_varlen_fwd_window",
+    "attn_varlen_bwd_window",
     "attn_varlen_bwd_workspace_size",
     "attn_varlen_error_string",
     "attn_varlen_version",
@@ -99,8 +101,12 @@ def _check_inputs(q, k, v, cu_q, cu_k):
 def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                     softmax_scale: Optional[float] = None, causal: bool = False, return_lse: bool = False,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """Forward pass. Returns ``out`` or ``(out, lse)`` when ``return_lse`` (or ``lse`` is given)."""
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    window_size: Tuple[int, int] = (-1, -1)):
+    """Forward pass. Returns ``out`` or ``(out, lse)`` when ``return_lse`` (or ``lse`` is given).
+
+    ``window_size = (left, right)`` restricts each query to a local band of keys
+    (``attn_varlen_fwd_window``); ``(-1, -1)`` is no window."""
     dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     total_q, Hq, D = q.shape
     total_k, Hkv, _ = k.shape
@@ -117,12 +123,13 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     if lse is not None:
         if lse.dtype != torch.float32 or lse.shape != (Hq, total_q) or not lse.is_contiguous() or lse.device != dev:
             raise ValueError(f"lse must be contiguous float32 ({Hq}, {total_q}) on {dev}")
-    rc = lib().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                               cu_seqlens_q.numel() - 1, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k),
-                               Hq, Hkv, D, float(softmax_scale), int(bool(causal)), _ptr(out), _ptr(lse),
-                               _stream(dev))
+    wl, wr = (int(window_size[0]), int(window_size[1]))
+    rc = lib().attn_varlen_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                      cu_seqlens_q.numel() - 1, total_q, total_k, int(max_seqlen_q),
+                                      int(max_seqlen_k), Hq, Hkv, D, float(softmax_scale), int(bool(causal)), wl, wr,
+                                      _ptr(out), _ptr(lse), _stream(dev))
     if rc != 0:
-        raise AttnVarlenError(rc, "attn_varlen_fwd")
+        raise AttnVarlenError(rc, "attn_varlen_fwd_window")
     return (out, lse) if lse is not None else out
 
 
@@ -135,8 +142,11 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
                     lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                     max_seqlen_k: int, softmax_scale: Optional[float] = None, causal: bool = False,
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                    dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Backward pass: returns ``(dq, dk, dv)`` for the loss ``sum(dout * out)``."""
+                    dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    window_size: Tuple[int, int] = (-1, -1)):
+    """Backward pass: returns ``(dq, dk, dv)`` for the loss ``sum(dout * out)``.
+
+    ``window_size`` must be the forward's (``attn_varlen_bwd_window``)."""
     dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     _check_bf16("dout", dout, dev)
     _check_bf16("out", out, dev)
@@ -159,12 +169,14 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
     ws_bytes = attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    rc = lib().attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q,
-                               total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, float(softmax_scale),
-                               int(bool(causal)), _ptr(dout), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    wl, wr = (int(window_size[0]), int(window_size[1]))
+    rc = lib().attn_varlen_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
+                                      total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
+                                      float(softmax_scale), int(bool(causal)), wl, wr, _ptr(dout), _ptr(out),
+                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(dev))
     if rc != 0:
-        raise AttnVarlenError(rc, "attn_varlen_bwd")
+        raise AttnVarlenError(rc, "attn_varlen_bwd_window")
     return dq, dk, dv
 
 
@@ -198,26 +210,41 @@ def attn_varlen_schedule_device(cu_seqlens_q: torch.Tensor, max_seqlen_q: int, b
 
 class _AttnVarlenFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal):
-        out, lse = attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, return_lse=True)
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, window_size):
+        out, lse = attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, return_lse=True,
+                                   window_size=window_size)
         ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
-        ctx.args = (max_q, max_k, softmax_scale, causal)
+        ctx.args = (max_q, max_k, softmax_scale, causal, window_size)
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
-        max_q, max_k, softmax_scale, causal = ctx.args
+        max_q, max_k, softmax_scale, causal, window_size = ctx.args
         dq, dk, dv = attn_varlen_bwd(dout.contiguous(), q, k, v, out, lse, cu_q, cu_k, max_q, max_k, softmax_scale,
-                                     causal)
-        return dq, dk, dv, None, None, None, None, None, None
+                                     causal, window_size=window_size)
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
 def attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
-                     causal=False):
+                     causal=False, window_size=(-1, -1)):
     """Differentiable varlen attention (forward kernel, then the backward kernels on ``.backward``)."""
     return _AttnVarlenFunction.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
-                                     causal)
+                                     causal, tuple(window_size))
+
+
+def attn_varlen_fwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                           causal=False, window_left=-1, window_right=-1, **kw):
+    """``attn_varlen_fwd`` with a local window (the C entry point of the same name)."""
+    return attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                           window_size=(window_left, window_right), **kw)
+
+
+def attn_varlen_bwd_window(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                           softmax_scale=None, causal=False, window_left=-1, window_right=-1, **kw):
+    """``attn_varlen_bwd`` with a local window (the C entry point of the same name)."""
+    return attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                           softmax_scale, causal, window_size=(window_left, window_right), **kw)
 
 
 def attn_varlen_profile_enable(enable: bool = True) -> None:

@@ -24,6 +24,11 @@ c_size = ctypes.c_size_t
 _SIGNATURES = {
     "attn_varlen_fwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
                                        c_i32, c_f32, c_i32, c_vp, c_vp, c_vp]),
+    "attn_varlen_fwd_window": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                              c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "attn_varlen_bwd_window": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                              c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                              c_vp, c_vp, c_size, c_vp]),
     "attn_varlen_bwd_workspace_size": (c_size, [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32]),
     "attn_varlen_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
                                        c_i32, c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 0;
+constexpr int kVersionMinor = 1;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -46,7 +46,8 @@ int check_common(const void* q, const void* k, const void* v, const int32_t* cu_
 
 av::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
                           int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t max_q, int32_t max_k,
-                          int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t causal, void* stream) {
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t causal, int32_t window_left,
+                          int32_t window_right, void* stream) {
   av::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -63,6 +64,12 @@ av::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const int
   a.D = D;
   a.scale = scale;
   a.causal = causal;
+  // A side wider than any sequence bounds nothing: a left bound >= total_k puts
+  // every row's first key below 0, a right bound >= total_q every row's last key
+  // past Lk - 1. Such sides become unbounded, so they take the kernels of the
+  // plain problem and no per-key arithmetic can overflow.
+  a.window_left = (window_left < 0 || window_left >= total_k) ? -1 : window_left;
+  a.window_right = (window_right < 0 || window_right >= total_q) ? -1 : window_right;
   a.out = nullptr;
   a.lse = nullptr;
   a.stream = stream;
@@ -73,10 +80,11 @@ av::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const int
 
 extern "C" {
 
-int attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
-                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
-                    int32_t head_dim, float softmax_scale, int32_t causal, void* out, float* lse, void* stream) {
+int attn_varlen_fwd_window(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                           int32_t window_right, void* out, float* lse, void* stream) {
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
@@ -84,10 +92,20 @@ int attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* 
   if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return ATTN_VARLEN_ERR_MISALIGNED;
   if (total_q == 0) return ATTN_VARLEN_OK;
   av::FwdArgs a = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
-                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, stream);
+                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left,
+                                window_right, stream);
   a.out = out;
   a.lse = lse;
   return av::launch_fwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+}
+
+int attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, float softmax_scale, int32_t causal, void* out, float* lse, void* stream) {
+  return attn_varlen_fwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
+                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, -1, -1, out,
+                                lse, stream);
 }
 
 size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t n_q_heads,
@@ -97,12 +115,12 @@ size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t
   return av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
 }
 
-int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
-                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
-                    int32_t head_dim, float softmax_scale, int32_t causal, const void* dout, const void* out,
-                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+int attn_varlen_bwd_window(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                           int32_t window_right, const void* dout, const void* out, const float* lse, void* dq,
+                           void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
@@ -116,7 +134,7 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* 
   if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;
   av::BwdArgs a;
   a.f = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
-                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, stream);
+                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, stream);
   a.dout = dout;
   a.out = out;
   a.lse = lse;
@@ -125,6 +143,17 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* 
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
   return av::launch_bwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+}
+
+int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, float softmax_scale, int32_t causal, const void* dout, const void* out,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return attn_varlen_bwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
+                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, -1, -1, dout,
+                                out, lse, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 const char* attn_varlen_error_string(int code) {

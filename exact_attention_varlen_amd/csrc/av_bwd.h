@@ -31,6 +31,7 @@ struct BwdParams {
   int Hkv;
   int splits;        // query-head splits of the dK / dV work (1: write dK / dV directly)
   int levels;        // query-block or key-block levels, per kernel
+  int wl, wr;        // visible band of a row (keys i + Lk - Lq - wl .. + wr; < 0: unbounded)
   float scale;       // softmax_scale
   float scale_log2;  // softmax_scale * log2(e)
 };

@@ -29,7 +29,10 @@
 // with ds_read_b64_tr_b16 from the row-major tiles; all products are
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "av_bwd.h"
 #include "av_common.h"
@@ -149,7 +152,7 @@ constexpr int kSchedValu = 0x002;
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_kstep(const f32x16& s, const f32x16& dp, int ks, const lds_char* qblk,
                                            const lds_char* dblk, const float* lse2_s, const float* dlt_s, f32x16* dk,
-                                           f32x16* dv, float c, int qrow0, int klim, const OperandOffsets<D>& off,
+                                           f32x16* dv, float c, int qrow0, int rlo, int rhi, const OperandOffsets<D>& off,
                                            int half) {
   using T = DkdvCfg<D>;
   const lds_char* qrows = qblk + 16 * ks * T::ROW;
@@ -175,7 +178,7 @@ __device__ __forceinline__ void dkdv_kstep(const f32x16& s, const f32x16& dp, in
   for (int e = 0; e < 8; ++e) {
     const int v = 8 * ks + e;
     float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
-    if (MASK) pe = (qo + e >= klim) ? pe : 0.f;
+    if (MASK) pe = (qo + e >= rlo && qo + e <= rhi) ? pe : 0.f;
     pv[e] = pe;
     dsv[e] = pe * (dp[v] - dl[e]);
   }
@@ -195,7 +198,7 @@ __device__ __forceinline__ void dkdv_kstep(const f32x16& s, const f32x16& dp, in
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
                                           const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
-                                          f32x16* dv, float c, int m0, int klim, const OperandOffsets<D>& off,
+                                          f32x16* dv, float c, int m0, int rlo, int rhi, const OperandOffsets<D>& off,
                                           int half) {
   using T = DkdvCfg<D>;
   constexpr int KK = D / 16;
@@ -231,12 +234,13 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         dkdv_kstep<D, MASK>(acc[2 * b], acc[2 * b + 1], ks, src[2 * b], src[2 * b + 1], lse2_s, dlt_s, dk, dv, c,
-                            64 * qp + 32 * b, klim - m0, off, half);
+                            64 * qp + 32 * b, rlo - m0, rhi - m0, off, half);
     }
   }
 }
 
-template <int D, bool CAUSAL>
+// BAND: the visible keys of a row form a band (causal and / or a local window).
+template <int D, bool BAND>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -265,17 +269,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const bool kvalid = kj < Lk;
   const int r = p.Hq / p.Hkv;
 
-  // query steps that can see a key of this block
-  int mfirst = 0;
-  if (CAUSAL) {
-    mfirst = n0 - (Lk - Lq);
-    mfirst = mfirst < 0 ? 0 : (mfirst > Lq ? Lq : mfirst);
+  // query steps [sfirst, sfirst + nsteps) whose rows see a key of this block,
+  // and among them the unmasked ones [s_full_lo, s_full_hi): every row sees
+  // every key of the block (rows past Lq read as zero and add nothing)
+  int sfirst = 0, nsteps = ceil_div(Lq, T::BMQ), s_full_lo = 0, s_full_hi = nsteps;
+  if (BAND) {
+    const RowRange rr = block_rows(n0, min(n0 + T::BNK, Lk) - 1, Lq, Lk, p.wl, p.wr);
+    sfirst = rr.lo / T::BMQ;
+    const int slast = (rr.hi > rr.lo) ? ceil_div(rr.hi, T::BMQ) : sfirst;
+    nsteps = slast - sfirst;
+    s_full_lo = max(sfirst, ceil_div(rr.full_lo, T::BMQ));
+    s_full_hi = (rr.full_hi >= Lq) ? slast : min(slast, rr.full_hi / T::BMQ);
+    s_full_hi = max(s_full_lo, s_full_hi);
+    s_full_lo -= sfirst;
+    s_full_hi -= sfirst;
   }
-  const int sfirst = mfirst / T::BMQ;
-  const int nsteps = ceil_div(Lq, T::BMQ) - sfirst;
   const int total = (nsteps > 0) ? nsteps * r : 0;
-  // steps whose first row is at or past this bound need no causal mask
-  const int mask_end = CAUSAL ? (n0 + T::BNK - 1) - (Lk - Lq) : 0;
 
   const uint32_t pitch = (uint32_t)p.Hq * D * 2;
   const uint32_t lds0 = lds_addr(lds);
@@ -312,13 +321,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     dv[db] = zero16();
   }
   const float c = p.scale_log2;
-  const int klim = kj - (Lk - Lq);  // query rows i >= klim see this lane's key (causal)
+  // query rows rlo .. rhi see this lane's key
+  const int rlo = (BAND && p.wr >= 0) ? kj - (Lk - Lq) - p.wr : INT_MIN / 2;
+  const int rhi = (BAND && p.wl >= 0) ? kj - (Lk - Lq) + p.wl : INT_MAX / 2;
 
-  // Per query head of the group: the steps that need the causal mask (their
-  // first row is below mask_end) come first, then the unmasked ones; two loops
-  // so the accumulators keep their registers from step to step. `it` counts
-  // steps over all heads for the double-buffer and copy pipeline.
-  const int nmask = CAUSAL ? min(nsteps, max(0, ceil_div(mask_end, T::BMQ) - sfirst)) : 0;
+  // Per query head of the group: masked steps (near the band's right edge),
+  // unmasked steps, masked steps (near its left edge), as separate loops so the
+  // accumulators keep their registers from step to step. `it` counts steps over
+  // all heads for the double-buffer and copy pipeline.
   auto stage_in = [&](int it) {
     if (it + 1 < total) {
       issue(it + 1, lds0 + ((it + 1) & 1) * T::STAGE);
@@ -329,23 +339,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     lds_barrier();
   };
   int it = 0;
+  auto step = [&](int st, auto masked) {
+    stage_in(it);
+    const int m0 = (sfirst + st) * T::BMQ;
+    const lds_char* stg = lds + (it & 1) * T::STAGE;
+    const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
+    dkdv_step<D, decltype(masked)::value>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, rlo, rhi,
+                                          off, half);
+    lds_barrier();
+    ++it;
+  };
   for (int hg = 0; hg < (total > 0 ? r : 0); ++hg) {
-    for (int st = 0; st < nmask; ++st, ++it) {
-      stage_in(it);
-      const int m0 = (sfirst + st) * T::BMQ;
-      const lds_char* stg = lds + (it & 1) * T::STAGE;
-      const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-      dkdv_step<D, true>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, klim, off, half);
-      lds_barrier();
-    }
-    for (int st = nmask; st < nsteps; ++st, ++it) {
-      stage_in(it);
-      const int m0 = (sfirst + st) * T::BMQ;
-      const lds_char* stg = lds + (it & 1) * T::STAGE;
-      const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-      dkdv_step<D, false>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, klim, off, half);
-      lds_barrier();
-    }
+    for (int st = 0; st < s_full_lo; ++st) step(st, std::true_type());
+    for (int st = s_full_lo; st < s_full_hi; ++st) step(st, std::false_type());
+    for (int st = s_full_hi; st < nsteps; ++st) step(st, std::true_type());
   }
 
   if (kvalid) {
@@ -388,9 +395,10 @@ __device__ __forceinline__ void issue_kv_dq(uint32_t stage, const i32x4& rk, con
   }
 }
 
-template <int D, bool MASK, bool CAUSAL>
+// Keys klo .. khi - 1 are visible to this lane's query row.
+template <int D, bool MASK>
 __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, const bf16x8* df,
-                                        f32x16* dq, float c, float lse2, float dlt, int n0, int Lk, int qlim,
+                                        f32x16* dq, float c, float lse2, float dlt, int n0, int klo, int khi,
                                         const OperandOffsets<D>& off, int half) {
   using T = DqCfg<D>;
   constexpr int KK = D / 16;
@@ -425,8 +433,7 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
     float pe = fast_exp2(__builtin_fmaf(s[v], c, -lse2));
     if (MASK) {
       const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
-      const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
-      pe = vis ? pe : 0.f;
+      pe = (key >= klo && key < khi) ? pe : 0.f;
     }
     dsv[v] = pe * (dp[v] - dlt);
   }
@@ -443,7 +450,8 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
   }
 }
 
-template <int D, bool CAUSAL>
+// BAND: the visible keys of a row form a band (causal and / or a local window).
+template <int D, bool BAND>
 __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(BwdParams p) {
   using T = DqCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -470,18 +478,25 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   const int qi = q0 + wave * 32 + col;
   const bool qvalid = qi < Lq;
 
-  int kend = Lk;
-  if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
-  const int ntiles = ceil_div(kend, T::BN);
-  const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
-  const int nfull = min(ntiles, kfull / T::BN);
+  // key tiles [t_lo, t_hi); the unmasked ones [f_lo, f_hi) lie between masked
+  // ones (the band's left edge before, its right edge and the sequence end after)
+  int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
+  if (BAND) {
+    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
+    t_lo = kr.lo / T::BN;
+    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
+    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
+    f_hi = max(f_lo, min(t_hi, kr.full_hi / T::BN));
+  }
+  const int klo = BAND ? band_lo(qi, Lq, Lk, p.wl) : 0;
+  const int khi = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
 
   const uint32_t pitch = (uint32_t)p.Hkv * D * 2;
   const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
   const i32x4 rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
   const i32x4 rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
   const uint32_t lds0 = lds_addr(lds);
-  if (ntiles > 0) issue_kv_dq<D>(lds0, rk, rv, pitch, 0, wave, lane);
+  if (t_hi > t_lo) issue_kv_dq<D>(lds0 + (t_lo & 1) * T::STAGE, rk, rv, pitch, t_lo * T::BN, wave, lane);
 
   bf16x8 qf[D / 16], df[D / 16];
   {
@@ -502,12 +517,11 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = zero16();
   const float c = p.scale_log2;
-  const int qlim = qi + (Lk - Lq);
 
-  // full tiles, then the masked ones: two loops so the accumulators keep their
-  // registers across iterations
+  // masked head, full tiles, masked tail: separate loops so the accumulators
+  // keep their registers across iterations
   auto stage_in = [&](int n) {
-    if (n + 1 < ntiles) {
+    if (n + 1 < t_hi) {
       issue_kv_dq<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
       wait_vmcnt<T::DMA_PER_WAVE>();
     } else {
@@ -515,24 +529,18 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
     }
     lds_barrier();
   };
-  for (int n = 0; n < nfull; ++n) {
+  auto tile = [&](int n, auto masked) {
     stage_in(n);
     const lds_char* cur = lds + (n & 1) * T::STAGE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      dq_half<D, false, CAUSAL>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c, lse2, dlt,
-                                n * T::BN + kb * 32, Lk, qlim, off, half);
+      dq_half<D, decltype(masked)::value>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c,
+                                          lse2, dlt, n * T::BN + kb * 32, klo, khi, off, half);
     lds_barrier();
-  }
-  for (int n = nfull; n < ntiles; ++n) {
-    stage_in(n);
-    const lds_char* cur = lds + (n & 1) * T::STAGE;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      dq_half<D, true, CAUSAL>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c, lse2, dlt,
-                               n * T::BN + kb * 32, Lk, qlim, off, half);
-    lds_barrier();
-  }
+  };
+  for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
+  for (int n = f_lo; n < f_hi; ++n) tile(n, std::false_type());
+  for (int n = f_hi; n < t_hi; ++n) tile(n, std::true_type());
 
   if (qvalid) {
     uint16_t* row = p.dq + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * half;
@@ -570,7 +578,7 @@ static hipError_t launch_prep(const BwdArgs& a, float* delta, float* lse2) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
@@ -594,12 +602,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   p.Hq = f.Hq;
   p.Hkv = f.Hkv;
   p.splits = 1;
+  const Band bd = band_of(f);
+  p.wl = bd.wl;
+  p.wr = bd.wr;
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
 
   if (f.total_k > 0) {
     using T = DkdvCfg<D>;
-    auto kern = bwd_dkdv_kernel<D, CAUSAL>;
+    auto kern = bwd_dkdv_kernel<D, BAND>;
     static bool done = false;
     hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
     if (e != hipSuccess) return e;
@@ -616,7 +627,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   }
   if (f.total_q > 0) {
     using T = DqCfg<D>;
-    auto kern = bwd_dq_kernel<D, CAUSAL>;
+    auto kern = bwd_dq_kernel<D, BAND>;
     static bool done = false;
     hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
     if (e != hipSuccess) return e;
@@ -648,7 +659,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     return launch_bwd_main_d256(a, lse2, splits > 1 ? reinterpret_cast<float*>(part) : nullptr,
                                 splits > 1 ? reinterpret_cast<float*>(part + pb) : nullptr, splits);
   } else {
-    return a.f.causal ? launch_bwd_t<D, true>(a, lse2) : launch_bwd_t<D, false>(a, lse2);
+    return band_of(a.f).band ? launch_bwd_t<D, true>(a, lse2) : launch_bwd_t<D, false>(a, lse2);
   }
 }
 

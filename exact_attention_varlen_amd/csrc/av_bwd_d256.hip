@@ -31,7 +31,10 @@
 //                      double-buffered K / V stages within 64 KB, so every LDS
 //                      operand address is a register plus an immediate.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "av_bwd.h"
 #include "av_common.h"
@@ -134,7 +137,7 @@ template <bool MASK>
 __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char* Qs, const lds_char* dOs,
                                              const float* lse2_s, const float* dlt_s, const bf16x8* kf,
                                              const uint32_t* vrow, f32x16 (&dk)[kDB], f32x16 (&dv)[kDB], float c,
-                                             int klim_rel, const OperandOffsets<kD>& off, int half) {
+                                             int rlo, int rhi, const OperandOffsets<kD>& off, int half) {
   using T = Dkdv256;
   constexpr int PF = T::PF, RV = T::RV;
   // S (query rows x keys) and dP: two independent chains, LDS operands
@@ -199,7 +202,7 @@ __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char
       for (int e = 0; e < 8; ++e) {
         const int v = 8 * ks + e;
         float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
-        if (MASK) pe = (qo + e >= klim_rel) ? pe : 0.f;
+        if (MASK) pe = (qo + e >= rlo && qo + e <= rhi) ? pe : 0.f;
         pv[e] = pe;
         dsv[e] = pe * (dp[v] - dl[e]);
       }
@@ -213,7 +216,8 @@ __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char
   }
 }
 
-template <bool CAUSAL>
+// BAND: the visible keys of a row form a band (causal and / or a local window).
+template <bool BAND>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   using T = Dkdv256;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -247,17 +251,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   const int r = p.Hq / p.Hkv;
   const int hper = r / S;  // query heads of this split: g r + split hper + [0, hper)
 
-  // query steps that can see a key of this block
-  int mfirst = 0;
-  if (CAUSAL) {
-    mfirst = n0 - (Lk - Lq);
-    mfirst = mfirst < 0 ? 0 : (mfirst > Lq ? Lq : mfirst);
+  // query steps [sfirst, sfirst + nsteps) whose rows see a key of this block,
+  // and among them the unmasked ones [s_full_lo, s_full_hi) (relative)
+  int sfirst = 0, nsteps = ceil_div(Lq, T::BMQ), s_full_lo = 0, s_full_hi = nsteps;
+  if (BAND) {
+    const RowRange rr = block_rows(n0, min(n0 + T::BNK, Lk) - 1, Lq, Lk, p.wl, p.wr);
+    sfirst = rr.lo / T::BMQ;
+    const int slast = (rr.hi > rr.lo) ? ceil_div(rr.hi, T::BMQ) : sfirst;
+    nsteps = slast - sfirst;
+    s_full_lo = max(sfirst, ceil_div(rr.full_lo, T::BMQ));
+    s_full_hi = (rr.full_hi >= Lq) ? slast : min(slast, rr.full_hi / T::BMQ);
+    s_full_hi = max(s_full_lo, s_full_hi);
+    s_full_lo -= sfirst;
+    s_full_hi -= sfirst;
   }
-  const int sfirst = mfirst / T::BMQ;
-  const int nsteps = ceil_div(Lq, T::BMQ) - sfirst;
   const int total = (nsteps > 0) ? nsteps * hper : 0;
-  // steps whose first row is at or past this bound need no causal mask
-  const int mask_end = CAUSAL ? (n0 + T::BNK - 1) - (Lk - Lq) : 0;
 
   const uint32_t pitch = (uint32_t)p.Hq * kD * 2;
   const uint32_t lds0 = lds_addr(lds);
@@ -308,7 +316,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   acc_fence(dk);
   acc_fence(dv);
   const float c = p.scale_log2;
-  const int klim = kj - (Lk - Lq);  // query rows i >= klim see this lane's key (causal)
+  // query rows rlo .. rhi see this lane's key
+  const int rlo = (BAND && p.wr >= 0) ? kj - (Lk - Lq) - p.wr : INT_MIN / 2;
+  const int rhi = (BAND && p.wl >= 0) ? kj - (Lk - Lq) + p.wl : INT_MAX / 2;
 
   // waves 0 and 1 have one more copy (lse2 / Delta) per stage in flight
   auto stage_in = [&](int it) {
@@ -323,27 +333,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
     }
     lds_barrier();
   };
-  // Per query head of the split: the steps that need the causal mask come
-  // first, then the unmasked ones (two loops, so the accumulators keep their
-  // registers). `it` counts steps over all heads for the copy pipeline.
-  const int nmask = CAUSAL ? min(nsteps, max(0, ceil_div(mask_end, T::BMQ) - sfirst)) : 0;
+  // Per query head of the split: masked steps, unmasked steps, masked steps
+  // (separate loops, so the accumulators keep their registers). `it` counts
+  // steps over all heads for the copy pipeline.
   int it = 0;
+  auto step = [&](int st, auto masked) {
+    stage_in(it);
+    const int m0 = (sfirst + st) * T::BMQ;
+    const lds_char* stg = lds + (it & 1) * T::STAGE;
+    const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
+    dkdv256_step<decltype(masked)::value>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, rlo - m0,
+                                          rhi - m0, off, half);
+    lds_barrier();
+    ++it;
+  };
   for (int hg = 0; hg < (total > 0 ? hper : 0); ++hg) {
-    for (int st = 0; st < nmask; ++st, ++it) {
-      stage_in(it);
-      const int m0 = (sfirst + st) * T::BMQ;
-      const lds_char* stg = lds + (it & 1) * T::STAGE;
-      const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
-      dkdv256_step<true>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, klim - m0, off, half);
-      lds_barrier();
-    }
-    for (int st = nmask; st < nsteps; ++st, ++it) {
-      stage_in(it);
-      const lds_char* stg = lds + (it & 1) * T::STAGE;
-      const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
-      dkdv256_step<false>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, 0, off, half);
-      lds_barrier();
-    }
+    for (int st = 0; st < s_full_lo; ++st) step(st, std::true_type());
+    for (int st = s_full_lo; st < s_full_hi; ++st) step(st, std::false_type());
+    for (int st = s_full_hi; st < nsteps; ++st) step(st, std::true_type());
   }
 
   acc_fence(dk);
@@ -431,10 +438,11 @@ __device__ __forceinline__ void issue_kv_dq256(uint32_t stage, const i32x4& rk, 
 
 // One 32-key tile: S^T = K Q^T and dP^T = V dO^T (two chains), dS, then
 // dQ^T += K^T dS^T one (k-step, head-dim block) unit at a time.
-template <bool MASK, bool CAUSAL>
+// Keys klo .. khi - 1 are visible to this lane's query row.
+template <bool MASK>
 __device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf,
                                            const bf16x8* df, f32x16 (&dq)[kDB], float c, float lse2, float dlt,
-                                           int n0, int Lk, int qlim, const OperandOffsets<kD>& off, int half) {
+                                           int n0, int klo, int khi, const OperandOffsets<kD>& off, int half) {
   using T = Dq256;
   constexpr int PF = T::PF, RV = T::RV;
   f32x16 s, dp;
@@ -472,8 +480,7 @@ __device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* V
     float pe = fast_exp2(__builtin_fmaf(s[v], c, -lse2));
     if (MASK) {
       const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
-      const bool vis = (key < Lk) && (!CAUSAL || key <= qlim);
-      pe = vis ? pe : 0.f;
+      pe = (key >= klo && key < khi) ? pe : 0.f;
     }
     dsv[v] = pe * (dp[v] - dlt);
   }
@@ -494,7 +501,7 @@ __device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* V
   }
 }
 
-template <bool CAUSAL>
+template <bool BAND>
 __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   using T = Dq256;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -521,18 +528,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   const int qi = q0 + wave * 32 + col;
   const bool qvalid = qi < Lq;
 
-  int kend = Lk;
-  if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
-  const int ntiles = ceil_div(kend, T::BN);
-  const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
-  const int nfull = min(ntiles, kfull / T::BN);
+  // key tiles [t_lo, t_hi), the unmasked ones [f_lo, f_hi)
+  int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
+  if (BAND) {
+    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
+    t_lo = kr.lo / T::BN;
+    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
+    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
+    f_hi = max(f_lo, min(t_hi, kr.full_hi / T::BN));
+  }
+  const int klo = BAND ? band_lo(qi, Lq, Lk, p.wl) : 0;
+  const int khi = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
 
   const uint32_t pitch = (uint32_t)p.Hkv * kD * 2;
   const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * kD;
   const i32x4 rk = head_rows_rsrc<kD>(p.k + kvoff, Lk, pitch);
   const i32x4 rv = head_rows_rsrc<kD>(p.v + kvoff, Lk, pitch);
   const uint32_t lds0 = lds_addr(lds);
-  if (ntiles > 0) issue_kv_dq256(lds0, rk, rv, pitch, 0, wave, lane);
+  if (t_hi > t_lo) issue_kv_dq256(lds0 + (t_lo & 1) * T::STAGE, rk, rv, pitch, t_lo * T::BN, wave, lane);
 
   bf16x8 qf[kKK], df[kKK];
   {
@@ -554,10 +567,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   for (int db = 0; db < kDB; ++db) dq[db] = zero16();
   acc_fence(dq);
   const float c = p.scale_log2;
-  const int qlim = qi + (Lk - Lq);
 
   auto stage_in = [&](int n) {
-    if (n + 1 < ntiles) {
+    if (n + 1 < t_hi) {
       issue_kv_dq256(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
       wait_vmcnt<T::DMA_PER_WAVE>();
     } else {
@@ -565,18 +577,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
     }
     lds_barrier();
   };
-  for (int n = 0; n < nfull; ++n) {
+  auto tile = [&](int n, auto masked) {
     stage_in(n);
     const lds_char* cur = lds + (n & 1) * T::STAGE;
-    dq256_tile<false, CAUSAL>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, Lk, qlim, off, half);
+    dq256_tile<decltype(masked)::value>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, klo, khi, off, half);
     lds_barrier();
-  }
-  for (int n = nfull; n < ntiles; ++n) {
-    stage_in(n);
-    const lds_char* cur = lds + (n & 1) * T::STAGE;
-    dq256_tile<true, CAUSAL>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, Lk, qlim, off, half);
-    lds_barrier();
-  }
+  };
+  for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
+  for (int n = f_lo; n < f_hi; ++n) tile(n, std::false_type());
+  for (int n = f_hi; n < t_hi; ++n) tile(n, std::true_type());
 
   acc_fence(dq);
   if (qvalid) {
@@ -595,7 +604,7 @@ hipError_t set_lds_limit256(K kern, size_t bytes, bool& done) {
   return e;
 }
 
-template <bool CAUSAL>
+template <bool BAND>
 hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
@@ -619,12 +628,15 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   p.Hq = f.Hq;
   p.Hkv = f.Hkv;
   p.splits = splits;
+  const Band bd = band_of(f);
+  p.wl = bd.wl;
+  p.wr = bd.wr;
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
 
   if (f.total_k > 0) {
     using T = Dkdv256;
-    auto kern = bwd_dkdv256_kernel<CAUSAL>;
+    auto kern = bwd_dkdv256_kernel<BAND>;
     static bool done = false;
     hipError_t e = set_lds_limit256(kern, T::LDS_BYTES, done);
     if (e != hipSuccess) return e;
@@ -652,7 +664,7 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   }
   if (f.total_q > 0) {
     using T = Dq256;
-    auto kern = bwd_dq256_kernel<CAUSAL>;
+    auto kern = bwd_dq256_kernel<BAND>;
     static bool done = false;
     hipError_t e = set_lds_limit256(kern, T::LDS_BYTES, done);
     if (e != hipSuccess) return e;
@@ -673,8 +685,8 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
 }  // namespace
 
 hipError_t launch_bwd_main_d256(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
-  return a.f.causal ? launch_main_t<true>(a, lse2, part_dk, part_dv, splits)
-                    : launch_main_t<false>(a, lse2, part_dk, part_dv, splits);
+  return band_of(a.f).band ? launch_main_t<true>(a, lse2, part_dk, part_dv, splits)
+                            : launch_main_t<false>(a, lse2, part_dk, part_dv, splits);
 }
 
 }  // namespace av

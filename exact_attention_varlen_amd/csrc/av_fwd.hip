@@ -105,6 +105,7 @@ struct FwdParams {
   int levels;        // ceil(max_seqlen_q / BM)
   float scale_log2;  // |softmax_scale| * log2(e), at least FLT_MIN
   int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
+  int wl, wr;        // visible band of a row (keys i + Lk - Lq - wl .. + wr; < 0: unbounded)
 };
 
 // O^T accumulation. At head_dim 256 (one wave per SIMD, O = 128 registers per
@@ -146,25 +147,27 @@ __device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, uint32_t bytes) {
 }
 
 // Per-wave state of the forward item that the pipeline steps share.
-template <int D, int BM, int BN>
+template <int D, int BM, int BN, int MODE>
 struct FwdCtx {
   using T = FwdCfg<D, BM, BN>;
+  static constexpr bool LEFT = MODE == 2;  // rows' bands have a first key (a left window bound)
   const lds_char* lds;
   uint32_t lds0;
   i32x4 rk, rv;          // K / V rows of this (sequence, KV head), from key 0
   uint32_t tile_bytes;   // BN rows of the K / V tensor
   uint32_t voff[T::DMA]; // this lane's source offset within a tile, per copy
   int wave, half;
-  int ntiles;
-  int kvis_end;          // first key invisible to this lane's query row
+  int ntiles;            // one past the item's last tile
+  int kvis_lo;           // first key visible to this lane's query row
+  int kvis_end;          // one past the last one
   float c;               // exp2 scale factor
   OperandOffsets<D> off;
   bf16x8 qf[T::KK];
 };
 
 // Copy this wave's share of a 64-row tile (rows row0 ..) into LDS at `dst`.
-template <int D, int BM, int BN>
-__device__ __forceinline__ void issue_tile(const FwdCtx<D, BM, BN>& x, uint32_t dst, const i32x4& rsrc, int row0) {
+template <int D, int BM, int BN, int MODE>
+__device__ __forceinline__ void issue_tile(const FwdCtx<D, BM, BN, MODE>& x, uint32_t dst, const i32x4& rsrc, int row0) {
   using T = FwdCfg<D, BM, BN>;
   const i32x4 r = rsrc_advance(rsrc, (uint32_t)row0 * (x.tile_bytes / T::BN));
 #pragma unroll
@@ -173,11 +176,16 @@ __device__ __forceinline__ void issue_tile(const FwdCtx<D, BM, BN>& x, uint32_t 
 
 // Score register v of accumulator a (a = 0: keys 0..31 of the tile, a = 1:
 // keys 32..63) is key 32 a + 16 (v / 8) + 8 half + v % 8.
-template <int D, int BM, int BN>
-__device__ __forceinline__ void mask_scores(const FwdCtx<D, BM, BN>& x, f32x16& s, int first_key) {
-  const int t = x.kvis_end - first_key - 8 * x.half;  // visible iff 16 (v / 8) + v % 8 < t
+template <int D, int BM, int BN, int MODE>
+__device__ __forceinline__ void mask_scores(const FwdCtx<D, BM, BN, MODE>& x, f32x16& s, int first_key) {
+  // visible iff t0 <= 16 (v / 8) + v % 8 < t1
+  const int t0 = x.kvis_lo - first_key - 8 * x.half;
+  const int t1 = x.kvis_end - first_key - 8 * x.half;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) s[v] = (16 * (v >> 3) + (v & 7) < t) ? s[v] : -INFINITY;
+  for (int v = 0; v < 16; ++v) {
+    const int o = 16 * (v >> 3) + (v & 7);
+    s[v] = ((!x.LEFT || o >= t0) && o < t1) ? s[v] : -INFINITY;
+  }
 }
 
 __device__ __forceinline__ float max16(const f32x16& s, float m) {
@@ -224,8 +232,8 @@ __device__ __forceinline__ void exp_score(const f32x16* sc, int i, float c, floa
 }
 
 // S^T of one key tile (NA accumulators of 32 keys) for this wave's 32 queries.
-template <int D, int BM, int BN>
-__device__ __forceinline__ void qk_tile(const FwdCtx<D, BM, BN>& x, const lds_char* Ks,
+template <int D, int BM, int BN, int MODE>
+__device__ __forceinline__ void qk_tile(const FwdCtx<D, BM, BN, MODE>& x, const lds_char* Ks,
                                         f32x16 (&s)[FwdCfg<D, BM, BN>::NA]) {
   using T = FwdCfg<D, BM, BN>;
   constexpr int NA = T::NA, PF = T::PF;
@@ -257,8 +265,8 @@ __device__ __forceinline__ void qk_tile(const FwdCtx<D, BM, BN>& x, const lds_ch
 //        one, is masked (tiles treated as masked may well be full).
 // On entry sc holds S(n) and mx this lane's max over it; on return sn holds
 // S(n + 1) and mx its max (when tile n + 1 exists).
-template <int D, int BM, int BN, int PAR, bool MC, int NX>
-__device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN>& x, int n, const f32x16 (&sc)[FwdCfg<D, BM, BN>::NA],
+template <int D, int BM, int BN, int MODE, int PAR, bool MC, int NX>
+__device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n, const f32x16 (&sc)[FwdCfg<D, BM, BN>::NA],
                                          f32x16 (&sn)[FwdCfg<D, BM, BN>::NA], f32x16 (&o)[FwdCfg<D, BM, BN>::DB],
                                          float& m_ref, float& l_run, float& l_o, float& mx) {
   using T = FwdCfg<D, BM, BN>;
@@ -400,8 +408,9 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN>& x, int n, cons
       for (int i = 16 * NA * e / (NU - UH); i < 16 * NA * (e + 1) / (NU - UH); ++i) {
         const int v = i & 15;
         if (NX < 0) {
-          const int t = x.kvis_end - (n + 1) * T::BN - 32 * (i >> 4) - 8 * x.half;
-          sn[i >> 4][v] = (16 * (v >> 3) + (v & 7) < t) ? sn[i >> 4][v] : -INFINITY;
+          const int base = (n + 1) * T::BN + 32 * (i >> 4) + 8 * x.half;
+          const int o = 16 * (v >> 3) + (v & 7);
+          sn[i >> 4][v] = ((!x.LEFT || o >= x.kvis_lo - base) && o < x.kvis_end - base) ? sn[i >> 4][v] : -INFINITY;
         }
         mxa = fmaxf(mxa, sn[i >> 4][v]);
       }
@@ -412,7 +421,10 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN>& x, int n, cons
   mx = mxa;  // meaningless when there is no tile n + 1
 }
 
-template <int D, int BM, int BN, bool CAUSAL, bool WRITE_LSE>
+// MODE 0: full attention; 1: the visible keys of a row end at a band edge
+// (causal and / or a right window bound); 2: they also start at one (a left
+// window bound), so an item may begin with masked tiles.
+template <int D, int BM, int BN, int MODE, bool WRITE_LSE>
 __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void fwd_kernel(
     FwdParams p) {
   using T = FwdCfg<D, BM, BN>;
@@ -432,7 +444,7 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   const int ck = p.cu_k[b];
   const int Lk = p.cu_k[b + 1] - ck;
 
-  FwdCtx<D, BM, BN> x;
+  FwdCtx<D, BM, BN, MODE> x;
   x.lds = (const lds_char*)smem;
   x.lds0 = lds_addr((lds_char*)smem);
   const int tid = threadIdx.x;
@@ -443,13 +455,27 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   const int qi = q0 + x.wave * 32 + (lane & 31);  // this lane's query row (sequence-relative)
   const bool qvalid = qi < Lq;
 
-  int kend = Lk;
-  if (CAUSAL) kend = causal_key_end(min(q0 + T::BM, Lq), Lq, Lk);
-  x.ntiles = ceil_div(kend, T::BN);
-  // tiles [0, nfull) need no mask: every key is below Lk and visible to every row
-  const int kfull = CAUSAL ? causal_key_full_end(q0, Lq, Lk) : Lk;
-  const int nfull = min(x.ntiles, kfull / T::BN);
-  x.kvis_end = CAUSAL ? min(Lk, qi + (Lk - Lq) + 1) : Lk;
+  // key tiles of this block, [t_lo, t_hi), and the unmasked ones among them,
+  // [f_lo, f_hi): every key below Lk and inside every row's band
+  constexpr bool BAND = MODE > 0;
+  int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
+  if (BAND) {
+    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
+    t_lo = kr.lo / T::BN;
+    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
+    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
+    f_hi = min(t_hi, kr.full_hi / T::BN);
+  }
+  x.ntiles = t_hi;
+  x.kvis_lo = (MODE == 2) ? band_lo(qi, Lq, Lk, p.wl) : 0;
+  (void)f_lo;
+  x.kvis_end = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
+  // tile order: the unmasked tiles [t_lo, f_hi) (nm of them), then the masked
+  // ones. With a left window bound (MODE 2) the first tiles are masked too; such
+  // items run every tile as a masked step (a separate masked head before the
+  // unmasked tiles needs more registers than 2 waves per SIMD leave).
+  const int ntot = t_hi - t_lo;
+  const int nm = (MODE == 2) ? 0 : f_hi;
   x.c = p.scale_log2;
 
   // K / V buffer resources for this (sequence, KV head): rows past Lk read as 0
@@ -465,11 +491,12 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
     x.voff[i] = (uint32_t)row * pitch + (uint32_t)cidx * 16u;
   }
 
-  // prologue copies: K(0) -> K0, V(0) -> V0, K(1) -> K1; then Q^T into VGPRs
-  if (x.ntiles > 0) {
-    issue_tile(x, x.lds0, x.rk, 0);
-    issue_tile(x, x.lds0 + T::VBASE, x.rv, 0);
-    if (x.ntiles > 1) issue_tile(x, x.lds0 + T::TILE, x.rk, T::BN);
+  // prologue copies: K(t_lo) -> K0, V(t_lo) -> V0, K(t_lo + 1) -> K1; then Q^T
+  // into VGPRs. Buffer parity follows the local tile index n - t_lo.
+  if (ntot > 0) {
+    issue_tile(x, x.lds0, x.rk, t_lo * T::BN);
+    issue_tile(x, x.lds0 + T::VBASE, x.rv, t_lo * T::BN);
+    if (ntot > 1) issue_tile(x, x.lds0 + T::TILE, x.rk, (t_lo + 1) * T::BN);
   }
   {
     // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
@@ -497,40 +524,42 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   float mx = -INFINITY;
   f32x16 sa[NA], sb[NA];
 
-  if (x.ntiles > 0) {
+  if (ntot > 0) {
     wait_vmcnt<0>();
     lds_barrier();
     qk_tile(x, x.lds, sa);
-    if (nfull == 0) {
+    if (nm <= 0) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a) mask_scores(x, sa[a], 32 * a);
+      for (int a = 0; a < NA; ++a) mask_scores(x, sa[a], t_lo * T::BN + 32 * a);
     }
 #pragma unroll
     for (int a = 0; a < NA; ++a) mx = max16(sa[a], mx);
   }
 
-  // Steady state, unrolled by two so the buffer parity is a constant: tile n
-  // and tile n + 1 both unmasked. S(n) lives in sa for even n, sb for odd n.
-  int n = 0;
-  if (nfull > 0) {
-    for (; n + 3 <= nfull; n += 2) {
-      fwd_step<D, BM, BN, 0, false, 1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
-      fwd_step<D, BM, BN, 1, false, 1>(x, n + 1, sb, sa, o, m_ref, l_run, l_o, mx);
+  // S(n) lives in sa for even local index t = n - t_lo, sb for odd t; steps
+  // get the absolute tile index n. (t_lo is 0 unless MODE 2.)
+  int t = 0;
+  if (nm > 0) {
+    // steady state, unrolled by two so the buffer parity is a constant: tiles
+    // t and t + 1 both unmasked
+    for (; t + 3 <= nm; t += 2) {
+      fwd_step<D, BM, BN, MODE, 0, false, 1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
+      fwd_step<D, BM, BN, MODE, 1, false, 1>(x, t_lo + t + 1, sb, sa, o, m_ref, l_run, l_o, mx);
     }
-    // last unmasked step (n is even); the tiles after it are all treated as
+    // last unmasked step (t is even); the tiles after it are all treated as
     // masked, which is exact for full tiles too
-    fwd_step<D, BM, BN, 0, false, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
-    ++n;
-  } else if (x.ntiles > 0) {
-    fwd_step<D, BM, BN, 0, true, -1>(x, 0, sa, sb, o, m_ref, l_run, l_o, mx);
-    n = 1;
+    fwd_step<D, BM, BN, MODE, 0, false, -1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
+    ++t;
+  } else if (ntot > 0) {
+    fwd_step<D, BM, BN, MODE, 0, true, -1>(x, t_lo, sa, sb, o, m_ref, l_run, l_o, mx);
+    t = 1;
   }
-  // masked tail from an odd n, unrolled by two like the steady state
-  while (n < x.ntiles) {
-    fwd_step<D, BM, BN, 1, true, -1>(x, n, sb, sa, o, m_ref, l_run, l_o, mx);
-    if (++n >= x.ntiles) break;
-    fwd_step<D, BM, BN, 0, true, -1>(x, n, sa, sb, o, m_ref, l_run, l_o, mx);
-    ++n;
+  // masked tail from an odd t, unrolled by two like the steady state
+  while (t < ntot) {
+    fwd_step<D, BM, BN, MODE, 1, true, -1>(x, t_lo + t, sb, sa, o, m_ref, l_run, l_o, mx);
+    if (++t >= ntot) break;
+    fwd_step<D, BM, BN, MODE, 0, true, -1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
+    ++t;
   }
 
   // epilogue: O = O / l, LSE = ln(2) * (m + log2 l)
@@ -549,11 +578,11 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   }
 }
 
-template <int D, bool CAUSAL, bool WRITE_LSE>
+template <int D, int MODE, bool WRITE_LSE>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int BM = FwdBlock<D>::BM, BN = FwdBlock<D>::BN;
   using T = FwdCfg<D, BM, BN>;
-  auto kern = fwd_kernel<D, BM, BN, CAUSAL, WRITE_LSE>;
+  auto kern = fwd_kernel<D, BM, BN, MODE, WRITE_LSE>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -578,6 +607,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   // all map to exp2(~0) = 1 as for scale 0, while masked scores (-inf) stay -inf
   p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
   p.neg_scale = a.scale < 0.f ? 1 : 0;
+  const Band bd = band_of(a);
+  p.wl = bd.wl;
+  p.wr = bd.wr;
   const int r = a.Hq / a.Hkv;
   const int64_t grid = grid_for(a.total_q, a.num_seqs, T::BM, a.Hq, r);
   if (grid == 0 || p.levels == 0) return hipSuccess;
@@ -591,8 +623,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
   const bool lse = a.lse != nullptr;
-  if (a.causal) return lse ? launch_fwd_t<D, true, true>(a) : launch_fwd_t<D, true, false>(a);
-  return lse ? launch_fwd_t<D, false, true>(a) : launch_fwd_t<D, false, false>(a);
+  const Band bd = band_of(a);
+  if (bd.wl >= 0) return lse ? launch_fwd_t<D, 2, true>(a) : launch_fwd_t<D, 2, false>(a);
+  if (bd.band) return lse ? launch_fwd_t<D, 1, true>(a) : launch_fwd_t<D, 1, false>(a);
+  return lse ? launch_fwd_t<D, 0, true>(a) : launch_fwd_t<D, 0, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {

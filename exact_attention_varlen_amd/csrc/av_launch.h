@@ -25,10 +25,27 @@ struct FwdArgs {
   int D;
   float scale;
   int causal;
+  int window_left;   // local window bounds (< 0: unbounded), as passed by the caller
+  int window_right;
   void* out;
   float* lse;
   void* stream;
 };
+
+// Visible band of a query row i: keys i + (Lk - Lq) - wl .. i + (Lk - Lq) + wr,
+// a negative bound meaning unbounded; causal attention caps wr at 0. `band` is
+// false for full attention.
+struct Band {
+  int wl, wr;
+  bool band;
+};
+inline Band band_of(const FwdArgs& a) {
+  Band b;
+  b.wl = a.window_left < 0 ? -1 : a.window_left;
+  b.wr = a.causal ? 0 : (a.window_right < 0 ? -1 : a.window_right);
+  b.band = b.wl >= 0 || b.wr >= 0;
+  return b;
+}
 
 struct BwdArgs {
   FwdArgs f;  // q, k, v, packing, heads, scale, causal, stream (f.out / f.lse unused)

@@ -52,19 +52,51 @@ AV_HD inline int64_t grid_for(int64_t total_q, int num_seqs, int bm, int heads, 
   return ((n + group - 1) / group) * group;
 }
 
-// Causal block range of a query block: exclusive end of the visible keys of
-// the block's last row, clamped to [0, Lk]. Key j is visible to query i when
-// j <= i + Lk - Lq.
-AV_HD inline int causal_key_end(int q_end, int Lq, int Lk) {
-  int e = q_end + (Lk - Lq);
-  return e < 0 ? 0 : (e > Lk ? Lk : e);
+// Visible keys of a query row, as a band around the bottom-right-aligned
+// diagonal (FlashAttention repository guide, Public API: causal,
+// window_size_left / window_size_right). Key j is visible to query i when
+//   i + (Lk - Lq) - wl <= j <= i + (Lk - Lq) + wr,
+// a negative bound meaning none on that side; causal attention is wr = 0.
+// band_lo / band_hi are the row's first visible key and one past its last,
+// clamped to [0, Lk] (band_lo >= band_hi: no visible key).
+AV_HD inline int clamp_key(int64_t e, int Lk) { return e < 0 ? 0 : (e > Lk ? Lk : (int)e); }
+AV_HD inline int band_lo(int i, int Lq, int Lk, int wl) {
+  return wl < 0 ? 0 : clamp_key((int64_t)i + (Lk - Lq) - wl, Lk);
+}
+AV_HD inline int band_hi(int i, int Lq, int Lk, int wr) {
+  return wr < 0 ? Lk : clamp_key((int64_t)i + (Lk - Lq) + wr + 1, Lk);
 }
 
-// First key index that may be masked for a query block starting at q0 (the
-// keys below it are visible to every row of the block).
-AV_HD inline int causal_key_full_end(int q0, int Lq, int Lk) {
-  int e = q0 + 1 + (Lk - Lq);
-  return e < 0 ? 0 : (e > Lk ? Lk : e);
+// Key range of a block of query rows [r0, r1] (inclusive, r1 < Lq): the keys
+// some row sees, [lo, hi), and the keys every row sees, [full_lo, full_hi)
+// (empty when full_lo >= full_hi).
+struct KeyRange {
+  int lo, hi, full_lo, full_hi;
+};
+AV_HD inline KeyRange block_keys(int r0, int r1, int Lq, int Lk, int wl, int wr) {
+  KeyRange k;
+  k.lo = band_lo(r0, Lq, Lk, wl);
+  k.hi = band_hi(r1, Lq, Lk, wr);
+  k.full_lo = band_lo(r1, Lq, Lk, wl);
+  k.full_hi = band_hi(r0, Lq, Lk, wr);
+  return k;
+}
+
+// Query rows that see some key of a key block [c0, c1] (inclusive, c1 < Lk),
+// [lo, hi), and the rows that see every key of it, [full_lo, full_hi); rows
+// clamped to [0, Lq]. Row i sees key j iff j - (Lk - Lq) - wr <= i <= j - (Lk - Lq) + wl.
+struct RowRange {
+  int lo, hi, full_lo, full_hi;
+};
+AV_HD inline int clamp_row(int64_t e, int Lq) { return e < 0 ? 0 : (e > Lq ? Lq : (int)e); }
+AV_HD inline RowRange block_rows(int c0, int c1, int Lq, int Lk, int wl, int wr) {
+  RowRange r;
+  const int64_t off = (int64_t)Lk - Lq;
+  r.lo = wr < 0 ? 0 : clamp_row(c0 - off - wr, Lq);
+  r.hi = wl < 0 ? Lq : clamp_row(c1 - off + wl + 1, Lq);
+  r.full_lo = wr < 0 ? 0 : clamp_row(c1 - off - wr, Lq);
+  r.full_hi = wl < 0 ? Lq : clamp_row(c0 - off + wl + 1, Lq);
+  return r;
 }
 
 // Host reference of the ranking: enumerate (b, m) in rank order.

@@ -97,6 +97,30 @@ int attn_varlen_fwd(const void* q, const void* k, const void* v,
                     void* out, float* lse, void* stream);
 
 /*
+ * Forward pass with local (sliding-window) attention ([GUIDE] Public API:
+ * window_size_left / window_size_right; Core Abstractions: the local mask).
+ * Arguments as attn_varlen_fwd, plus:
+ *   window_left, window_right  key j of a sequence is visible to query i when
+ *                       i + (Lk - Lq) - window_left <= j <= i + (Lk - Lq) + window_right;
+ *                       a negative value leaves that side unbounded. causal = 1
+ *                       intersects this with j <= i + (Lk - Lq), i.e. a right bound
+ *                       of 0. (-1, -1) with causal = 0 is full attention; rows
+ *                       that see no key get out = 0 and lse = -inf. A side at
+ *                       least total_k (left) or total_q (right) bounds no row
+ *                       and is taken as unbounded (bit-identical results).
+ *                       No error codes beyond those of attn_varlen_fwd.
+ * attn_varlen_fwd is this call with window_left = window_right = -1.
+ */
+int attn_varlen_fwd_window(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t num_seqs, int64_t total_q, int64_t total_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           float softmax_scale, int32_t causal,
+                           int32_t window_left, int32_t window_right,
+                           void* out, float* lse, void* stream);
+
+/*
  * Bytes of device workspace attn_varlen_bwd needs for these sizes. It holds the
  * fp32 row term Delta_i = sum_d dout_id * out_id per query row and head ([GUIDE]
  * Backward Kernels: the preprocess kernel) and the LSE in base 2, each
@@ -131,6 +155,22 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v,
                     const void* dout, const void* out, const float* lse,
                     void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of attn_varlen_fwd_window (same window arguments; the same
+ * workspace size as attn_varlen_bwd). attn_varlen_bwd is this call with
+ * window_left = window_right = -1.
+ */
+int attn_varlen_bwd_window(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t num_seqs, int64_t total_q, int64_t total_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           float softmax_scale, int32_t causal,
+                           int32_t window_left, int32_t window_right,
+                           const void* dout, const void* out, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of an error code. Never NULL. */
 const char* attn_varlen_error_string(int code);

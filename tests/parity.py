@@ -39,14 +39,20 @@ def to_dev(inp: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
     return {k: v.to(dev) for k, v in inp.items()}
 
 
+def window_of(wl: W.Workload):
+    return (-1, -1) if wl.window is None else tuple(wl.window)
+
+
 def gpu_fwd(wl: W.Workload, d: Dict[str, torch.Tensor], return_lse: bool = True):
     return A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
-                             wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=return_lse)
+                             wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=return_lse,
+                             window_size=window_of(wl))
 
 
 def gpu_bwd(wl: W.Workload, d: Dict[str, torch.Tensor], out, lse):
     return A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
-                             wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
+                             wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
+                             window_size=window_of(wl))
 
 
 def f64(t: torch.Tensor) -> np.ndarray:

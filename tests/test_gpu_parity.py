@@ -17,11 +17,12 @@ def full_parity(wl: W.Workload, backward: bool = True):
     inp = W.make_inputs(wl)
     d = to_dev(inp)
     announce(f"fwd {wl.name} seqlens_q={wl.seqlens_q} seqlens_k={wl.seqlens_k} Hq={wl.n_q_heads} "
-             f"Hkv={wl.n_kv_heads} D={wl.head_dim} causal={wl.causal}")
+             f"Hkv={wl.n_kv_heads} D={wl.head_dim} causal={wl.causal} window={wl.window}")
     out, lse = gpu_fwd(wl, d)
     torch.cuda.synchronize()
     q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
-    ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal)
+    ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal,
+                             window=wl.window)
     check_out(f64(out), ref_o)
     check_lse(f64(lse), ref_l)
     if not backward:
@@ -29,7 +30,8 @@ def full_parity(wl: W.Workload, backward: bool = True):
     announce(f"bwd {wl.name}")
     dq, dk, dv = gpu_bwd(wl, d, out, lse)
     torch.cuda.synchronize()
-    rq, rk, rv = O.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do)
+    rq, rk, rv = O.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do,
+                            window=wl.window)
     check_grad(f64(dq), rq, "dq")
     check_grad(f64(dk), rk, "dk")
     check_grad(f64(dv), rv, "dv")
@@ -64,6 +66,32 @@ def test_parity_small(wl):
     full_parity(wl)
 
 
+# local (sliding-window) attention: band (left, right) around the bottom-right
+# diagonal; causal fixes right = 0. Windows narrower than a tile, wider than a
+# sequence, zero-width, one-sided, and bands that leave rows without a key.
+WINDOWED = []
+for D in (64, 128, 256):
+    for c, win in ((False, (100, 37)), (False, (17, 3)), (False, (0, 0)), (False, (130, -1)),
+                   (False, (-1, 50)), (True, (64, -1)), (True, (0, -1)), (True, (200, -1)), (True, (700, 5))):
+        WINDOWED.append(W.Workload(f"ragged-d{D}-{'c' if c else 'f'}-w{win[0]}_{win[1]}",
+                                   [1, 77, 300, 513, 0, 129], 8, 2, D, c, window=win))
+WINDOWED += [
+    W.Workload("lq-ne-lk-d128-f-w20_10", [100, 300, 5, 0], 4, 1, 128, False, seqlens_k=[250, 64, 0, 33],
+               window=(20, 10)),
+    W.Workload("lq-ne-lk-d128-c-w50", [100, 300, 5, 0], 4, 1, 128, True, seqlens_k=[250, 64, 0, 33],
+               window=(50, -1)),
+    W.Workload("lq-gt-lk-d64-f-w10_5", [300, 70], 2, 2, 64, False, seqlens_k=[64, 200], window=(10, 5)),
+    W.Workload("lq-ne-lk-d256-c-w33", [65, 190], 2, 1, 256, True, seqlens_k=[200, 64], window=(33, -1)),
+    W.Workload("long-band-d128-c-w256", [2100, 1500], 4, 2, 128, True, window=(256, -1)),
+    W.Workload("long-band-d64-f-w300_200", [1800], 4, 4, 64, False, window=(300, 200)),
+]
+
+
+@pytest.mark.parametrize("wl", WINDOWED, ids=[w.name for w in WINDOWED])
+def test_parity_window(wl):
+    full_parity(wl)
+
+
 # --------------------------------------------------------------------------
 # full-size workloads
 # --------------------------------------------------------------------------
@@ -90,19 +118,20 @@ def sampled_parity(wl: W.Workload, dkdv_mode: str):
     torch.cuda.synchronize()
     q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
     rows = sample_rows(cu_q, extra=64)
-    r, ro, rl = O.forward_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, rows)
+    r, ro, rl = O.forward_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, rows, window=wl.window)
     check_out(f64(out[torch.as_tensor(r)]), ro)
     check_lse(f64(lse[:, torch.as_tensor(r)]), rl)
     if not wl.backward:
         return
     do = W.to_f64(inp["dout"])
-    r, rdq = O.backward_dq_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, rows)
+    r, rdq = O.backward_dq_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, rows, window=wl.window)
     check_grad(f64(dq[torch.as_tensor(r)]), rdq, "dq(sampled rows)")
     if dkdv_mode in ("tail", "spread"):
         krows = sample_rows(cu_k, extra=32, tail_only=(dkdv_mode == "tail"))
         if dkdv_mode == "spread":  # keep the oracle cost bounded: keys of the first two sequences only
             krows = krows[krows < cu_k[min(2, len(cu_k) - 1)]]
-        r, rdk, rdv = O.backward_dkdv_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, krows)
+        r, rdk, rdv = O.backward_dkdv_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, krows,
+                                           window=wl.window)
         check_grad(f64(dk[torch.as_tensor(r)]), rdk, "dk(sampled rows)")
         check_grad(f64(dv[torch.as_tensor(r)]), rdv, "dv(sampled rows)")
     check_gradient_sums(wl, d, dk, dv)
@@ -145,6 +174,10 @@ FULL_SIZE = [
     (W.hd256_gqa(1, 131072, False), "none"),
     (W.hd256_gqa(1, 131072, True), "tail"),
     (W.single_16k_full(), "none"),
+    (W.Workload("single-4096-gqa32/8-d128-full-w512_512", [4096], 32, 8, 128, False, window=(512, 512)), "spread"),
+    (W.Workload("packed16k-docs-gqa32/8-d128-causal-w1024", list(W.PACKED_16K_DOC_LENGTHS), 32, 8, 128, True,
+                window=(1024, -1)), "tail"),
+    (W.Workload("8x4096-gqa8/1-d256-causal-w1000", [4096] * 8, 8, 1, 256, True, window=(1000, -1)), "tail"),
 ]
 
 
@@ -276,6 +309,38 @@ def test_device_schedule_matches_host(lengths, bm):
     seq, blk = seq.cpu().tolist(), blk.cpu().tolist()
     assert list(zip(seq[:len(host)], blk[:len(host)])) == host
     assert seq[len(host):] == [-1] * 5 and blk[len(host):] == [-1] * 5
+
+
+@pytest.mark.parametrize("causal,win", [(False, (90, 40)), (True, (200, -1))])
+def test_window_deterministic_and_autograd(causal, win):
+    wl = W.Workload("win-autograd", [700, 33, 1200], 8, 2, 128, causal, window=win)
+    d = to_dev(W.make_inputs(wl))
+    announce(f"window determinism + autograd causal={causal} window={win}")
+    a = _run_all(wl, d)
+    b = _run_all(wl, d)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    q = d["q"].clone().requires_grad_(True)
+    k = d["k"].clone().requires_grad_(True)
+    v = d["v"].clone().requires_grad_(True)
+    out = A.attn_varlen_func(q, k, v, d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+                             wl.softmax_scale, causal, window_size=win)
+    out.backward(d["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), a[0])
+    assert torch.equal(q.grad, a[2]) and torch.equal(k.grad, a[3]) and torch.equal(v.grad, a[4])
+
+
+def test_unbounded_window_equals_plain_call():
+    wl = W.Workload("win-unbounded", [300, 517], 8, 4, 128, True)
+    d = to_dev(W.make_inputs(wl))
+    announce("window (-1,-1) and wide windows vs plain")
+    plain = _run_all(wl, d)
+    for win in ((-1, -1), (100000, -1), (100000, 100000)):
+        wlw = W.Workload("win-unbounded", [300, 517], 8, 4, 128, True, window=win)
+        got = _run_all(wlw, d)
+        for x, y in zip(plain, got):
+            assert torch.equal(x, y), f"window {win}"
 
 
 def test_autograd_wrapper_matches_direct_calls():

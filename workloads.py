@@ -26,7 +26,7 @@ draws on the CPU so that the oracle and the GPU consume identical bits):
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 import torch
@@ -73,6 +73,9 @@ class Workload:
     seed: int = 0
     notes: str = ""
     softmax_scale: Optional[float] = None
+    # local attention band (left, right) around the bottom-right diagonal; None or
+    # a negative side: unbounded on that side
+    window: Optional[Tuple[int, int]] = None
 
     def __post_init__(self):
         if self.seqlens_k is None:
@@ -122,6 +125,7 @@ class Workload:
             "head_dim": self.head_dim,
             "causal": self.causal,
             "total_tokens": self.total_q,
+            **({"window": list(self.window)} if self.window is not None else {}),
         }
 
 
