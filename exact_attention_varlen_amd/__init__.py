@@ -8,7 +8,8 @@ code path.
 
 Entry points (same names as the C functions):
   * ``attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-    softmax_scale=None, causal=False, return_lse=False, out=None, lse=None)``
+    softmax_scale=None, causal=False, return_lse=False, out=None, lse=None,
+    window_size=(-1, -1), num_splits=1)``
   * ``attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k,
     max_seqlen_q, max_seqlen_k, softmax_scale=None, causal=False, ...)``
   * ``attn_varlen_func(...)``: autograd wrapper (forward, then ``.backward(dout)``).
@@ -34,6 +35,9 @@ __all__ = [
     "attn_varlen_fwd_window",
     "attn_varlen_bwd_window",
     "attn_varlen_bwd_workspace_size",
+    "attn_varlen_fwd_splitkv",
+    "attn_varlen_fwd_splitkv_workspace_size",
+    "attn_varlen_fwd_num_splits",
     "attn_varlen_error_string",
     "attn_varlen_version",
     "attn_varlen_schedule_host",
@@ -102,11 +106,14 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                     softmax_scale: Optional[float] = None, causal: bool = False, return_lse: bool = False,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    window_size: Tuple[int, int] = (-1, -1)):
+                    window_size: Tuple[int, int] = (-1, -1), num_splits: int = 1,
+                    workspace: Optional[torch.Tensor] = None):
     """Forward pass. Returns ``out`` or ``(out, lse)`` when ``return_lse`` (or ``lse`` is given).
 
     ``window_size = (left, right)`` restricts each query to a local band of keys
-    (``attn_varlen_fwd_window``); ``(-1, -1)`` is no window."""
+    (``attn_varlen_fwd_window``); ``(-1, -1)`` is no window. ``num_splits > 1``
+    splits every item's keys over that many workgroups and merges the partial
+    results (``attn_varlen_fwd_splitkv``); ``0`` lets the library choose."""
     dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     total_q, Hq, D = q.shape
     total_k, Hkv, _ = k.shape
@@ -124,6 +131,21 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         if lse.dtype != torch.float32 or lse.shape != (Hq, total_q) or not lse.is_contiguous() or lse.device != dev:
             raise ValueError(f"lse must be contiguous float32 ({Hq}, {total_q}) on {dev}")
     wl, wr = (int(window_size[0]), int(window_size[1]))
+    num_seqs = cu_seqlens_q.numel() - 1
+    if num_splits == 0:
+        num_splits = attn_varlen_fwd_num_splits(num_seqs, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, D)
+    if num_splits != 1:
+        ws_bytes = attn_varlen_fwd_splitkv_workspace_size(total_q, Hq, D, num_splits)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        rc = lib().attn_varlen_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                           num_seqs, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv,
+                                           D, float(softmax_scale), int(bool(causal)), wl, wr, int(num_splits),
+                                           _ptr(out), _ptr(lse), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(dev))
+        if rc != 0:
+            raise AttnVarlenError(rc, "attn_varlen_fwd_splitkv")
+        return (out, lse) if lse is not None else out
     rc = lib().attn_varlen_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                       cu_seqlens_q.numel() - 1, total_q, total_k, int(max_seqlen_q),
                                       int(max_seqlen_k), Hq, Hkv, D, float(softmax_scale), int(bool(causal)), wl, wr,
@@ -131,6 +153,27 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     if rc != 0:
         raise AttnVarlenError(rc, "attn_varlen_fwd_window")
     return (out, lse) if lse is not None else out
+
+
+def attn_varlen_fwd_splitkv_workspace_size(total_q: int, n_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(lib().attn_varlen_fwd_splitkv_workspace_size(total_q, n_q_heads, head_dim, num_splits))
+
+
+def attn_varlen_fwd_num_splits(num_seqs: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int, n_q_heads: int,
+                               n_kv_heads: int, head_dim: int) -> int:
+    """The library's split count for these sizes (host-only)."""
+    n = int(lib().attn_varlen_fwd_num_splits(num_seqs, total_q, int(max_seqlen_q), int(max_seqlen_k), n_q_heads,
+                                             n_kv_heads, head_dim))
+    if n < 0:
+        raise AttnVarlenError(n, "attn_varlen_fwd_num_splits")
+    return n
+
+
+def attn_varlen_fwd_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                            causal=False, window_left=-1, window_right=-1, num_splits=0, **kw):
+    """``attn_varlen_fwd`` with split-KV (the C entry point of the same name); ``num_splits=0``: library choice."""
+    return attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                           window_size=(window_left, window_right), num_splits=num_splits, **kw)
 
 
 def attn_varlen_bwd_workspace_size(num_seqs: int, total_q: int, total_k: int, n_q_heads: int, n_kv_heads: int,
@@ -210,9 +253,9 @@ def attn_varlen_schedule_device(cu_seqlens_q: torch.Tensor, max_seqlen_q: int, b
 
 class _AttnVarlenFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, window_size):
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, window_size, num_splits):
         out, lse = attn_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, softmax_scale, causal, return_lse=True,
-                                   window_size=window_size)
+                                   window_size=window_size, num_splits=num_splits)
         ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
         ctx.args = (max_q, max_k, softmax_scale, causal, window_size)
         return out
@@ -223,14 +266,14 @@ class _AttnVarlenFunction(torch.autograd.Function):
         max_q, max_k, softmax_scale, causal, window_size = ctx.args
         dq, dk, dv = attn_varlen_bwd(dout.contiguous(), q, k, v, out, lse, cu_q, cu_k, max_q, max_k, softmax_scale,
                                      causal, window_size=window_size)
-        return dq, dk, dv, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None
 
 
 def attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
-                     causal=False, window_size=(-1, -1)):
+                     causal=False, window_size=(-1, -1), num_splits=1):
     """Differentiable varlen attention (forward kernel, then the backward kernels on ``.backward``)."""
     return _AttnVarlenFunction.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale,
-                                     causal, tuple(window_size))
+                                     causal, tuple(window_size), int(num_splits))
 
 
 def attn_varlen_fwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,

@@ -29,6 +29,11 @@ _SIGNATURES = {
     "attn_varlen_bwd_window": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
                                               c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                               c_vp, c_vp, c_size, c_vp]),
+    "attn_varlen_fwd_splitkv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32,
+                                               c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                               c_vp, c_size, c_vp]),
+    "attn_varlen_fwd_splitkv_workspace_size": (c_size, [c_i64, c_i32, c_i32, c_i32]),
+    "attn_varlen_fwd_num_splits": (c_i32, [c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "attn_varlen_bwd_workspace_size": (c_size, [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32]),
     "attn_varlen_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
                                        c_i32, c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

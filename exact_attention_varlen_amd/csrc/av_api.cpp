@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 1;
+constexpr int kVersionMinor = 2;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -108,6 +108,50 @@ int attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* 
                                 lse, stream);
 }
 
+int attn_varlen_fwd_splitkv(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                            int32_t window_right, int32_t num_splits, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                        n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
+  if (rc != ATTN_VARLEN_OK) return rc;
+  if (!out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (num_splits < 1 || num_splits > ATTN_VARLEN_MAX_SPLITS) return ATTN_VARLEN_ERR_BAD_SPLITS;
+  // the split grid multiplies the forward's (query block x head) units by num_splits
+  if ((total_q / 128 + (int64_t)num_seqs) * n_q_heads * num_splits * 256 >= kMaxGridThreads)
+    return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  const size_t need = av::split_workspace_bytes(total_q, n_q_heads, head_dim, num_splits);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return ATTN_VARLEN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
+  }
+  if (total_q == 0) return ATTN_VARLEN_OK;
+  av::FwdArgs a = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
+                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left,
+                                window_right, stream);
+  a.out = out;
+  a.lse = lse;
+  return av::launch_fwd_split(a, num_splits, workspace) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+}
+
+size_t attn_varlen_fwd_splitkv_workspace_size(int64_t total_q, int32_t n_q_heads, int32_t head_dim,
+                                              int32_t num_splits) {
+  if (total_q < 0 || n_q_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
+  return av::split_workspace_bytes(total_q, n_q_heads, head_dim, num_splits);
+}
+
+int32_t attn_varlen_fwd_num_splits(int32_t num_seqs, int64_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_VARLEN_ERR_BAD_HEAD_DIM;
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return ATTN_VARLEN_ERR_BAD_HEADS;
+  if (num_seqs < 1 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_seqlen_q > total_q)
+    return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  return av::fwd_num_splits(num_seqs, total_q, max_seqlen_q, max_seqlen_k, n_q_heads, n_kv_heads, head_dim);
+}
+
 size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t head_dim) {
   (void)num_seqs;
@@ -168,6 +212,7 @@ const char* attn_varlen_error_string(int code) {
     case ATTN_VARLEN_ERR_WORKSPACE: return "workspace is NULL or too small";
     case ATTN_VARLEN_ERR_BAD_FLAG: return "causal must be 0 or 1";
     case ATTN_VARLEN_ERR_HIP: return "HIP runtime error at kernel launch";
+    case ATTN_VARLEN_ERR_BAD_SPLITS: return "num_splits must be in [1, ATTN_VARLEN_MAX_SPLITS]";
     default: return "unknown error code";
   }
 }

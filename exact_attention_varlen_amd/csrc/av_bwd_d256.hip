@@ -74,14 +74,6 @@ __device__ __forceinline__ void acc_fence(f32x16 (&a)[kDB]) {
                : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]), "+a"(a[6]), "+a"(a[7]));
 }
 
-// fp32 twin of store_acc_row: register v of lane l is head-dim 8 (v / 4) +
-// 4 (l / 32) + v % 4 of the block; the caller adds 4 (l / 32).
-__device__ __forceinline__ void store_acc_row_f32(float* row_db, const f32x16& a) {
-#pragma unroll
-  for (int gq = 0; gq < 4; ++gq)
-    *reinterpret_cast<float4*>(row_db + 8 * gq) = make_float4(a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]);
-}
-
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------

@@ -1,582 +1,12 @@
-// av_fwd.hip — forward kernel: exact attention over packed variable-length
-// sequences with grouped-query heads, bf16 in, fp32 accumulation, optional LSE.
-//
-// What it computes follows the forward loop the FlashAttention repository guide
-// describes under Key Patterns (load a Q tile, loop over K/V blocks, online
-// softmax with running row max and row sum, store O and LSE) and Core
-// Abstractions (online softmax; causal block ranges; varlen offsets). The
-// result is the exact softmax(QK^T * scale + mask) V of each packed sequence.
-//
-// gfx950 design (one workgroup = BM / 32 waves = one query block of BM rows of
-// one query head; each wave owns 32 query rows):
-//  * Q^T stays in VGPRs for the whole item as the B operand of S^T = K Q^T.
-//  * K and V tiles of 64 keys go HBM -> LDS with buffer_load ... lds (no VGPR
-//    staging, out-of-range rows read as zero) into separate double buffers.
-//    Rows are stored row-major with an XOR swizzle of 16-byte chunks (swz<D>).
-//    The tile's first row is folded into the buffer descriptor (scalar ops),
-//    so the per-lane copy offsets never change.
-//  * Software pipeline inside each wave. Iteration n holds the scores of tile
-//    n and runs two phases: (B) the MFMAs of S(n+1) = K(n+1) Q^T interleaved
-//    with the exp / row-sum / bf16 packing of most of P(n); (C) the MFMAs of
-//    O^T += V(n)^T P(n)^T interleaved with the rest of P(n) and the row max of
-//    S(n+1). The vector ALU work of the softmax thus issues while the matrix
-//    cores run, instead of between MFMA bursts. K(n+1) and V(n) are resident
-//    together, and the copies of K(n+2) and V(n+1) are in flight meanwhile.
-//  * V^T comes from the row-major V tile through transposing LDS reads
-//    (ds_read_b64_tr_b16); the key permutation kperm makes the fp32 score
-//    registers the B operand of the PV product after a bf16 conversion.
-//  * Each lane owns one query column: running max, running sum and rescale
-//    factor are per-lane values; the row max needs one exchange with lane ^ 32
-//    per tile (v_permlane32_swap), the row sum is combined once at the end.
-//  * exp2 with the scale folded into one FMA per score. The running max is
-//    only moved (and O rescaled) when a tile's max exceeds it by more than
-//    kRescaleSlack (in log2 units), so P <= 2^kRescaleSlack and most tiles do
-//    no rescaling; the result is the same softmax, only the reference point of
-//    the exponentials changes. Two row sums are kept: the fp32 sum of P gives
-//    the LSE, and the sum of the bf16-rounded P that enter the PV product
-//    normalises O, so the rounding of P cancels in O's weighted average even
-//    when one key carries almost all of a row's weight.
-//  * Masking runs only on key tiles that cross the causal diagonal or the end
-//    of the sequence: their invisible scores are set to -inf once, when the
-//    tile's scores are formed (the scale factor is always > 0, so exp2 maps
-//    them to exactly 0). Tiles past the causal range are never visited. On
-//    masked tiles P is split into bf16 hi + lo parts so rows with very few
-//    visible keys stay accurate.
+// av_fwd.hip — launch of the forward kernel (av_fwd_kernel.h) with one
+// workgroup per (query block, query head) visiting every visible key tile.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
 
-#include "av_common.h"
-#include "av_launch.h"
-#include "av_tiles.h"
+#include "av_fwd_kernel.h"
 
 namespace av {
-
-constexpr float kRescaleSlack = 8.0f;
-
-template <int D, int BM_, int BN_>
-struct FwdCfg {
-  using KV = RowTile<D, BN_>;
-  static constexpr int BM = BM_;                      // query rows per workgroup
-  static constexpr int WAVES = BM / 32;               // one wave per 32 rows
-  static constexpr int BN = BN_;                      // keys per tile (32 or 64)
-  static constexpr int NA = BN / 32;                  // 32-key score accumulators per wave
-  static constexpr int NS = BN / 2;                   // scores per lane per tile
-  static constexpr int NJ = BN / 16;                  // 16-key k-steps of the PV product
-  static constexpr int NT = 64 * WAVES;               // threads per workgroup
-  static constexpr int ROW = KV::ROW;                 // bytes per key row in LDS
-  static constexpr int TILE = KV::BYTES;              // bytes of one K or V tile
-  static constexpr int VBASE = 2 * TILE;              // K0 K1 | V0 V1
-  static constexpr size_t LDS_BYTES = 4 * TILE;
-  static constexpr int DMA = KV::DMAS / WAVES;        // copies per wave per tile
-  static constexpr int KK = D / 16;                   // k-steps of S = K Q^T
-  static constexpr int DB = D / 32;                   // 32-wide head-dim blocks of O
-  static constexpr int PF = 2;                        // K operand prefetch distance
-  // head_dim 256 needs more than 256 registers per lane (O alone is 128): one
-  // wave per SIMD, with the accumulators free to use AGPRs
-  static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
-  static constexpr int MIN_BLOCKS_PER_CU = WAVES_PER_SIMD * 4 / WAVES;
-  static_assert(KV::DMAS % WAVES == 0, "tile copies must split evenly over the waves");
-  static_assert(LDS_BYTES * MIN_BLOCKS_PER_CU <= 160 * 1024, "LDS budget");
-};
-
-// The forward kernel's tile sizes for a head_dim (the grid depends on BM).
-// head_dim 256 uses 32-key tiles: the four K / V buffers then take 64 KB, so
-// every LDS operand address is a register plus a 16-bit immediate, and the
-// score state of the pipeline halves.
-template <int D>
-struct FwdBlock {
-  static constexpr int BM = 128;
-  static constexpr int BN = (D <= 128) ? 64 : 32;
-};
-
-struct FwdParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  uint16_t* out;
-  float* lse;
-  int num_seqs;
-  int total_q;
-  int Hq;
-  int Hkv;
-  int levels;        // ceil(max_seqlen_q / BM)
-  float scale_log2;  // |softmax_scale| * log2(e), at least FLT_MIN
-  int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
-  int wl, wr;        // visible band of a row (keys i + Lk - Lq - wl .. + wr; < 0: unbounded)
-};
-
-// O^T accumulation. At head_dim 256 (one wave per SIMD, O = 128 registers per
-// lane) the accumulators are pinned to AGPRs through an inline-asm MFMA: left
-// to itself the register allocator gives the loop-carried O different register
-// files in the two unrolled steps and copies all of it every step. The asm is
-// opaque to the compiler's hazard checks, so it carries its own: s_nop 1 before
-// the MFMA covers a VALU-written P operand, and o_fence() separates MFMA writes
-// of O from VALU accesses (rescale, epilogue) in both directions.
-template <int D>
-__device__ __forceinline__ void pv_mfma(f32x16& o, const bf16x8& v, const bf16x8& p) {
-  if constexpr (D == 256) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
-  } else {
-    o = mfma32x32x16(v, p, o);
-  }
-}
-
-template <int D, int DB>
-__device__ __forceinline__ void o_fence(f32x16 (&o)[DB]) {
-  if constexpr (D == 256) {
-    static_assert(DB == 8, "fence written for 8 accumulators");
-    // 24 wait states: more than an MFMA result needs before a VALU read, and
-    // than a VALU write needs before an MFMA reads it as the accumulator
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
-  }
-}
-
-// Descriptor of the same rows starting `bytes` further on.
-__device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, uint32_t bytes) {
-  const uint64_t base = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + bytes;
-  i32x4 o;
-  o[0] = (int)(uint32_t)base;
-  o[1] = (int)((uint32_t)(base >> 32) & 0xffffu);
-  o[2] = (int)((uint32_t)r[2] - bytes);
-  o[3] = r[3];
-  return o;
-}
-
-// Per-wave state of the forward item that the pipeline steps share.
-template <int D, int BM, int BN, int MODE>
-struct FwdCtx {
-  using T = FwdCfg<D, BM, BN>;
-  static constexpr bool LEFT = MODE == 2;  // rows' bands have a first key (a left window bound)
-  const lds_char* lds;
-  uint32_t lds0;
-  i32x4 rk, rv;          // K / V rows of this (sequence, KV head), from key 0
-  uint32_t tile_bytes;   // BN rows of the K / V tensor
-  uint32_t voff[T::DMA]; // this lane's source offset within a tile, per copy
-  int wave, half;
-  int ntiles;            // one past the item's last tile
-  int kvis_lo;           // first key visible to this lane's query row
-  int kvis_end;          // one past the last one
-  float c;               // exp2 scale factor
-  OperandOffsets<D> off;
-  bf16x8 qf[T::KK];
-};
-
-// Copy this wave's share of a 64-row tile (rows row0 ..) into LDS at `dst`.
-template <int D, int BM, int BN, int MODE>
-__device__ __forceinline__ void issue_tile(const FwdCtx<D, BM, BN, MODE>& x, uint32_t dst, const i32x4& rsrc, int row0) {
-  using T = FwdCfg<D, BM, BN>;
-  const i32x4 r = rsrc_advance(rsrc, (uint32_t)row0 * (x.tile_bytes / T::BN));
-#pragma unroll
-  for (int i = 0; i < T::DMA; ++i) lds_dma16(r, dst + (x.wave * T::DMA + i) * 1024, x.voff[i]);
-}
-
-// Score register v of accumulator a (a = 0: keys 0..31 of the tile, a = 1:
-// keys 32..63) is key 32 a + 16 (v / 8) + 8 half + v % 8.
-template <int D, int BM, int BN, int MODE>
-__device__ __forceinline__ void mask_scores(const FwdCtx<D, BM, BN, MODE>& x, f32x16& s, int first_key) {
-  // visible iff t0 <= 16 (v / 8) + v % 8 < t1
-  const int t0 = x.kvis_lo - first_key - 8 * x.half;
-  const int t1 = x.kvis_end - first_key - 8 * x.half;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int o = 16 * (v >> 3) + (v & 7);
-    s[v] = ((!x.LEFT || o >= t0) && o < t1) ? s[v] : -INFINITY;
-  }
-}
-
-__device__ __forceinline__ float max16(const f32x16& s, float m) {
-#pragma unroll
-  for (int v = 0; v < 16; ++v) m = fmaxf(m, s[v]);
-  return m;
-}
-
-// P for score i (0 .. 31) of the tile: register i % 16 of accumulator i / 16,
-// i.e. PV k-step i / 8, slot i % 8. Scores are exponentiated one at a time so
-// the work can be spread evenly between MFMAs, in two stages: exp_issue forms
-// p = exp2(s c - m); exp_finish adds it to the row sums and, with the second
-// score of a pair, packs the pair to bf16 (and, on masked tiles, splits it
-// into hi / lo parts). Issuing the exponentials one MFMA ahead of their use
-// hides the latency of the transcendental unit.
-__device__ __forceinline__ void exp_issue(const f32x16* sc, int i, float c, float nm, float* pe) {
-  pe[i] = fast_exp2(__builtin_fmaf(sc[i >> 4][i & 15], c, nm));
-}
-
-template <bool SPLIT>
-__device__ __forceinline__ void exp_finish(int i, float& l_run, float& l_o, const float* pe, uint32_t* ph,
-                                           uint32_t* pl) {
-  const float p = pe[i];
-  l_run += p;
-  if (i & 1) {
-    const float p0 = pe[i - 1];
-    const uint32_t h = pack_bf16x2(p0, p);
-    ph[i >> 1] = h;
-    if (SPLIT) {
-      pl[i >> 1] = pack_bf16x2(p0 - bf16_lo(h), p - bf16_hi(h));
-      l_o += p0;
-      l_o += p;
-    } else {
-      l_o = add_bf16x2(h, l_o);
-    }
-  }
-}
-
-template <bool SPLIT>
-__device__ __forceinline__ void exp_score(const f32x16* sc, int i, float c, float nm, float& l_run, float& l_o,
-                                          float* pe, uint32_t* ph, uint32_t* pl) {
-  exp_issue(sc, i, c, nm, pe);
-  exp_finish<SPLIT>(i, l_run, l_o, pe, ph, pl);
-}
-
-// S^T of one key tile (NA accumulators of 32 keys) for this wave's 32 queries.
-template <int D, int BM, int BN, int MODE>
-__device__ __forceinline__ void qk_tile(const FwdCtx<D, BM, BN, MODE>& x, const lds_char* Ks,
-                                        f32x16 (&s)[FwdCfg<D, BM, BN>::NA]) {
-  using T = FwdCfg<D, BM, BN>;
-  constexpr int NA = T::NA, PF = T::PF;
-  uint4 fr[PF + 1][NA];
-#pragma unroll
-  for (int kk = 0; kk < PF; ++kk) {
-#pragma unroll
-    for (int a = 0; a < NA; ++a) fr[kk][a] = lds_ld16(Ks + 32 * a * T::ROW + x.off.row(kk));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int kk = 0; kk < T::KK; ++kk) {
-    if (kk + PF < T::KK) {
-#pragma unroll
-      for (int a = 0; a < NA; ++a)
-        fr[(kk + PF) % (PF + 1)][a] = lds_ld16(Ks + 32 * a * T::ROW + x.off.row(kk + PF));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int a = 0; a < NA; ++a) s[a] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][a]), x.qf[kk], kk ? s[a] : zero16());
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// One pipeline step: tile n's softmax and PV product, tile n + 1's scores.
-//  PAR   buffer parity of n;
-//  MC    tile n is masked (its scores in sc already hold -inf where invisible);
-//  NX    1: tile n + 1 exists and is unmasked; -1: tile n + 1, if there is
-//        one, is masked (tiles treated as masked may well be full).
-// On entry sc holds S(n) and mx this lane's max over it; on return sn holds
-// S(n + 1) and mx its max (when tile n + 1 exists).
-template <int D, int BM, int BN, int MODE, int PAR, bool MC, int NX>
-__device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n, const f32x16 (&sc)[FwdCfg<D, BM, BN>::NA],
-                                         f32x16 (&sn)[FwdCfg<D, BM, BN>::NA], f32x16 (&o)[FwdCfg<D, BM, BN>::DB],
-                                         float& m_ref, float& l_run, float& l_o, float& mx) {
-  using T = FwdCfg<D, BM, BN>;
-  constexpr int KK = T::KK, PF = T::PF, DB = T::DB, NA = T::NA, NS = T::NS, NJ = T::NJ;
-  constexpr int par = PAR;
-  const bool next = NX > 0 || n + 1 < x.ntiles;
-
-  // every wave is done with tile n - 1; V(n) and K(n + 1) have landed
-  wait_vmcnt<0>();
-  lds_barrier();
-  if (next) {
-    if (n + 2 < x.ntiles) issue_tile(x, x.lds0 + par * T::TILE, x.rk, (n + 2) * T::BN);
-    issue_tile(x, x.lds0 + T::VBASE + (par ^ 1) * T::TILE, x.rv, (n + 1) * T::BN);
-  }
-  const lds_char* Kn = x.lds + (par ^ 1) * T::TILE;         // K(n + 1)
-  const lds_char* Vc = x.lds + T::VBASE + par * T::TILE;    // V(n)
-
-  uint4 fr[PF + 1][NA];
-  if (next) {
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-#pragma unroll
-      for (int a = 0; a < NA; ++a) fr[kk][a] = lds_ld16(Kn + 32 * a * T::ROW + x.off.row(kk));
-    }
-  }
-
-  // running max: move the reference (and rescale O) only when the tile's max
-  // exceeds it by more than the slack, for any lane of the wave
-  {
-    const float mt = max_xor32(mx);
-    const float cand = (mt == -INFINITY) ? -INFINITY : mt * x.c;
-    if (__ballot(cand > m_ref + kRescaleSlack)) {
-      const float mn = fmaxf(m_ref, cand);
-      // 0 when m_ref = -inf (O and l are still 0); rows that have seen no
-      // visible key yet keep mn = -inf and must not form exp2(-inf - -inf)
-      const float alpha = fast_exp2(m_ref - (mn == -INFINITY ? 0.f : mn));
-      m_ref = mn;
-      l_run *= alpha;
-      l_o *= alpha;
-      o_fence<D>(o);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      }
-      o_fence<D>(o);
-    }
-  }
-  const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
-
-  // The matrix core runs one MFMA at a time and a wave issues in order, so the
-  // VALU work is spread in small shares between consecutive MFMAs: each share
-  // issues while the MFMA before it executes.
-  //
-  // phase B: S(n + 1) on the matrix cores (NA KK MFMAs); on the VALU, P(n)
-  // scores 0 .. SB - 1 (unmasked tile) or 0 .. 7 (masked tile: its hi / lo
-  // parts are formed one PV k-step ahead in phase C instead, which keeps fewer
-  // registers live). The last share of phase B holds no score of PV k-step 0.
-  constexpr int SB = MC ? 8 : NS * 9 / 16;
-  constexpr int NB = NA * KK;
-  static_assert(MC || SB * (NB - 1) / NB >= 8, "phase B's last share must not hold k-step 0");
-  float pe[NS];
-  uint32_t ph[NS / 2], pl[NS / 2];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int m = 0; m < NB; ++m) {
-    const int kk = m / NA, a = m % NA;
-    if (next) {
-      if (a == 0 && kk + PF < KK) {
-#pragma unroll
-        for (int b = 0; b < NA; ++b)
-          fr[(kk + PF) % (PF + 1)][b] = lds_ld16(Kn + 32 * b * T::ROW + x.off.row(kk + PF));
-      }
-      sn[a] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][a]), x.qf[kk], kk ? sn[a] : zero16());
-    }
-    if (MC) {
-#pragma unroll
-      for (int i = SB * m / NB; i < SB * (m + 1) / NB; ++i) exp_score<MC>(sc, i, x.c, nm, l_run, l_o, pe, ph, pl);
-    } else {
-      // this share's exponentials, and the sums / packing of the previous share's
-#pragma unroll
-      for (int i = SB * m / NB; i < SB * (m + 1) / NB; ++i) exp_issue(sc, i, x.c, nm, pe);
-      if (m > 0) {
-#pragma unroll
-        for (int i = SB * (m - 1) / NB; i < SB * m / NB; ++i) exp_finish<MC>(i, l_run, l_o, pe, ph, pl);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // phase C: O^T += V(n)^T P(n)^T on the matrix cores, one MFMA unit (PV
-  // k-step j, head-dim block db) at a time with the V^T operands read RV - 1
-  // units ahead. On the VALU, unmasked tile: the first UC units finish P(n)
-  // (scores SB .. NS - 1, each share finished one unit later, the first unit
-  // finishing phase B's last share), all of it before the first unit of k-step
-  // NJ / 2; the units of the second half of the k-steps take the max of
-  // S(n + 1). A masked tile instead forms the next k-step's P during each k-step.
-  constexpr int NU = NJ * DB, RV = 3;
-  constexpr int UH = (NJ / 2) * DB;  // first unit of the second half
-  constexpr int UC = UH - 1;         // units that issue P(n) shares
-  static_assert(MC || SB >= 8 * (NJ / 2), "phase C's shares must belong to the second half of the k-steps");
-  bf16x8 va[RV];
-#pragma unroll
-  for (int u = 0; u < RV - 1; ++u) va[u] = tr_operand<D>(Vc + 16 * (u / DB) * T::ROW, x.off, u % DB);
-  float mxa = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int j = u / DB, db = u % DB;
-    if (u + RV - 1 < NU) {
-      const int w = u + RV - 1;
-      va[w % RV] = tr_operand<D>(Vc + 16 * (w / DB) * T::ROW, x.off, w % DB);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 pb = as_bf16x8(make_uint4(ph[4 * j], ph[4 * j + 1], ph[4 * j + 2], ph[4 * j + 3]));
-    pv_mfma<D>(o[db], va[u % RV], pb);
-    if (MC) {
-      const bf16x8 pq = as_bf16x8(make_uint4(pl[4 * j], pl[4 * j + 1], pl[4 * j + 2], pl[4 * j + 3]));
-      pv_mfma<D>(o[db], va[u % RV], pq);
-      if (j + 1 < NJ) {
-#pragma unroll
-        for (int i = 8 * (j + 1) + 8 * db / DB; i < 8 * (j + 1) + 8 * (db + 1) / DB; ++i)
-          exp_score<MC>(sc, i, x.c, nm, l_run, l_o, pe, ph, pl);
-      }
-    } else if (u <= UC) {
-      if (u < UC) {
-#pragma unroll
-        for (int i = SB + (NS - SB) * u / UC; i < SB + (NS - SB) * (u + 1) / UC; ++i) exp_issue(sc, i, x.c, nm, pe);
-      }
-      const int f0 = u ? SB + (NS - SB) * (u - 1) / UC : SB * (NB - 1) / NB;
-      const int f1 = u ? SB + (NS - SB) * u / UC : SB;
-#pragma unroll
-      for (int i = f0; i < f1; ++i) exp_finish<MC>(i, l_run, l_o, pe, ph, pl);
-    }
-    if (next && u >= UH) {
-      // mask and max of S(n + 1): NA x 16 values spread over the units of the
-      // second half of the k-steps
-      const int e = u - UH;
-#pragma unroll
-      for (int i = 16 * NA * e / (NU - UH); i < 16 * NA * (e + 1) / (NU - UH); ++i) {
-        const int v = i & 15;
-        if (NX < 0) {
-          const int base = (n + 1) * T::BN + 32 * (i >> 4) + 8 * x.half;
-          const int o = 16 * (v >> 3) + (v & 7);
-          sn[i >> 4][v] = ((!x.LEFT || o >= x.kvis_lo - base) && o < x.kvis_end - base) ? sn[i >> 4][v] : -INFINITY;
-        }
-        mxa = fmaxf(mxa, sn[i >> 4][v]);
-      }
-      asm volatile("" : "+v"(mxa));  // keep this unit's share of the max here
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  mx = mxa;  // meaningless when there is no tile n + 1
-}
-
-// MODE 0: full attention; 1: the visible keys of a row end at a band edge
-// (causal and / or a right window bound); 2: they also start at one (a left
-// window bound), so an item may begin with masked tiles.
-template <int D, int BM, int BN, int MODE, bool WRITE_LSE>
-__global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void fwd_kernel(
-    FwdParams p) {
-  using T = FwdCfg<D, BM, BN>;
-  constexpr int NA = T::NA;
-  extern __shared__ __align__(16) uint16_t smem[];
-
-  const int r = p.Hq / p.Hkv;
-  const int64_t L = xcd_logical(blockIdx.x, r);
-  const int rank = (int)(L / p.Hq);
-  const int h = (int)(L % p.Hq);
-  int b, mblk;
-  if (!decode_rank(p.cu_q, p.num_seqs, T::BM, p.levels, rank, b, mblk)) return;
-  const int g = h / r;
-
-  const int cq = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - cq;
-  const int ck = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - ck;
-
-  FwdCtx<D, BM, BN, MODE> x;
-  x.lds = (const lds_char*)smem;
-  x.lds0 = lds_addr((lds_char*)smem);
-  const int tid = threadIdx.x;
-  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  x.half = lane >> 5;
-  const int q0 = mblk * T::BM;
-  const int qi = q0 + x.wave * 32 + (lane & 31);  // this lane's query row (sequence-relative)
-  const bool qvalid = qi < Lq;
-
-  // key tiles of this block, [t_lo, t_hi), and the unmasked ones among them,
-  // [f_lo, f_hi): every key below Lk and inside every row's band
-  constexpr bool BAND = MODE > 0;
-  int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
-  if (BAND) {
-    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
-    t_lo = kr.lo / T::BN;
-    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
-    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
-    f_hi = min(t_hi, kr.full_hi / T::BN);
-  }
-  x.ntiles = t_hi;
-  x.kvis_lo = (MODE == 2) ? band_lo(qi, Lq, Lk, p.wl) : 0;
-  (void)f_lo;
-  x.kvis_end = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
-  // tile order: the unmasked tiles [t_lo, f_hi) (nm of them), then the masked
-  // ones. With a left window bound (MODE 2) the first tiles are masked too; such
-  // items run every tile as a masked step (a separate masked head before the
-  // unmasked tiles needs more registers than 2 waves per SIMD leave).
-  const int ntot = t_hi - t_lo;
-  const int nm = (MODE == 2) ? 0 : f_hi;
-  x.c = p.scale_log2;
-
-  // K / V buffer resources for this (sequence, KV head): rows past Lk read as 0
-  const uint32_t pitch = (uint32_t)p.Hkv * D * 2;
-  x.tile_bytes = pitch * T::BN;
-  const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
-  x.rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
-  x.rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
-#pragma unroll
-  for (int i = 0; i < T::DMA; ++i) {
-    const int row = (x.wave * T::DMA + i) * T::KV::ROWS_PER_DMA + lane / T::KV::CPR;
-    const int cidx = (lane % T::KV::CPR) ^ swz<D>(row);
-    x.voff[i] = (uint32_t)row * pitch + (uint32_t)cidx * 16u;
-  }
-
-  // prologue copies: K(t_lo) -> K0, V(t_lo) -> V0, K(t_lo + 1) -> K1; then Q^T
-  // into VGPRs. Buffer parity follows the local tile index n - t_lo.
-  if (ntot > 0) {
-    issue_tile(x, x.lds0, x.rk, t_lo * T::BN);
-    issue_tile(x, x.lds0 + T::VBASE, x.rv, t_lo * T::BN);
-    if (ntot > 1) issue_tile(x, x.lds0 + T::TILE, x.rk, (t_lo + 1) * T::BN);
-  }
-  {
-    // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
-    // (sign-flipped when the scale is negative, so the scale applied is positive)
-    const uint16_t* qrow = p.q + ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * x.half;
-    const uint32_t flip = p.neg_scale ? 0x80008000u : 0u;
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      uint4 u = qvalid ? ld16(qrow + 16 * kk) : zero_u4();
-      u.x ^= flip;
-      u.y ^= flip;
-      u.z ^= flip;
-      u.w ^= flip;
-      x.qf[kk] = as_bf16x8(u);
-    }
-  }
-  operand_offsets<D>(x.off, lane);
-
-  f32x16 o[T::DB];
-#pragma unroll
-  for (int db = 0; db < T::DB; ++db) o[db] = zero16();
-  float m_ref = -INFINITY;
-  float l_run = 0.f;  // sum of P (fp32): the LSE
-  float l_o = 0.f;    // sum of the P values as they enter the PV product: normalises O
-  float mx = -INFINITY;
-  f32x16 sa[NA], sb[NA];
-
-  if (ntot > 0) {
-    wait_vmcnt<0>();
-    lds_barrier();
-    qk_tile(x, x.lds, sa);
-    if (nm <= 0) {
-#pragma unroll
-      for (int a = 0; a < NA; ++a) mask_scores(x, sa[a], t_lo * T::BN + 32 * a);
-    }
-#pragma unroll
-    for (int a = 0; a < NA; ++a) mx = max16(sa[a], mx);
-  }
-
-  // S(n) lives in sa for even local index t = n - t_lo, sb for odd t; steps
-  // get the absolute tile index n. (t_lo is 0 unless MODE 2.)
-  int t = 0;
-  if (nm > 0) {
-    // steady state, unrolled by two so the buffer parity is a constant: tiles
-    // t and t + 1 both unmasked
-    for (; t + 3 <= nm; t += 2) {
-      fwd_step<D, BM, BN, MODE, 0, false, 1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
-      fwd_step<D, BM, BN, MODE, 1, false, 1>(x, t_lo + t + 1, sb, sa, o, m_ref, l_run, l_o, mx);
-    }
-    // last unmasked step (t is even); the tiles after it are all treated as
-    // masked, which is exact for full tiles too
-    fwd_step<D, BM, BN, MODE, 0, false, -1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
-    ++t;
-  } else if (ntot > 0) {
-    fwd_step<D, BM, BN, MODE, 0, true, -1>(x, t_lo, sa, sb, o, m_ref, l_run, l_o, mx);
-    t = 1;
-  }
-  // masked tail from an odd t, unrolled by two like the steady state
-  while (t < ntot) {
-    fwd_step<D, BM, BN, MODE, 1, true, -1>(x, t_lo + t, sb, sa, o, m_ref, l_run, l_o, mx);
-    if (++t >= ntot) break;
-    fwd_step<D, BM, BN, MODE, 0, true, -1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
-    ++t;
-  }
-
-  // epilogue: O = O / l, LSE = ln(2) * (m + log2 l)
-  o_fence<D>(o);
-  const float l_tot = add_xor32(l_run);
-  const float lo_tot = add_xor32(l_o);
-  if (qvalid) {
-    const float inv = (lo_tot > 0.f) ? 1.f / lo_tot : 0.f;
-    uint16_t* orow = p.out + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * x.half;
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) store_acc_row(orow + db * 32, o[db], inv);
-    if (WRITE_LSE && x.half == 0) {
-      p.lse[(int64_t)h * p.total_q + cq + qi] =
-          (l_tot > 0.f && m_ref != -INFINITY) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
-  }
-}
 
 template <int D, int MODE, bool WRITE_LSE>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
@@ -590,26 +20,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  FwdParams p;
-  p.q = static_cast<const uint16_t*>(a.q);
-  p.k = static_cast<const uint16_t*>(a.k);
-  p.v = static_cast<const uint16_t*>(a.v);
-  p.cu_q = a.cu_q;
-  p.cu_k = a.cu_k;
-  p.out = static_cast<uint16_t*>(a.out);
-  p.lse = a.lse;
-  p.num_seqs = a.num_seqs;
-  p.total_q = (int)a.total_q;
-  p.Hq = a.Hq;
-  p.Hkv = a.Hkv;
-  p.levels = ceil_div(a.max_q, T::BM);
-  // a zero (or tiny) scale becomes the smallest normal float: the scores then
-  // all map to exp2(~0) = 1 as for scale 0, while masked scores (-inf) stay -inf
-  p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
-  p.neg_scale = a.scale < 0.f ? 1 : 0;
-  const Band bd = band_of(a);
-  p.wl = bd.wl;
-  p.wr = bd.wr;
+  FwdParams p = fwd_params(a, T::BM);
   const int r = a.Hq / a.Hkv;
   const int64_t grid = grid_for(a.total_q, a.num_seqs, T::BM, a.Hq, r);
   if (grid == 0 || p.levels == 0) return hipSuccess;

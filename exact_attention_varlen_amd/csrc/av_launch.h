@@ -59,6 +59,23 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
+
+// Split-KV forward (av_fwd_split.hip). The workspace holds the chunks' partial
+// outputs, fp32 [splits][total_q][Hq][D], then their log2 row sums, fp32
+// [splits][2][Hq][total_q], each part padded to 256 bytes.
+constexpr int kMaxSplits = 64;
+constexpr int kNumCu = 256;  // compute units of the gfx950 part (8 XCDs x 32)
+inline size_t split_pad(size_t b) { return (b + 255) / 256 * 256; }
+inline size_t split_part_o_bytes(int64_t total_q, int Hq, int D, int splits) {
+  return split_pad((size_t)splits * (size_t)total_q * (size_t)Hq * (size_t)D * sizeof(float));
+}
+inline size_t split_workspace_bytes(int64_t total_q, int Hq, int D, int splits) {
+  if (splits <= 1) return 0;
+  return split_part_o_bytes(total_q, Hq, D, splits) +
+         split_pad((size_t)splits * 2 * (size_t)Hq * (size_t)total_q * sizeof(float));
+}
+hipError_t launch_fwd_split(const FwdArgs& a, int splits, void* workspace);
+int fwd_num_splits(int num_seqs, int64_t total_q, int max_q, int max_k, int Hq, int Hkv, int D);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_schedule_probe(const int32_t* cu_q, int num_seqs, int max_q, int block_m, int32_t* seq_out,
                                  int32_t* block_out, int count, void* stream);

@@ -110,6 +110,14 @@ __device__ __forceinline__ void store_acc_row(uint16_t* row_db, const f32x16& a,
   }
 }
 
+// The same block stored as fp32, unscaled / scaled (partial results).
+__device__ __forceinline__ void store_acc_row_f32(float* row_db, const f32x16& a, float scale = 1.f) {
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq)
+    *reinterpret_cast<float4*>(row_db + 8 * gq) =
+        make_float4(a[4 * gq] * scale, a[4 * gq + 1] * scale, a[4 * gq + 2] * scale, a[4 * gq + 3] * scale);
+}
+
 }  // namespace av
 
 #endif  // AV_TILES_H

@@ -71,8 +71,11 @@ enum {
   ATTN_VARLEN_ERR_BAD_SCALE = -6,         /* softmax_scale is not finite */
   ATTN_VARLEN_ERR_WORKSPACE = -7,         /* workspace NULL or smaller than attn_varlen_bwd_workspace_size() */
   ATTN_VARLEN_ERR_BAD_FLAG = -8,          /* causal not 0 or 1 */
-  ATTN_VARLEN_ERR_HIP = -9                /* the HIP runtime reported an error at launch */
+  ATTN_VARLEN_ERR_HIP = -9,               /* the HIP runtime reported an error at launch */
+  ATTN_VARLEN_ERR_BAD_SPLITS = -10        /* num_splits outside [1, ATTN_VARLEN_MAX_SPLITS] */
 };
+
+#define ATTN_VARLEN_MAX_SPLITS 64
 
 /*
  * Forward pass. [A100] benchmark script `call`; [LSE] make_call (out=, lse=,
@@ -119,6 +122,54 @@ int attn_varlen_fwd_window(const void* q, const void* k, const void* v,
                            float softmax_scale, int32_t causal,
                            int32_t window_left, int32_t window_right,
                            void* out, float* lse, void* stream);
+
+/*
+ * Split-KV forward ([GUIDE] Public API: num_splits; Forward Kernels: the
+ * combine kernel that merges partial outputs and LSEs). The visible key tiles
+ * of every (query block, query head) item are cut into num_splits contiguous
+ * chunks computed by separate workgroups; each writes its partial output and
+ * row log-sum-exp to the workspace, and a second kernel merges them in chunk
+ * order. The result is the forward of attn_varlen_fwd_window (same arguments,
+ * same outputs), up to rounding; it pays off when there are too few items to
+ * fill the GPU (short query chunks against long keys).
+ *   num_splits         1 .. ATTN_VARLEN_MAX_SPLITS; 1 runs the one-pass kernel
+ *                      (bit-identical to attn_varlen_fwd_window, workspace unused)
+ *   workspace          device scratch of at least
+ *                      attn_varlen_fwd_splitkv_workspace_size() bytes, 16-byte
+ *                      aligned (may be NULL when num_splits = 1); contents on
+ *                      entry are ignored
+ * Errors: those of attn_varlen_fwd_window, ATTN_VARLEN_ERR_BAD_SPLITS,
+ * ATTN_VARLEN_ERR_WORKSPACE. Deterministic: fixed chunking and merge order.
+ */
+int attn_varlen_fwd_splitkv(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t num_seqs, int64_t total_q, int64_t total_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            float softmax_scale, int32_t causal,
+                            int32_t window_left, int32_t window_right, int32_t num_splits,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Workspace bytes of attn_varlen_fwd_splitkv: fp32 partial outputs
+ * [num_splits][total_q][n_q_heads][head_dim] and fp32 row sums
+ * [num_splits][2][n_q_heads][total_q], each rounded up to 256 bytes; 0 when
+ * num_splits <= 1 or for negative sizes / non-positive heads.
+ */
+size_t attn_varlen_fwd_splitkv_workspace_size(int64_t total_q, int32_t n_q_heads, int32_t head_dim,
+                                              int32_t num_splits);
+
+/*
+ * A split count for these sizes (host-only, no device access): the number of
+ * chunks that best fills the GPU's concurrent workgroup slots with the
+ * forward's (query block, head) items, keeping every chunk at least four key
+ * tiles long; 1 when the items already fill the GPU. Returns a negative
+ * ATTN_VARLEN_ERR_* code for bad sizes or heads.
+ */
+int32_t attn_varlen_fwd_num_splits(int32_t num_seqs, int64_t total_q, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim);
 
 /*
  * Bytes of device workspace attn_varlen_bwd needs for these sizes. It holds the

@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_error_strings():
-    assert A.attn_varlen_version() == (1, 1)
+    assert A.attn_varlen_version() == (1, 2)
     for name, code in header_enums().items():
         s = A.attn_varlen_error_string(code)
         assert s and s != "unknown error code", name
@@ -141,6 +141,89 @@ def test_bwd_workspace_size_splits(total, hq, hkv, d, splits):
     planes = 2 * _pad(total * hq * 4)
     parts = 2 * _pad(splits * total * hkv * d * 4) if splits > 1 else 0
     assert A.attn_varlen_bwd_workspace_size(1, total, total, hq, hkv, d) == planes + parts
+
+
+def split_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=1, total_q=16, total_k=16, max_q=16, max_k=16,
+             Hq=4, Hkv=2, D=128, scale=0.125, causal=0, wl=-1, wr=-1, splits=2, out=FAKE, lse=None, ws=FAKE,
+             ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    return _lib.lib().attn_varlen_fwd_splitkv(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"],
+                                              a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["Hq"], a["Hkv"],
+                                              a["D"], a["scale"], a["causal"], a["wl"], a["wr"], a["splits"],
+                                              a["out"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), "ATTN_VARLEN_ERR_BAD_HEAD_DIM"),
+    (dict(out=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(causal=3), "ATTN_VARLEN_ERR_BAD_FLAG"),
+    (dict(splits=0), "ATTN_VARLEN_ERR_BAD_SPLITS"),
+    (dict(splits=-2), "ATTN_VARLEN_ERR_BAD_SPLITS"),
+    (dict(splits=65), "ATTN_VARLEN_ERR_BAD_SPLITS"),
+    (dict(ws=None), "ATTN_VARLEN_ERR_WORKSPACE"),
+    (dict(ws_bytes=2 * 16 * 4 * 128 * 4), "ATTN_VARLEN_ERR_WORKSPACE"),
+    (dict(ws=FAKE + 8), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(lse=FAKE + 2), "ATTN_VARLEN_ERR_MISALIGNED"),
+])
+def test_splitkv_argument_errors(over, code):
+    assert split_call(**over) == E[code]
+
+
+def test_splitkv_trivial_calls_need_no_workspace():
+    # empty problem: success without a launch; one split needs no workspace (the
+    # call is then the one-pass forward, whose launch is not reached here because
+    # total_q == 0)
+    assert split_call(total_q=0, max_q=0, ws=None, ws_bytes=0) == 0
+    assert split_call(total_q=0, max_q=0, splits=1, ws=None, ws_bytes=0) == 0
+
+
+@pytest.mark.parametrize("total_q, hq, d, splits", [(16, 4, 128, 2), (1000, 32, 64, 7), (513, 8, 256, 64),
+                                                    (0, 4, 128, 3)])
+def test_splitkv_workspace_size(total_q, hq, d, splits):
+    """fp32 partial outputs [splits][total_q][Hq][D] and row sums [splits][2][Hq][total_q], 256-byte padded."""
+    want = _pad(splits * total_q * hq * d * 4) + _pad(splits * 2 * hq * total_q * 4)
+    assert A.attn_varlen_fwd_splitkv_workspace_size(total_q, hq, d, splits) == want
+    assert A.attn_varlen_fwd_splitkv_workspace_size(total_q, hq, d, 1) == 0
+    assert A.attn_varlen_fwd_splitkv_workspace_size(-1, hq, d, splits) == 0
+
+
+@pytest.mark.parametrize("lengths_q, lengths_k, hq, hkv, d", [
+    ([3523, 2702, 2219, 1292, 1438, 413, 544, 319, 929, 3005], [3523, 2702, 2219, 1292, 1438, 413, 544, 319, 929, 3005],
+     32, 8, 128),
+    ([16384], [16384], 32, 8, 128),
+    ([4096] * 8, [4096] * 8, 8, 1, 256),
+    ([16384, 16384], [16384, 16384], 16, 16, 64),
+])
+def test_num_splits_is_one_when_items_fill_the_gpu(lengths_q, lengths_k, hq, hkv, d):
+    n = A.attn_varlen_fwd_num_splits(len(lengths_q), sum(lengths_q), max(lengths_q), max(lengths_k), hq, hkv, d)
+    assert n == 1
+
+
+@pytest.mark.parametrize("num_seqs, lq, lk, hq, hkv, d", [
+    (1, 128, 32768, 32, 8, 128),   # 32 items for 512 slots
+    (2, 256, 32768, 32, 8, 128),
+    (4, 64, 8192, 8, 1, 256),
+    (1, 1, 131072, 16, 16, 64),
+])
+def test_num_splits_fills_the_gpu_for_few_items(num_seqs, lq, lk, hq, hkv, d):
+    n = A.attn_varlen_fwd_num_splits(num_seqs, num_seqs * lq, lq, lk, hq, hkv, d)
+    bn = 64 if d <= 128 else 32
+    items = num_seqs * -(-lq // 128) * hq
+    slots = 256 * (2 if d <= 128 else 1)
+    assert 1 < n <= 64
+    assert n <= -(-lk // bn) // 4                  # every chunk keeps at least 4 key tiles
+    assert items * n >= 0.85 * slots or n == min(64, -(-lk // bn) // 4)
+
+
+def test_num_splits_short_keys_and_errors():
+    assert A.attn_varlen_fwd_num_splits(1, 128, 128, 128, 4, 4, 128) == 1   # 2 key tiles: nothing to split
+    with pytest.raises(A.AttnVarlenError):
+        A.attn_varlen_fwd_num_splits(1, 128, 128, 128, 4, 4, 96)
+    with pytest.raises(A.AttnVarlenError):
+        A.attn_varlen_fwd_num_splits(1, 128, 128, 128, 6, 4, 128)
+    with pytest.raises(A.AttnVarlenError):
+        A.attn_varlen_fwd_num_splits(0, 128, 128, 128, 4, 4, 128)
 
 
 def test_schedule_device_argument_errors():

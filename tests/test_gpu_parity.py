@@ -8,7 +8,8 @@ import torch
 import exact_attention_varlen_amd as A
 import oracle.attention as O
 import workloads as W
-from parity import (announce, check_grad, check_lse, check_out, f64, gpu_bwd, gpu_fwd, sample_rows, to_dev)
+from parity import (announce, check_grad, check_lse, check_out, f64, gpu_bwd, gpu_fwd, sample_rows, to_dev,
+                    window_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +91,79 @@ WINDOWED += [
 @pytest.mark.parametrize("wl", WINDOWED, ids=[w.name for w in WINDOWED])
 def test_parity_window(wl):
     full_parity(wl)
+
+
+# split-KV forward: the keys of every item are cut into chunks whose partial
+# results are merged; the result is the same attention (oracle), and the LSE it
+# returns drives the backward like the one-pass forward's.
+def split_parity(wl: W.Workload, splits: int, backward: bool = False):
+    inp = W.make_inputs(wl)
+    d = to_dev(inp)
+    announce(f"split-kv fwd {wl.name} splits={splits} seqlens_q={wl.seqlens_q} seqlens_k={wl.seqlens_k} "
+             f"D={wl.head_dim} causal={wl.causal} window={wl.window}")
+    out, lse = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                                 wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=True,
+                                 window_size=window_of(wl), num_splits=splits)
+    torch.cuda.synchronize()
+    q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
+    ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal,
+                             window=wl.window)
+    check_out(f64(out), ref_o)
+    check_lse(f64(lse), ref_l)
+    if backward:
+        announce(f"bwd after split-kv fwd {wl.name}")
+        dq, dk, dv = gpu_bwd(wl, d, out, lse)
+        torch.cuda.synchronize()
+        rq, rk, rv = O.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do,
+                                window=wl.window)
+        check_grad(f64(dq), rq, "dq")
+        check_grad(f64(dk), rk, "dk")
+        check_grad(f64(dv), rv, "dv")
+
+
+SPLIT_CASES = []
+for D in (64, 128, 256):
+    for c in (False, True):
+        for sp in (2, 7):
+            SPLIT_CASES.append((W.Workload(f"ragged-d{D}-{'c' if c else 'f'}", [1, 77, 300, 513, 0, 129], 8, 2, D, c),
+                                sp))
+SPLIT_CASES += [
+    (W.Workload("chunk-vs-long-d128-c", [100, 37], 8, 2, 128, True, seqlens_k=[1500, 900]), 3),
+    (W.Workload("chunk-vs-long-d128-c", [100, 37], 8, 2, 128, True, seqlens_k=[1500, 900]), 64),
+    (W.Workload("lq-ne-lk-d128-f", [100, 300, 5, 0], 4, 1, 128, False, seqlens_k=[250, 64, 0, 33]), 5),
+    (W.Workload("lq-gt-lk-d64-c", [300, 70], 2, 2, 64, True, seqlens_k=[64, 200]), 3),
+    (W.Workload("window-d128-f-w100_37", [1, 77, 300, 513, 0, 129], 8, 2, 128, False, window=(100, 37)), 4),
+    (W.Workload("window-d256-c-w200", [700, 129], 8, 2, 256, True, window=(200, -1)), 3),
+    (W.Workload("window-d64-c-w64", [1200], 4, 4, 64, True, window=(64, -1)), 16),
+    (W.Workload("decode-like-d256-c", [1, 1, 2, 1], 8, 1, 256, True, seqlens_k=[700, 33, 1000, 64]), 8),
+]
+
+
+@pytest.mark.parametrize("wl,splits", SPLIT_CASES, ids=[f"{w.name}-s{s}" for w, s in SPLIT_CASES])
+def test_parity_splitkv(wl, splits):
+    split_parity(wl, splits)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_splitkv_drives_backward(D):
+    split_parity(W.Workload(f"split-bwd-d{D}", [300, 129, 513], 8, 2, D, True), 3, backward=True)
+
+
+def test_splitkv_one_split_is_the_plain_call_and_deterministic():
+    wl = W.Workload("split-one", [700, 33, 1200], 8, 2, 128, True)
+    d = to_dev(W.make_inputs(wl, with_dout=False))
+    announce("split-kv splits=1 vs plain, determinism")
+    args = (d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+            wl.softmax_scale, True)
+    o1, l1 = A.attn_varlen_fwd(*args, return_lse=True)
+    o2, l2 = A.attn_varlen_fwd(*args, return_lse=True, num_splits=1)
+    o3, l3 = A.attn_varlen_fwd(*args, return_lse=True, num_splits=5)
+    o4, l4 = A.attn_varlen_fwd(*args, return_lse=True, num_splits=5)
+    o5 = A.attn_varlen_fwd(*args, num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    assert torch.equal(o3, o5)
 
 
 # --------------------------------------------------------------------------
@@ -184,6 +258,34 @@ FULL_SIZE = [
 @pytest.mark.parametrize("wl,mode", FULL_SIZE, ids=[w.name for w, _ in FULL_SIZE])
 def test_parity_full_size_sampled(wl, mode):
     sampled_parity(wl, mode)
+
+
+# query chunks against long keys (few items per launch): the split-KV forward
+# with the library's split count, sampled rows against the oracle
+SPLIT_FULL = [
+    W.Workload("2x256-vs-32768-gqa32/8-d128-causal", [256, 256], 32, 8, 128, True, seqlens_k=[32768, 32768],
+               backward=False),
+    W.Workload("4x64-vs-8192-gqa8/1-d256-causal", [64] * 4, 8, 1, 256, True, seqlens_k=[8192] * 4, backward=False),
+    W.Workload("1x128-vs-65536-mha16-d64-full", [128], 16, 16, 64, False, seqlens_k=[65536], backward=False),
+]
+
+
+@pytest.mark.parametrize("wl", SPLIT_FULL, ids=[w.name for w in SPLIT_FULL])
+def test_parity_splitkv_full_size_sampled(wl):
+    inp = W.make_inputs(wl, with_dout=False)
+    d = to_dev(inp)
+    n = A.attn_varlen_fwd_num_splits(len(wl.seqlens_q), wl.total_q, wl.max_seqlen_q, wl.max_seqlen_k,
+                                     wl.n_q_heads, wl.n_kv_heads, wl.head_dim)
+    assert n > 1
+    announce(f"split-kv fwd {wl.name} (full size, {n} splits, sampled oracle)")
+    out, lse = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                                 wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=True, num_splits=0)
+    torch.cuda.synchronize()
+    q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+    rows = sample_rows(wl.cu_seqlens_q, extra=64)
+    r, ro, rl = O.forward_rows(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, rows)
+    check_out(f64(out[torch.as_tensor(r)]), ro)
+    check_lse(f64(lse[:, torch.as_tensor(r)]), rl)
 
 
 # --------------------------------------------------------------------------
