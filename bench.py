@@ -402,6 +402,95 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
     return 0
 
 
+def visible_pairs(wl) -> int:
+    """Exact number of visible (query, key) pairs per head, with the causal
+    mask and the local window of the workload (bottom-right aligned band)."""
+    import numpy as np
+
+    wl_, wr_ = (-1, -1) if wl.window is None else wl.window
+    if wl.causal:
+        wr_ = 0 if wr_ < 0 else min(wr_, 0)
+    total = 0
+    for Lq, Lk in zip(wl.seqlens_q, wl.seqlens_k):
+        i = np.arange(Lq, dtype=np.int64)
+        lo = np.zeros(Lq, dtype=np.int64) if wl_ < 0 else np.clip(i + Lk - Lq - wl_, 0, Lk)
+        hi = np.full(Lq, Lk, dtype=np.int64) if wr_ < 0 else np.clip(i + Lk - Lq + wr_ + 1, 0, Lk)
+        total += int(np.maximum(hi - lo, 0).sum())
+    return total
+
+
+def window_split_secondary():
+    """Local-window and split-KV forward timings (steady state, HIP graphs).
+
+    Work is counted as 4 * D * Hq per visible (query, key) pair (exact count),
+    the forward's algorithmic flop; fwd+bwd as 3.5 x that."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    out_rows = {}
+    cases = [
+        ("window", W.Workload("single-16384-gqa32/8-d128-causal-w4096", [16384], 32, 8, 128, True,
+                              window=(4096, -1)), None),
+        ("window", W.Workload("single-16384-gqa32/8-d128-causal-w512", [16384], 32, 8, 128, True,
+                              window=(512, -1)), None),
+        ("window", W.Workload("single-16384-gqa32/8-d128-full-w1024_1024", [16384], 32, 8, 128, False,
+                              window=(1024, 1024)), None),
+        ("split", W.Workload("2x256-vs-32768-gqa32/8-d128-causal", [256, 256], 32, 8, 128, True,
+                             seqlens_k=[32768, 32768]), (1, 0)),
+        ("split", W.Workload("1x128-vs-65536-mha16-d64-full", [128], 16, 16, 64, False, seqlens_k=[65536]),
+         (1, 0)),
+        ("split", W.Workload("4x64-vs-8192-gqa8/1-d256-causal", [64] * 4, 8, 1, 256, True, seqlens_k=[8192] * 4),
+         (1, 0)),
+    ]
+    for kind, wl, splits in cases:
+        log(f"{kind} workload {wl.name}")
+        d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+        mq, mk = wl.max_seqlen_q, wl.max_seqlen_k
+        win = (-1, -1) if wl.window is None else wl.window
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+        flop = 4.0 * visible_pairs(wl) * wl.n_q_heads * wl.head_dim
+        row = {**wl.describe(), "visible_pairs_per_head": visible_pairs(wl), "fwd_gflop": flop / 1e9}
+        for ns in (splits or (1,)):
+            n = ns if ns else A.attn_varlen_fwd_num_splits(len(wl.seqlens_q), wl.total_q, mq, mk, wl.n_q_heads,
+                                                           wl.n_kv_heads, wl.head_dim)
+            ws = torch.empty(max(16, A.attn_varlen_fwd_splitkv_workspace_size(wl.total_q, wl.n_q_heads,
+                                                                              wl.head_dim, n)),
+                             dtype=torch.uint8, device="cuda:0")
+
+            def fwd():
+                A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
+                                  wl.softmax_scale, wl.causal, out=out, lse=lse, window_size=win, num_splits=n,
+                                  workspace=ws)
+
+            ms = time_graph_steady(fwd, 10, 3)
+            key = "fwd" if splits is None else f"fwd_splits_{n}"
+            row[key + "_ms"] = ms
+            row[key + "_tflops"] = flop / (ms * 1e-3) / 1e12
+        if kind == "window":
+            dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+            wsb = torch.empty(max(16, A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k,
+                                                                       wl.n_q_heads, wl.n_kv_heads, wl.head_dim)),
+                              dtype=torch.uint8, device="cuda:0")
+
+            def step():
+                A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
+                                  wl.softmax_scale, wl.causal, out=out, lse=lse, window_size=win)
+                A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"],
+                                  d["cu_seqlens_k"], mq, mk, wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv,
+                                  workspace=wsb, window_size=win)
+
+            ms = time_graph_steady(step, 5, 3)
+            row["fwdbwd_ms"] = ms
+            row["fwdbwd_tflops"] = 3.5 * flop / (ms * 1e-3) / 1e12
+        out_rows[wl.name] = row
+        del d, out, lse
+        torch.cuda.empty_cache()
+    return out_rows
+
+
 def all_configs_table(include_long: bool):
     """Forward and forward+backward time of every config (fwd with LSE; steady
     state, several calls per HIP graph): one JSON object per config on stdout."""
@@ -458,6 +547,8 @@ def main(argv=None):
     ap.add_argument("--all-configs", action="store_true",
                     help="only time forward and forward+backward of every config (one JSON line each) and exit")
     ap.add_argument("--long", action="store_true", help="with --all-configs: include the 64K and 128K sequences")
+    ap.add_argument("--window-split", action="store_true",
+                    help="only time the local-window and split-KV workloads (one JSON line) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
@@ -477,6 +568,10 @@ def main(argv=None):
     if a.all_configs:
         warm_gpu(1.0)
         return all_configs_table(a.long)
+    if a.window_split:
+        warm_gpu(1.0)
+        print(json.dumps(window_split_secondary()), flush=True)
+        return 0
     if a.eager_only:
         return eager_only(W.packed_16k(), a.steps, a.warmup)
     primary = W.packed_16k()
@@ -498,6 +593,7 @@ def main(argv=None):
             }
         log("forward with / without LSE, head_dim 64")
         secondary["lse_ratio"] = lse_ratio(W.hd64_mha())
+        secondary["window_and_split_kv"] = window_split_secondary()
     log("sustained clocks and power of the primary step")
     clocks = power_phase(res.pop("_step_fn"))
     # dominant kernel of the step: the one with the largest total time

@@ -505,14 +505,29 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   }
   x.ntiles = t_hi;
   x.kvis_lo = (MODE == 2) ? band_lo(qi, Lq, Lk, p.wl) : 0;
-  (void)f_lo;
   x.kvis_end = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
-  // tile order: the unmasked tiles [t_lo, f_hi) (nm of them), then the masked
-  // ones. With a left window bound (MODE 2) the first tiles are masked too; such
-  // items run every tile as a masked step (a separate masked head before the
-  // unmasked tiles needs more registers than 2 waves per SIMD leave).
+  // tile order (local indices): the unmasked tiles [0, nm), then the masked
+  // ones. With a left window bound (MODE 2) the first tiles cross some row's
+  // left band edge: the nh (even) of them that lie left of every row's right
+  // edge are masked by the step before them and then take the unmasked P path,
+  // when the window is at least a tile wide (every row that reaches such a tile
+  // then sees at least BN keys, as in the unmasked tiles of any item). Narrower
+  // windows run every tile as a masked step.
   const int ntot = t_hi - t_lo;
-  const int nm = (MODE == 2) ? 0 : (SPLIT ? max(0, min(f_hi, t_hi) - t_lo) : f_hi);
+  int nh = 0;
+  int nm = SPLIT ? max(0, min(f_hi, t_hi) - t_lo) : f_hi;
+  if (MODE == 2) {
+    nm = 0;
+    if (p.wl >= T::BN) {
+      const int nme = max(0, min(f_hi, t_hi) - t_lo);
+      int hh = max(0, min(min(f_lo, f_hi), t_hi) - t_lo);
+      hh += hh & 1;
+      if (hh < nme) {
+        nh = hh;
+        nm = nme;
+      }
+    }
+  }
   x.c = p.scale_log2;
 
   // K / V buffer resources for this (sequence, KV head): rows past Lk read as 0
@@ -565,7 +580,7 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
     wait_vmcnt<0>();
     lds_barrier();
     qk_tile(x, x.lds, sa);
-    if (nm <= 0) {
+    if (MODE == 2 || nm <= 0) {
 #pragma unroll
       for (int a = 0; a < NA; ++a) mask_scores(x, sa[a], t_lo * T::BN + 32 * a);
     }
@@ -577,6 +592,13 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   // get the absolute tile index n. (t_lo is 0 unless MODE 2 or SPLIT.)
   int t = 0;
   if (nm > 0) {
+    if (MODE == 2) {
+      // left-edge tiles: each step masks the next tile's scores
+      for (; t < nh; t += 2) {
+        fwd_step<D, BM, BN, MODE, 0, false, -1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
+        fwd_step<D, BM, BN, MODE, 1, false, -1>(x, t_lo + t + 1, sb, sa, o, m_ref, l_run, l_o, mx);
+      }
+    }
     // steady state, unrolled by two so the buffer parity is a constant: tiles
     // t and t + 1 both unmasked
     for (; t + 3 <= nm; t += 2) {
