@@ -491,6 +491,34 @@ def window_split_secondary():
     return out_rows
 
 
+def persistent_vs_grid(wl, rounds: int = 3):
+    """Forward with the one-workgroup-per-item grid against the persistent
+    scheduler (attn_varlen_fwd_persistent), steady state, alternating rounds."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl, with_dout=False).items()}
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+    sched = torch.zeros(A.SCHED_BYTES, dtype=torch.uint8, device="cuda:0")
+
+    def fwd(pers):
+        return lambda: A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                         wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal, out=out,
+                                         lse=lse, persistent=pers, sched=sched)
+
+    times = {False: [], True: []}
+    for _ in range(rounds):
+        for pers in (False, True):
+            times[pers].append(time_graph_steady(fwd(pers), 10, 3))
+    g, p = statistics.median(times[False]), statistics.median(times[True])
+    fl = wl.accounted_fwd_flop()
+    return {"workload": wl.name, "grid_fwd_ms": g, "persistent_fwd_ms": p, "grid_tflops": fl / (g * 1e-3) / 1e12,
+            "persistent_tflops": fl / (p * 1e-3) / 1e12, "persistent_speedup": g / p}
+
+
 def all_configs_table(include_long: bool):
     """Forward and forward+backward time of every config (fwd with LSE; steady
     state, several calls per HIP graph): one JSON object per config on stdout."""
@@ -594,6 +622,7 @@ def main(argv=None):
         log("forward with / without LSE, head_dim 64")
         secondary["lse_ratio"] = lse_ratio(W.hd64_mha())
         secondary["window_and_split_kv"] = window_split_secondary()
+        secondary["persistent_scheduler"] = persistent_vs_grid(primary)
     log("sustained clocks and power of the primary step")
     clocks = power_phase(res.pop("_step_fn"))
     # dominant kernel of the step: the one with the largest total time

@@ -38,6 +38,8 @@ __all__ = [
     "attn_varlen_fwd_splitkv",
     "attn_varlen_fwd_splitkv_workspace_size",
     "attn_varlen_fwd_num_splits",
+    "attn_varlen_fwd_persistent",
+    "SCHED_BYTES",
     "attn_varlen_error_string",
     "attn_varlen_version",
     "attn_varlen_schedule_host",
@@ -107,13 +109,17 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
                     softmax_scale: Optional[float] = None, causal: bool = False, return_lse: bool = False,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     window_size: Tuple[int, int] = (-1, -1), num_splits: int = 1,
-                    workspace: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None, persistent: bool = False,
+                    sched: Optional[torch.Tensor] = None):
     """Forward pass. Returns ``out`` or ``(out, lse)`` when ``return_lse`` (or ``lse`` is given).
 
     ``window_size = (left, right)`` restricts each query to a local band of keys
     (``attn_varlen_fwd_window``); ``(-1, -1)`` is no window. ``num_splits > 1``
     splits every item's keys over that many workgroups and merges the partial
-    results (``attn_varlen_fwd_splitkv``); ``0`` lets the library choose."""
+    results (``attn_varlen_fwd_splitkv``); ``0`` lets the library choose.
+    ``persistent=True`` runs the persistent scheduler (``attn_varlen_fwd_persistent``,
+    one split only); ``sched`` is its zeroed scratch (``SCHED_BYTES`` bytes),
+    allocated per call when not given."""
     dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     total_q, Hq, D = q.shape
     total_k, Hkv, _ = k.shape
@@ -146,6 +152,20 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         if rc != 0:
             raise AttnVarlenError(rc, "attn_varlen_fwd_splitkv")
         return (out, lse) if lse is not None else out
+    if persistent:
+        if num_splits != 1:
+            raise ValueError("the persistent scheduler runs the one-pass forward (num_splits=1)")
+        if sched is None:
+            sched = torch.zeros(SCHED_BYTES, dtype=torch.uint8, device=dev)
+        elif sched.device != dev or sched.numel() * sched.element_size() < SCHED_BYTES:
+            raise ValueError(f"sched must hold {SCHED_BYTES} bytes on {dev}")
+        rc = lib().attn_varlen_fwd_persistent(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                              num_seqs, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq,
+                                              Hkv, D, float(softmax_scale), int(bool(causal)), wl, wr, _ptr(out),
+                                              _ptr(lse), _ptr(sched), _stream(dev))
+        if rc != 0:
+            raise AttnVarlenError(rc, "attn_varlen_fwd_persistent")
+        return (out, lse) if lse is not None else out
     rc = lib().attn_varlen_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                       cu_seqlens_q.numel() - 1, total_q, total_k, int(max_seqlen_q),
                                       int(max_seqlen_k), Hq, Hkv, D, float(softmax_scale), int(bool(causal)), wl, wr,
@@ -153,6 +173,16 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     if rc != 0:
         raise AttnVarlenError(rc, "attn_varlen_fwd_window")
     return (out, lse) if lse is not None else out
+
+
+SCHED_BYTES = 64  # ATTN_VARLEN_SCHED_BYTES
+
+
+def attn_varlen_fwd_persistent(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                               causal=False, window_left=-1, window_right=-1, sched=None, **kw):
+    """``attn_varlen_fwd`` with the persistent scheduler (the C entry point of the same name)."""
+    return attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                           window_size=(window_left, window_right), persistent=True, sched=sched, **kw)
 
 
 def attn_varlen_fwd_splitkv_workspace_size(total_q: int, n_q_heads: int, head_dim: int, num_splits: int) -> int:

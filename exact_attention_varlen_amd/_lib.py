@@ -33,6 +33,9 @@ _SIGNATURES = {
                                                c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                                                c_vp, c_size, c_vp]),
     "attn_varlen_fwd_splitkv_workspace_size": (c_size, [c_i64, c_i32, c_i32, c_i32]),
+    "attn_varlen_fwd_persistent": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32,
+                                                  c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                                  c_vp]),
     "attn_varlen_fwd_num_splits": (c_i32, [c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "attn_varlen_bwd_workspace_size": (c_size, [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32]),
     "attn_varlen_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,

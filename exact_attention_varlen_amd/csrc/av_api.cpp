@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 2;
+constexpr int kVersionMinor = 3;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -135,6 +135,27 @@ int attn_varlen_fwd_splitkv(const void* q, const void* k, const void* v, const i
   a.out = out;
   a.lse = lse;
   return av::launch_fwd_split(a, num_splits, workspace) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+}
+
+int attn_varlen_fwd_persistent(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                               int32_t window_right, void* out, float* lse, void* sched, void* stream) {
+  static_assert(ATTN_VARLEN_SCHED_BYTES >= av::kSchedWords * 4, "scheduler words");
+  int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                        n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
+  if (rc != ATTN_VARLEN_OK) return rc;
+  if (!out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (!sched) return ATTN_VARLEN_ERR_WORKSPACE;
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4)) || !aligned(sched, 4)) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (total_q == 0) return ATTN_VARLEN_OK;
+  av::FwdArgs a = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
+                                max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left,
+                                window_right, stream);
+  a.out = out;
+  a.lse = lse;
+  return av::launch_fwd_persistent(a, sched) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
 }
 
 size_t attn_varlen_fwd_splitkv_workspace_size(int64_t total_q, int32_t n_q_heads, int32_t head_dim,

@@ -119,6 +119,9 @@ struct FwdParams {
   float* part_o;
   float* part_l;
   int splits;
+  // persistent scheduling (fwd_kernel_persistent only): 8 queue counters and a
+  // count of finished workgroups, all 0 on entry and returned to 0 on exit
+  unsigned int* sched;
 };
 
 // O^T accumulation. At head_dim 256 (one wave per SIMD, O = 128 registers per
@@ -436,17 +439,15 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n
 // window bound), so an item may begin with masked tiles.
 // SPLIT: the workgroup runs one chunk of the item's key tiles and writes the
 // chunk's partial result (FwdParams::part_o / part_l) instead of out / lse.
-template <int D, int BM, int BN, int MODE, bool WRITE_LSE, bool SPLIT = false>
-__global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void fwd_kernel(
-    FwdParams p) {
+//
+// One work item: logical index L = (query block rank, key chunk) x query head,
+// heads innermost, so that the r heads of a KV group are adjacent indices.
+template <int D, int BM, int BN, int MODE, bool WRITE_LSE, bool SPLIT>
+__device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t* smem) {
   using T = FwdCfg<D, BM, BN>;
   constexpr int NA = T::NA;
-  extern __shared__ __align__(16) uint16_t smem[];
 
-  // work unit = (query block rank, key chunk) x query head; the r heads of a KV
-  // group are adjacent (same XCD), and so share the chunk's K / V in L2
   const int r = p.Hq / p.Hkv;
-  const int64_t L = xcd_logical(blockIdx.x, r);
   const int h = (int)(L % p.Hq);
   int rank, split = 0;
   if (SPLIT) {
@@ -652,6 +653,66 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
   }
 }
 
+// One workgroup per work item; the block index is spread over the XCDs so that
+// the r heads of a KV group (adjacent logical indices) run on one XCD and share
+// K / V in its L2.
+template <int D, int BM, int BN, int MODE, bool WRITE_LSE, bool SPLIT = false>
+__global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void fwd_kernel(
+    FwdParams p) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  fwd_item<D, BM, BN, MODE, WRITE_LSE, SPLIT>(p, xcd_logical(blockIdx.x, p.Hq / p.Hkv), smem);
+}
+
+// Persistent scheduling (FlashAttention repository guide, Core Abstractions:
+// the varlen-aware persistent tile scheduler): as many workgroups as the chip
+// holds at once, each running work items until none is left. The n_items
+// logical indices (longest first, a multiple of 8 r) are dealt to 8 queues by
+// KV group: queue q holds the groups q, q + 8, q + 16, ... in order. A
+// workgroup takes items from the queue of the XCD it runs on, then from the
+// other queues in turn. The heads of a group thus mostly share one XCD's L2,
+// and XCDs that run faster (under the board power limit they do not all hold
+// the same clock) take more of the work, which a fixed block-to-XCD assignment
+// cannot do. Every workgroup leaves the loop once all queues are exhausted;
+// the last one to finish returns the counters to 0 for the next call.
+template <int D, int BM, int BN, int MODE, bool WRITE_LSE>
+__global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void
+fwd_kernel_persistent(FwdParams p, unsigned int n_items) {
+  using T = FwdCfg<D, BM, BN>;
+  extern __shared__ __align__(16) uint16_t smem[];
+  volatile int* slot = reinterpret_cast<volatile int*>(reinterpret_cast<char*>(smem) + T::LDS_BYTES);
+  const unsigned int r = (unsigned int)(p.Hq / p.Hkv);
+  const unsigned int per_queue = n_items / kNumXcd;  // items per queue (whole groups)
+  unsigned int xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+  unsigned int k = 0;  // queues found empty so far (meaningful in thread 0)
+  for (;;) {
+    __syncthreads();  // every wave is done with the previous item's LDS and slot
+    if (threadIdx.x == 0) {
+      int L = -1;
+      while (k < (unsigned int)kNumXcd) {
+        const unsigned int q = (xcc + k) % kNumXcd;
+        const unsigned int idx = atomicAdd(p.sched + q, 1u);
+        if (idx < per_queue) {
+          L = (int)(((idx / r) * kNumXcd + q) * r + idx % r);
+          break;
+        }
+        ++k;
+      }
+      *slot = L;
+    }
+    __syncthreads();
+    const int L = __builtin_amdgcn_readfirstlane(*slot);  // the same in every lane
+    if (L < 0) break;
+    fwd_item<D, BM, BN, MODE, WRITE_LSE, false>(p, L, smem);
+  }
+  if (threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(p.sched + kNumXcd, 1u) == gridDim.x - 1) {
+      for (int q = 0; q <= kNumXcd; ++q) atomicExch(p.sched + q, 0u);
+    }
+  }
+}
+
 // Kernel parameters of a validated call (the grid's query blocks have bm rows).
 inline FwdParams fwd_params(const FwdArgs& a, int bm) {
   FwdParams p;
@@ -677,6 +738,7 @@ inline FwdParams fwd_params(const FwdArgs& a, int bm) {
   p.part_o = nullptr;
   p.part_l = nullptr;
   p.splits = 1;
+  p.sched = nullptr;
   return p;
 }
 

@@ -75,6 +75,9 @@ inline size_t split_workspace_bytes(int64_t total_q, int Hq, int D, int splits) 
          split_pad((size_t)splits * 2 * (size_t)Hq * (size_t)total_q * sizeof(float));
 }
 hipError_t launch_fwd_split(const FwdArgs& a, int splits, void* workspace);
+// Persistent forward (av_fwd_persist.hip); sched: kSchedWords zeroed words.
+constexpr int kSchedWords = 9;
+hipError_t launch_fwd_persistent(const FwdArgs& a, void* sched);
 int fwd_num_splits(int num_seqs, int64_t total_q, int max_q, int max_k, int Hq, int Hkv, int D);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_schedule_probe(const int32_t* cu_q, int num_seqs, int max_q, int block_m, int32_t* seq_out,

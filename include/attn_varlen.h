@@ -152,6 +152,31 @@ int attn_varlen_fwd_splitkv(const void* q, const void* k, const void* v,
                             void* stream);
 
 /*
+ * Forward with persistent, varlen-aware scheduling ([GUIDE] Core
+ * Abstractions: the persistent tile scheduler). Same arguments, outputs and
+ * results as attn_varlen_fwd_window (bit-identical: each work item runs the
+ * same code); only the assignment of work items to workgroups differs. The
+ * kernel launches as many workgroups as the GPU holds at once; they take the
+ * (query block, query head) items, longest first, from eight per-XCD queues
+ * (their own XCD's first, then the others), so that faster XCDs take more work.
+ *   sched              device scratch of ATTN_VARLEN_SCHED_BYTES bytes, 4-byte
+ *                      aligned, all zero before its first use; every call
+ *                      leaves it zero again. Calls that share one sched buffer
+ *                      must not run concurrently (stream-ordered use is fine).
+ * Errors: those of attn_varlen_fwd_window; ATTN_VARLEN_ERR_WORKSPACE for a NULL
+ * sched, ATTN_VARLEN_ERR_MISALIGNED for a misaligned one.
+ */
+#define ATTN_VARLEN_SCHED_BYTES 64
+int attn_varlen_fwd_persistent(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t num_seqs, int64_t total_q, int64_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                               float softmax_scale, int32_t causal,
+                               int32_t window_left, int32_t window_right,
+                               void* out, float* lse, void* sched, void* stream);
+
+/*
  * Workspace bytes of attn_varlen_fwd_splitkv: fp32 partial outputs
  * [num_splits][total_q][n_q_heads][head_dim] and fp32 row sums
  * [num_splits][2][n_q_heads][total_q], each rounded up to 256 bytes; 0 when

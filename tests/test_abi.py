@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_error_strings():
-    assert A.attn_varlen_version() == (1, 2)
+    assert A.attn_varlen_version() == (1, 3)
     for name, code in header_enums().items():
         s = A.attn_varlen_error_string(code)
         assert s and s != "unknown error code", name
@@ -224,6 +224,38 @@ def test_num_splits_short_keys_and_errors():
         A.attn_varlen_fwd_num_splits(1, 128, 128, 128, 6, 4, 128)
     with pytest.raises(A.AttnVarlenError):
         A.attn_varlen_fwd_num_splits(0, 128, 128, 128, 4, 4, 128)
+
+
+def persist_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=1, total_q=16, total_k=16, max_q=16, max_k=16,
+             Hq=4, Hkv=2, D=128, scale=0.125, causal=0, wl=-1, wr=-1, out=FAKE, lse=None, sched=FAKE, stream=None)
+    a.update(over)
+    return _lib.lib().attn_varlen_fwd_persistent(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"],
+                                                 a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["Hq"],
+                                                 a["Hkv"], a["D"], a["scale"], a["causal"], a["wl"], a["wr"],
+                                                 a["out"], a["lse"], a["sched"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), "ATTN_VARLEN_ERR_BAD_HEAD_DIM"),
+    (dict(out=None), "ATTN_VARLEN_ERR_NULL_POINTER"),
+    (dict(sched=None), "ATTN_VARLEN_ERR_WORKSPACE"),
+    (dict(sched=FAKE + 2), "ATTN_VARLEN_ERR_MISALIGNED"),
+    (dict(Hq=5), "ATTN_VARLEN_ERR_BAD_HEADS"),
+    (dict(causal=7), "ATTN_VARLEN_ERR_BAD_FLAG"),
+])
+def test_persistent_argument_errors(over, code):
+    assert persist_call(**over) == E[code]
+
+
+def test_persistent_empty_problem_is_a_no_op():
+    assert persist_call(total_q=0, max_q=0) == 0
+
+
+def test_sched_bytes_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_VARLEN_SCHED_BYTES (\d+)", text)
+    assert m and int(m.group(1)) == A.SCHED_BYTES
 
 
 def test_schedule_device_argument_errors():

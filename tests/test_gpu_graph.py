@@ -97,3 +97,38 @@ def test_graph_replays_match_eager_splitkv_window(wl, splits):
         torch.cuda.synchronize()
         for name, t, r in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk, dv), ref):
             assert torch.equal(t, r), f"replay {rep}: {name} differs from the eager result"
+
+
+def test_graph_replays_match_eager_persistent():
+    wl = W.Workload("graph-persistent-d128", [300, 77, 900], 8, 2, 128, True)
+    d = to_dev(W.make_inputs(wl, with_dout=False))
+    dev = d["q"].device
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device=dev)
+    sched = torch.zeros(A.SCHED_BYTES, dtype=torch.uint8, device=dev)
+
+    def fwd():
+        A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                          wl.max_seqlen_k, wl.softmax_scale, wl.causal, out=out, lse=lse, persistent=True,
+                          sched=sched)
+
+    announce(f"graph eager {wl.name}")
+    fwd()
+    torch.cuda.synchronize()
+    ref = [out.clone(), lse.clone()]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    announce(f"graph capture {wl.name}")
+    with torch.cuda.graph(g, stream=stream):
+        fwd()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        announce(f"graph replay {rep} {wl.name}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {rep} differs"
+        assert int(sched.count_nonzero()) == 0

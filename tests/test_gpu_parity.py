@@ -458,3 +458,52 @@ def test_autograd_wrapper_matches_direct_calls():
     o2, l2, dq, dk, dv = _run_all(wl, d)
     assert torch.equal(out.detach(), o2)
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+
+
+# persistent scheduler: the same items run by fewer workgroups that take them
+# from per-XCD queues; every result must be bit-identical to the one-pass grid,
+# and the scheduler scratch must be zero again after each call
+PERSIST_CASES = [
+    W.packed_16k(),
+    W.Workload("ragged-d64-f", [1, 77, 300, 513, 0, 129], 8, 2, 64, False),
+    W.Workload("ragged-d256-c", [1, 77, 300, 513, 0, 129], 8, 2, 256, True),
+    W.Workload("window-d128-c-w300", [2100, 1500, 7], 8, 2, 128, True, window=(300, -1)),
+    W.Workload("lq-ne-lk-d128-f-w20_10", [100, 300, 5, 0], 4, 1, 128, False, seqlens_k=[250, 64, 0, 33],
+               window=(20, 10)),
+    W.Workload("many-items-d128-c", [8192] * 4, 32, 8, 128, True, backward=False),
+]
+
+
+@pytest.mark.parametrize("wl", PERSIST_CASES, ids=[w.name for w in PERSIST_CASES])
+def test_persistent_scheduler_matches_grid(wl):
+    d = to_dev(W.make_inputs(wl, with_dout=False))
+    sched = torch.zeros(A.SCHED_BYTES, dtype=torch.uint8, device=d["q"].device)
+    args = (d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+            wl.softmax_scale, wl.causal)
+    win = window_of(wl)
+    announce(f"persistent vs grid {wl.name}")
+    o1, l1 = A.attn_varlen_fwd(*args, return_lse=True, window_size=win)
+    for rep in range(2):
+        o2, l2 = A.attn_varlen_fwd(*args, return_lse=True, window_size=win, persistent=True, sched=sched)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"call {rep}: out differs"
+        assert torch.equal(l1, l2), f"call {rep}: lse differs"
+        assert int(sched.count_nonzero()) == 0, f"call {rep}: scheduler scratch not reset"
+
+
+def test_persistent_scheduler_against_oracle_and_smaller_second_call():
+    sched = torch.zeros(A.SCHED_BYTES, dtype=torch.uint8, device="cuda:0")
+    for wl in (W.Workload("persist-a", [700, 33, 1200], 8, 2, 128, True),
+               W.Workload("persist-b", [90, 300], 4, 2, 64, False)):
+        inp = W.make_inputs(wl, with_dout=False)
+        d = to_dev(inp)
+        announce(f"persistent vs oracle {wl.name}")
+        out, lse = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                                     wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=True, persistent=True,
+                                     sched=sched)
+        torch.cuda.synchronize()
+        q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+        ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal)
+        check_out(f64(out), ref_o)
+        check_lse(f64(lse), ref_l)
+        assert int(sched.count_nonzero()) == 0
