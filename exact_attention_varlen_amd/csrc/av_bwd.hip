@@ -145,97 +145,139 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kSchedValu = 0x002;
 
-// dV += P^T dO and dK += dS^T Q for one k-step (16 queries) of a 32-query
-// block whose S and dP are done. The transposed operands and the rows'
-// lse2 / Delta are read from LDS before the exp / convert work, so that work
-// covers their latency.
-template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_kstep(const f32x16& s, const f32x16& dp, int ks, const lds_char* qblk,
-                                           const lds_char* dblk, const float* lse2_s, const float* dlt_s, f32x16* dk,
-                                           f32x16* dv, float c, int qrow0, int rlo, int rhi, const OperandOffsets<D>& off,
-                                           int half) {
-  using T = DkdvCfg<D>;
-  const lds_char* qrows = qblk + 16 * ks * T::ROW;
-  const lds_char* drows = dblk + 16 * ks * T::ROW;
-  bf16x8 at_do[D / 32], at_q[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    at_do[db] = tr_operand<D>(drows, off, db);
-    at_q[db] = tr_operand<D>(qrows, off, db);
-  }
-  // register v <-> query row (qrow0 + 16*(v/8) + 8*half + (v%8)) of the step; the 8
-  // registers of k-step ks are the 8 consecutive queries 16 ks + 8 half + e
-  const int qo = qrow0 + 16 * ks + 8 * half;
-  const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
-  const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
-  const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
-  const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
-  const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-  const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-  __builtin_amdgcn_sched_barrier(0);  // all of this k-step's LDS reads are in flight
-  float pv[8], dsv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int v = 8 * ks + e;
-    float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
-    if (MASK) pe = (qo + e >= rlo && qo + e <= rhi) ? pe : 0.f;
-    pv[e] = pe;
-    dsv[e] = pe * (dp[v] - dl[e]);
-  }
-  const bf16x8 pb = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-  const bf16x8 sb = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dv[db] = mfma32x32x16(at_do[db], pb, dv[db]);
-    dk[db] = mfma32x32x16(at_q[db], sb, dk[db]);
-  }
-}
-
 // One step: BMQ query rows (starting at sequence row m0) against this wave's
-// 32 keys. For each pair of 32-query blocks the S and dP products (four
-// independent MFMA chains) run with their LDS operands fetched two k-steps
-// ahead; then each block's dV / dK updates.
+// 32 keys, as NB blocks of 32 query rows. Each block b needs
+//   A(b): S = Q K^T and dP = dO V^T (2 KK MFMAs, Q / dO rows from LDS),
+//   B(b): P = exp2(S c - lse2) (masked), dS = P (dP - Delta), packed to bf16,
+//         for its two 16-query k-steps (8 scores per lane each),
+//   C(b): dV += P^T dO and dK += dS^T Q (4 DB MFMAs, transposed rows from LDS).
+// The matrix core runs one MFMA at a time and a wave issues in order, so the
+// vector work of B only overlaps the MFMAs when it is spread between them. The
+// step is software-pipelined over the blocks in phases of NU = 2 KK = 4 DB MFMA
+// units each:
+//   X(b): A(b)     with B(b - 1, k-step 1) between its MFMAs,
+//   Y(b): C(b - 1) with B(b, k-step 0) between its MFMAs,
+// for b = 0 .. NB (the first and last phases run without partner work). Each
+// unit also issues the LDS reads one or two units ahead: the next k-steps of
+// the Q / dO rows, the transposed operands of C (a ring of RV), and the rows'
+// lse2 / Delta of the next B part.
 template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
                                           const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
                                           f32x16* dv, float c, int m0, int rlo, int rhi, const OperandOffsets<D>& off,
                                           int half) {
   using T = DkdvCfg<D>;
-  constexpr int KK = D / 16;
-  constexpr int PF = 2;  // prefetch distance in k-steps
-#pragma unroll
-  for (int qp = 0; qp < T::BMQ / 64; ++qp) {
-    const lds_char* src[4] = {Qs + (64 * qp) * T::ROW, dOs + (64 * qp) * T::ROW, Qs + (64 * qp + 32) * T::ROW,
-                              dOs + (64 * qp + 32) * T::ROW};
-    f32x16 acc[4] = {zero16(), zero16(), zero16(), zero16()};  // s0, dp0, s1, dp1
-    uint4 fr[PF + 1][4];
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fr[kk][j] = lds_ld16(src[j] + off.row(kk));
+  constexpr int KK = D / 16, DB = D / 32, NB = T::BMQ / 32, PF = 2, RV = 3;
+  constexpr int NU = 2 * KK;  // MFMA units per phase
+  static_assert(NU == 4 * DB, "the units of A(b) and C(b) must pair up");
+  const int rl = rlo - m0, rh = rhi - m0;  // step-relative rows that see this lane's key
+
+  f32x16 sacc[2], dacc[2];          // S and dP of block b in [b & 1]
+  uint32_t pw[2][2][4], sw[2][2][4];  // bf16 pairs of P and dS: [b & 1][k-step][pair]
+  float l2[2][8], dl[2][8];         // lse2 / Delta of the rows of B(., k-step)
+  float pe[8], pm[8], dsv[8];
+  uint4 fr[PF + 1][2];              // Q / dO row operands of A, PF k-steps ahead
+  bf16x8 va[RV];                    // transposed operands of C, RV - 1 units ahead
+
+  auto load_rowvals = [&](int b, int ks) {
+    const int qo = 32 * b + 16 * ks + 8 * half;
+    const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
+    const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
+    const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
+    l2[ks][0] = a0.x; l2[ks][1] = a0.y; l2[ks][2] = a0.z; l2[ks][3] = a0.w;
+    l2[ks][4] = a1.x; l2[ks][5] = a1.y; l2[ks][6] = a1.z; l2[ks][7] = a1.w;
+    dl[ks][0] = b0.x; dl[ks][1] = b0.y; dl[ks][2] = b0.z; dl[ks][3] = b0.w;
+    dl[ks][4] = b1.x; dl[ks][5] = b1.y; dl[ks][6] = b1.z; dl[ks][7] = b1.w;
+  };
+  auto load_rows = [&](int b, int kk) {
+    fr[kk % (PF + 1)][0] = lds_ld16(Qs + 32 * b * T::ROW + off.row(kk));
+    fr[kk % (PF + 1)][1] = lds_ld16(dOs + 32 * b * T::ROW + off.row(kk));
+  };
+  // unit w of C(b): k-step w / (2 DB), head-dim block (w / 2) % DB, dV (even) or dK (odd)
+  auto load_tr = [&](int b, int w) {
+    const int ks = w / (2 * DB), db = (w / 2) % DB;
+    const lds_char* rows = ((w & 1) ? Qs : dOs) + (32 * b + 16 * ks) * T::ROW;
+    va[w % RV] = tr_operand<D>(rows, off, db);
+  };
+  // B(b, ks): score e is issued (exp) at unit iss(e) and finished one unit later
+  auto b_issue = [&](int b, int ks, int e) {
+    pe[e] = fast_exp2(__builtin_fmaf(sacc[b & 1][8 * ks + e], c, -l2[ks][e]));
+  };
+  auto b_finish = [&](int b, int ks, int e) {
+    float pv = pe[e];
+    if (MASK) {
+      const int row = 32 * b + 16 * ks + 8 * half + e;
+      pv = (row >= rl && row <= rh) ? pv : 0.f;
     }
-    // The fences keep the compiler from sinking each load to just before its
-    // MFMA: the loads of k-step kk + PF are issued ahead of the MFMAs of kk.
+    pm[e] = pv;
+    dsv[e] = pv * (dacc[b & 1][8 * ks + e] - dl[ks][e]);
+    if (e & 1) {
+      pw[b & 1][ks][e >> 1] = pack_bf16x2(pm[e - 1], pm[e]);
+      sw[b & 1][ks][e >> 1] = pack_bf16x2(dsv[e - 1], dsv[e]);
+    }
+  };
+  // the B share of unit u: issue the scores whose slot is u, finish those of u - 1
+  auto b_share = [&](int b, int ks, int u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e * NU / 8 == u) b_issue(b, ks, e);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e * NU / 8 + 1 == u) b_finish(b, ks, e);
+    }
+  };
+  auto b_tail = [&](int b, int ks) {  // scores whose finishing slot is past the phase
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e * NU / 8 + 1 >= NU) b_finish(b, ks, e);
+    }
+  };
+
+  load_rows(0, 0);
+  load_rows(0, 1);
+  load_rowvals(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b <= NB; ++b) {
+    // ---- X(b): A(b), B(b - 1, 1) ----
+    if (b >= 1) load_rowvals(b - 1, 1);  // lse2 / Delta of B(b - 1, 1)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + PF < KK) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fr[(kk + PF) % (PF + 1)][j] = lds_ld16(src[j] + off.row(kk + PF));
+    for (int u = 0; u < NU; ++u) {
+      const int kk = u / 2, j = u & 1;
+      if (b < NB) {
+        if (j == 0 && kk + PF < KK) load_rows(b, kk + PF);
+        f32x16& acc = j ? dacc[b & 1] : sacc[b & 1];
+        acc = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk], kk ? acc : zero16());
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[j] = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][j]), (j & 1) ? vf[kk] : kf[kk], acc[j]);
+      if (b >= 1) b_share(b - 1, 1, u);
+      // warm the ring of C(b - 1) and the lse2 / Delta of B(b, 0) in the last units
+      if (b >= 1 && u >= NU - (RV - 1)) load_tr(b - 1, u - (NU - (RV - 1)));
+      if (b < NB && u == NU - 1) load_rowvals(b, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (b >= 1) b_tail(b - 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- Y(b): C(b - 1), B(b, 0) ----
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        dkdv_kstep<D, MASK>(acc[2 * b], acc[2 * b + 1], ks, src[2 * b], src[2 * b + 1], lse2_s, dlt_s, dk, dv, c,
-                            64 * qp + 32 * b, rlo - m0, rhi - m0, off, half);
+    for (int u = 0; u < NU; ++u) {
+      if (b >= 1) {
+        if (u + RV - 1 < NU) load_tr(b - 1, u + RV - 1);
+        const int ks = u / (2 * DB), db = (u / 2) % DB;
+        const uint32_t* wv = (u & 1) ? sw[(b - 1) & 1][ks] : pw[(b - 1) & 1][ks];
+        const bf16x8 bop = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
+        f32x16& acc = (u & 1) ? dk[db] : dv[db];
+        acc = mfma32x32x16(va[u % RV], bop, acc);
+      }
+      if (b < NB) b_share(b, 0, u);
+      // the first Q / dO row k-steps of the next block
+      if (b + 1 < NB && u >= NU - PF) load_rows(b + 1, u - (NU - PF));
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (b < NB) b_tail(b, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
