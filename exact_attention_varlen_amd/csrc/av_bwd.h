@@ -15,8 +15,10 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* delta;
-  const float* lse2;
+  float* delta;       // Delta = rowsum(dO * O) [Hq][total_q] (written by the dQ kernel at head dims 64 / 128)
+  float* lse2;        // LSE * log2(e), +inf for rows without a visible key (likewise)
+  const uint16_t* out;  // forward output O and its LSE (read by the dQ kernel at head dims 64 / 128)
+  const float* lse;
   const int32_t* cu_q;
   const int32_t* cu_k;
   uint16_t* dq;

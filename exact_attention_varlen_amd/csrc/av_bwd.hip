@@ -3,11 +3,13 @@
 //
 // The FlashAttention repository guide (Backward Kernels) splits the backward
 // into a preprocess kernel, a main kernel and a postprocess kernel. Here:
-//  1. bwd_prep_kernel   per query row and head: Delta_i = sum_d dO_id * O_id
+//  1. row terms        per query row and head: Delta_i = sum_d dO_id * O_id
 //                       (fp32) and the LSE in base 2, lse2_i = lse_i * log2(e)
 //                       (+inf for rows without a visible key, so that
 //                       exp2(s - lse2) is exactly 0 there), into the caller's
-//                       workspace.
+//                       workspace: at head dims 64 / 128 by the dQ kernel (3),
+//                       which holds the row's dO anyway and runs first; at head
+//                       dim 256 by bwd_prep_kernel.
 //  2. bwd_dkdv_kernel   key-stationary: a workgroup owns 128 keys of one KV head
 //                       and loops over every query head of that head's group and
 //                       every 64-row query block that can see the keys,
@@ -549,9 +551,32 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
       df[kk] = as_bf16x8(qvalid ? ld16(p.dout + off + 16 * kk) : zero_u4());
     }
   }
+  // the row terms of the backward for this lane's query row (the preprocess of
+  // the FlashAttention repository guide's Backward Kernels, done here because
+  // this workgroup holds the row's dO already): Delta = sum_d dO_d O_d in fp32,
+  // lse2 = LSE log2(e), +inf for a row without a visible key so exp2(s - lse2)
+  // is exactly 0. Written for the dK / dV kernel, which runs after this one.
+  float dlt, lse2;
+  {
+    const int64_t off = ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * half;
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const uint4 o = qvalid ? ld16(p.out + off + 16 * kk) : zero_u4();
+      const uint4 d = __builtin_bit_cast(uint4, df[kk]);
+      part += dot8_bf16(d, o);
+    }
+    dlt = part + __shfl_xor(part, 32);
+  }
   const int64_t lidx = (int64_t)h * p.total_q + cq + qi;
-  const float lse2 = qvalid ? p.lse2[lidx] : INFINITY;
-  const float dlt = qvalid ? p.delta[lidx] : 0.f;
+  {
+    const float l = qvalid ? p.lse[lidx] : -INFINITY;
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+  if (qvalid && half == 0) {
+    p.delta[lidx] = dlt;
+    p.lse2[lidx] = lse2;
+  }
   OperandOffsets<D> off;
   operand_offsets<D>(off, lane);
 
@@ -631,6 +656,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   p.dout = static_cast<const uint16_t*>(a.dout);
   p.delta = a.delta;
   p.lse2 = lse2;
+  p.out = static_cast<const uint16_t*>(a.out);
+  p.lse = a.lse;
   p.cu_q = f.cu_q;
   p.cu_k = f.cu_k;
   p.dq = static_cast<uint16_t*>(a.dq);
@@ -650,23 +677,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
 
-  if (f.total_k > 0) {
-    using T = DkdvCfg<D>;
-    auto kern = bwd_dkdv_kernel<D, BAND>;
-    static bool done = false;
-    hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
-    if (e != hipSuccess) return e;
-    BwdParams pk = p;
-    pk.levels = ceil_div(f.max_k, T::BNK);
-    const int64_t grid = grid_for(f.total_k, f.num_seqs, T::BNK, f.Hkv, 1);
-    if (grid > 0 && pk.levels > 0) {
-      prof_begin("attn_bwd_dkdv", stream);
-      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
-      prof_end(stream);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
+  // dQ first: it also writes the Delta / lse2 rows that dK / dV reads
   if (f.total_q > 0) {
     using T = DqCfg<D>;
     auto kern = bwd_dq_kernel<D, BAND>;
@@ -684,13 +695,31 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
       if (e != hipSuccess) return e;
     }
   }
+  if (f.total_k > 0) {
+    using T = DkdvCfg<D>;
+    auto kern = bwd_dkdv_kernel<D, BAND>;
+    static bool done = false;
+    hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
+    if (e != hipSuccess) return e;
+    BwdParams pk = p;
+    pk.levels = ceil_div(f.max_k, T::BNK);
+    const int64_t grid = grid_for(f.total_k, f.num_seqs, T::BNK, f.Hkv, 1);
+    if (grid > 0 && pk.levels > 0) {
+      prof_begin("attn_bwd_dkdv", stream);
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
+      prof_end(stream);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   return hipSuccess;
 }
 
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a) {
   float* lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(a.delta) + ws_plane_bytes(a.f.total_q, a.f.Hq));
-  if (a.f.total_q > 0) {
+  // head dims 64 / 128: the dQ kernel forms the row terms itself
+  if (D == 256 && a.f.total_q > 0) {
     const hipError_t e = launch_prep<D>(a, a.delta, lse2);
     if (e != hipSuccess) return e;
   }

@@ -607,6 +607,8 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   p.dout = static_cast<const uint16_t*>(a.dout);
   p.delta = a.delta;
   p.lse2 = lse2;
+  p.out = static_cast<const uint16_t*>(a.out);
+  p.lse = a.lse;
   p.cu_q = f.cu_q;
   p.cu_k = f.cu_k;
   p.dq = static_cast<uint16_t*>(a.dq);
