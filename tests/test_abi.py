@@ -252,6 +252,15 @@ def test_persistent_empty_problem_is_a_no_op():
     assert persist_call(total_q=0, max_q=0) == 0
 
 
+def test_python_split_and_persistent_argument_errors():
+    """The binding passes bad split counts and scratch straight to the C checks."""
+    import torch
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):  # CPU tensors are rejected before any call
+        A.attn_varlen_fwd(q, q, q, cu, cu, 4, 4, num_splits=2)
+
+
 def test_sched_bytes_constant_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define ATTN_VARLEN_SCHED_BYTES (\d+)", text)

@@ -507,3 +507,33 @@ def test_persistent_scheduler_against_oracle_and_smaller_second_call():
         check_out(f64(out), ref_o)
         check_lse(f64(lse), ref_l)
         assert int(sched.count_nonzero()) == 0
+
+
+# edge cases of the split-KV and persistent paths: zero and negative scale,
+# single-token queries, one key, more splits than key tiles
+EDGE = [
+    (W.Workload("edge-scale0-d64-f", [150, 90], 2, 1, 64, False, softmax_scale=0.0), 3),
+    (W.Workload("edge-negscale-d128-c", [200, 64], 4, 2, 128, True, softmax_scale=-0.09), 4),
+    (W.Workload("edge-decode1-d256-f", [1, 1, 1], 8, 1, 256, False, seqlens_k=[1, 2000, 33]), 16),
+    (W.Workload("edge-onekey-d128-c", [5, 1], 4, 4, 128, True, seqlens_k=[1, 1]), 2),
+]
+
+
+@pytest.mark.parametrize("wl,splits", EDGE, ids=[w.name for w, _ in EDGE])
+def test_edge_cases_split_and_persistent(wl, splits):
+    inp = W.make_inputs(wl)
+    d = to_dev(inp)
+    q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+    ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal)
+    args = (d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+            wl.softmax_scale, wl.causal)
+    announce(f"edge split {wl.name} splits={splits}")
+    o1, l1 = A.attn_varlen_fwd(*args, return_lse=True, num_splits=splits)
+    announce(f"edge persistent {wl.name}")
+    o2, l2 = A.attn_varlen_fwd(*args, return_lse=True, persistent=True)
+    o3, l3 = A.attn_varlen_fwd(*args, return_lse=True)
+    torch.cuda.synchronize()
+    for o, l in ((o1, l1), (o2, l2)):
+        check_out(f64(o), ref_o)
+        check_lse(f64(l), ref_l)
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
