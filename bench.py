@@ -224,6 +224,34 @@ def power_phase(fn, seconds: float = 4.0):
     }
 
 
+# Numbers the pages print for workloads this bench also runs, on other GPUs
+# ("FA2 vs NATTEN on A100" results table: 16K single sequence, 32/8 heads, hd128,
+# non-causal; "[FA4/B200] return_lse=True ..." repro: 2x16384, 16 heads, hd64,
+# with the LSE). Context only: different hardware, not the target.
+PAGE_NUMBERS = {
+    "single-16384-gqa32/8-d128-full": {"source": "A100, FA2 (flash-attn 2.7.4)", "fwd_tflops": 216.0,
+                                       "fwdbwd_tflops": 196.0},
+    "2x16384-mha16-d64-full": {"source": "B200, FA4 forward with LSE", "fwd_tflops": 2.199e3 / 2.5281},
+}
+
+
+def context_other_hardware(secondary):
+    out = {}
+    s16 = secondary.get("single-16384-gqa32/8-d128-full")
+    if s16:
+        ref = PAGE_NUMBERS["single-16384-gqa32/8-d128-full"]
+        out["single-16384-gqa32/8-d128-full"] = {
+            "page": ref, "ours_fwd_tflops": s16["fwd_tflops"], "ours_fwdbwd_tflops": s16["fwdbwd_tflops"],
+            "fwd_ratio": s16["fwd_tflops"] / ref["fwd_tflops"],
+            "fwdbwd_ratio": s16["fwdbwd_tflops"] / ref["fwdbwd_tflops"]}
+    lr = secondary.get("lse_ratio")
+    if lr:
+        ref = PAGE_NUMBERS["2x16384-mha16-d64-full"]
+        out["2x16384-mha16-d64-full"] = {"page": ref, "ours_fwd_tflops_with_lse": lr["with_lse_tflops"],
+                                         "fwd_ratio": lr["with_lse_tflops"] / ref["fwd_tflops"]}
+    return out
+
+
 def lse_ratio(wl, rounds: int = 5, reps: int = 10):
     """Forward with and without the LSE output, timed in alternating rounds (the
     pages' with / without LSE comparison); returns medians and their ratio."""
@@ -678,6 +706,7 @@ def main(argv=None):
         "kernels": kern,
         "roofline": roofline,
         "secondary": secondary,
+        "context_other_hardware": context_other_hardware(secondary),
     }
     if not a.no_cpu_baseline:
         log("cpu baseline (float64 oracle)")
