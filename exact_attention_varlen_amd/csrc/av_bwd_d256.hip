@@ -170,7 +170,44 @@ __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char
     tdo[u] = tr_operand<kD>(dOs + 16 * (u / kDB) * T::ROW, off, u % kDB);
     tq[u] = tr_operand<kD>(Qs + 16 * (u / kDB) * T::ROW, off, u % kDB);
   }
-  bf16x8 pb, sb;
+  // P and dS of k-step ks (8 queries per lane: 16 ks + 8 half + e). k-step 0
+  // is formed before the first unit; k-step 1 is spread over the units of
+  // k-step 0 (one score issued per unit, finished one unit later), so that its
+  // vector work issues between those MFMAs instead of as one block.
+  float l2[2][8], dl[2][8];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int qo = 16 * ks + 8 * half;
+    const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
+    const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
+    const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
+    l2[ks][0] = a0.x; l2[ks][1] = a0.y; l2[ks][2] = a0.z; l2[ks][3] = a0.w;
+    l2[ks][4] = a1.x; l2[ks][5] = a1.y; l2[ks][6] = a1.z; l2[ks][7] = a1.w;
+    dl[ks][0] = b0.x; dl[ks][1] = b0.y; dl[ks][2] = b0.z; dl[ks][3] = b0.w;
+    dl[ks][4] = b1.x; dl[ks][5] = b1.y; dl[ks][6] = b1.z; dl[ks][7] = b1.w;
+  }
+  float pe[8], pm[8], dsv[8];
+  uint32_t pw[2][4], sw[2][4];
+  auto issue = [&](int ks, int e) { pe[e] = fast_exp2(__builtin_fmaf(s[8 * ks + e], c, -l2[ks][e])); };
+  auto finish = [&](int ks, int e) {
+    float pv = pe[e];
+    if (MASK) {
+      const int row = 16 * ks + 8 * half + e;
+      pv = (row >= rlo && row <= rhi) ? pv : 0.f;
+    }
+    pm[e] = pv;
+    dsv[e] = pv * (dp[8 * ks + e] - dl[ks][e]);
+    if (e & 1) {
+      pw[ks][e >> 1] = pack_bf16x2(pm[e - 1], pm[e]);
+      sw[ks][e >> 1] = pack_bf16x2(dsv[e - 1], dsv[e]);
+    }
+  };
+#pragma unroll
+  for (int e = 0; e < 8; ++e) issue(0, e);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) finish(0, e);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < 2 * kDB; ++u) {
     const int ks = u / kDB, db = u % kDB;
@@ -179,29 +216,13 @@ __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char
       tdo[w % RV] = tr_operand<kD>(dOs + 16 * (w / kDB) * T::ROW, off, w % kDB);
       tq[w % RV] = tr_operand<kD>(Qs + 16 * (w / kDB) * T::ROW, off, w % kDB);
     }
-    if (db == 0) {
-      // register v <-> query row 16 (v / 8) + 8 half + v % 8 of the step; the
-      // 8 registers of k-step ks are queries 16 ks + 8 half + e
-      const int qo = 16 * ks + 8 * half;
-      const float4 a0 = *reinterpret_cast<const float4*>(lse2_s + qo);
-      const float4 a1 = *reinterpret_cast<const float4*>(lse2_s + qo + 4);
-      const float4 b0 = *reinterpret_cast<const float4*>(dlt_s + qo);
-      const float4 b1 = *reinterpret_cast<const float4*>(dlt_s + qo + 4);
-      const float l2[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const float dl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = 8 * ks + e;
-        float pe = fast_exp2(__builtin_fmaf(s[v], c, -l2[e]));
-        if (MASK) pe = (qo + e >= rlo && qo + e <= rhi) ? pe : 0.f;
-        pv[e] = pe;
-        dsv[e] = pe * (dp[v] - dl[e]);
-      }
-      pb = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      sb = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-    }
+    // k-step 1's scores: issue score u, finish score u - 1 (the last one just
+    // before k-step 1's first unit)
+    if (u < 8) issue(1, u);
+    if (u >= 1 && u <= 8) finish(1, u - 1);
     __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 pb = as_bf16x8(make_uint4(pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]));
+    const bf16x8 sb = as_bf16x8(make_uint4(sw[ks][0], sw[ks][1], sw[ks][2], sw[ks][3]));
     mfma_agpr(dv[db], tdo[u % RV], pb);
     mfma_agpr(dk[db], tq[u % RV], sb);
     __builtin_amdgcn_sched_barrier(0);
