@@ -23,6 +23,7 @@ guide's Public API.
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Optional, Tuple
 
 import torch
@@ -41,6 +42,7 @@ __all__ = [
     "attn_varlen_fwd_persistent",
     "SCHED_BYTES",
     "attn_varlen_error_string",
+    "attn_varlen_validate_seqlens",
     "attn_varlen_version",
     "attn_varlen_schedule_host",
     "attn_varlen_schedule_device",
@@ -84,6 +86,34 @@ def _check_bf16(name: str, t: torch.Tensor, dev: torch.device):
         raise ValueError(f"{name} must be contiguous")
     if t.dim() != 3:
         raise ValueError(f"{name} must be 3-D (tokens, heads, head_dim), got {tuple(t.shape)}")
+
+
+SEQLEN_BITS = {1: "a first cu_seqlens entry is not 0", 2: "cu_seqlens decreases",
+               4: "a last cu_seqlens entry differs from the token count",
+               8: "a sequence is longer than its max_seqlen"}
+
+
+def attn_varlen_validate_seqlens(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, total_q: int, total_k: int,
+                                 max_seqlen_q: int, max_seqlen_k: int) -> int:
+    """Check the packing arrays on the device (waits for the result): returns 0 when valid, else the
+    ATTN_VARLEN_SEQLEN_* bit mask."""
+    dev = cu_seqlens_q.device
+    res = torch.empty(1, dtype=torch.int32, device=dev)
+    rc = lib().attn_varlen_validate_seqlens(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1,
+                                            int(total_q), int(total_k), int(max_seqlen_q), int(max_seqlen_k),
+                                            _ptr(res), _stream(dev))
+    if rc != 0:
+        raise AttnVarlenError(rc, "attn_varlen_validate_seqlens")
+    return int(res.item())
+
+
+def _maybe_validate(cu_q, cu_k, total_q, total_k, max_q, max_k):
+    if os.environ.get("ATTN_VARLEN_VALIDATE") != "1":
+        return
+    bits = attn_varlen_validate_seqlens(cu_q, cu_k, total_q, total_k, max_q, max_k)
+    if bits:
+        why = "; ".join(t for b, t in SEQLEN_BITS.items() if bits & b)
+        raise ValueError(f"invalid cu_seqlens / max_seqlen (mask {bits}): {why}")
 
 
 def _check_inputs(q, k, v, cu_q, cu_k):
@@ -138,6 +168,7 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
             raise ValueError(f"lse must be contiguous float32 ({Hq}, {total_q}) on {dev}")
     wl, wr = (int(window_size[0]), int(window_size[1]))
     num_seqs = cu_seqlens_q.numel() - 1
+    _maybe_validate(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)
     if num_splits == 0:
         num_splits = attn_varlen_fwd_num_splits(num_seqs, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, D)
     if num_splits != 1:
@@ -239,6 +270,7 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
         if t.shape != ref.shape:
             raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
     num_seqs = cu_seqlens_q.numel() - 1
+    _maybe_validate(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)
     ws_bytes = attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)

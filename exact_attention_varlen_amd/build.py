@@ -24,7 +24,8 @@ LIB_NAME = "libattn_varlen.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["av_api.cpp", "av_prof.cpp", "av_fwd.hip", "av_fwd_split.hip", "av_fwd_persist.hip", "av_bwd.hip", "av_bwd_d256.hip"]
+SOURCES = ["av_api.cpp", "av_prof.cpp", "av_fwd.hip", "av_fwd_split.hip", "av_fwd_persist.hip", "av_validate.hip",
+           "av_bwd.hip", "av_bwd_d256.hip"]
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops keeps the device compiler from
 # forming packed fp32 instructions; the host pass warns that it does not know the

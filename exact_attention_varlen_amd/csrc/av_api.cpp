@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 3;
+constexpr int kVersionMinor = 4;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -219,6 +219,25 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* 
   return attn_varlen_bwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
                                 max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, -1, -1, dout,
                                 out, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+int attn_varlen_validate_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                                 int64_t total_q, int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t* result, void* stream) {
+  static_assert(ATTN_VARLEN_SEQLEN_BAD_START == av::kSeqlenBadStart &&
+                    ATTN_VARLEN_SEQLEN_DECREASING == av::kSeqlenDecreasing &&
+                    ATTN_VARLEN_SEQLEN_BAD_TOTAL == av::kSeqlenBadTotal &&
+                    ATTN_VARLEN_SEQLEN_OVER_MAX == av::kSeqlenOverMax,
+                "result bits");
+  if (!cu_seqlens_q || !cu_seqlens_k || !result) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (num_seqs < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(result, 4))
+    return ATTN_VARLEN_ERR_MISALIGNED;
+  return av::launch_validate_seqlens(cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
+                                     max_seqlen_k, result, stream) == hipSuccess
+             ? ATTN_VARLEN_OK
+             : ATTN_VARLEN_ERR_HIP;
 }
 
 const char* attn_varlen_error_string(int code) {

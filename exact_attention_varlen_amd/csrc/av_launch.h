@@ -58,6 +58,14 @@ struct BwdArgs {
   float* delta;  // workspace (Delta, lse2, partial dK / dV): see av_bwd.h
 };
 
+// Packing-array check (av_validate.hip): bits of the result word.
+constexpr int kSeqlenBadStart = 1;    // cu_seqlens_q[0] or cu_seqlens_k[0] is not 0
+constexpr int kSeqlenDecreasing = 2;  // some cu_seqlens entry is smaller than the one before
+constexpr int kSeqlenBadTotal = 4;    // cu_seqlens_*[num_seqs] differs from total_q / total_k
+constexpr int kSeqlenOverMax = 8;     // some sequence is longer than max_seqlen_q / max_seqlen_k
+hipError_t launch_validate_seqlens(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int64_t total_q,
+                                   int64_t total_k, int max_q, int max_k, int32_t* result, void* stream);
+
 hipError_t launch_fwd(const FwdArgs& a);
 
 // Split-KV forward (av_fwd_split.hip). The workspace holds the chunks' partial

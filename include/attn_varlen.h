@@ -197,6 +197,30 @@ int32_t attn_varlen_fwd_num_splits(int32_t num_seqs, int64_t total_q, int32_t ma
                                    int32_t head_dim);
 
 /*
+ * Device-side check of the packing arrays, which every call takes as a
+ * precondition (the host-side checks only see the sizes): cu_seqlens_q[0] and
+ * cu_seqlens_k[0] are 0, both arrays are non-decreasing, their last entries are
+ * total_q and total_k, and no sequence is longer than max_seqlen_q /
+ * max_seqlen_k. Asynchronous on `stream`: writes to `result` (one device int32)
+ * a bit mask, 0 when the arrays are valid, else an OR of
+ *   ATTN_VARLEN_SEQLEN_BAD_START (1)  a first entry is not 0
+ *   ATTN_VARLEN_SEQLEN_DECREASING (2) an entry is smaller than the one before
+ *   ATTN_VARLEN_SEQLEN_BAD_TOTAL (4)  a last entry differs from the total
+ *   ATTN_VARLEN_SEQLEN_OVER_MAX (8)   a sequence is longer than its max_seqlen
+ * Errors: ATTN_VARLEN_ERR_NULL_POINTER, ATTN_VARLEN_ERR_BAD_SEQLEN (num_seqs < 1,
+ * negative sizes), ATTN_VARLEN_ERR_MISALIGNED (result not 4-byte aligned),
+ * ATTN_VARLEN_ERR_HIP. The Python binding runs it before each call when the
+ * environment variable ATTN_VARLEN_VALIDATE is 1 and raises on a non-zero mask.
+ */
+#define ATTN_VARLEN_SEQLEN_BAD_START 1
+#define ATTN_VARLEN_SEQLEN_DECREASING 2
+#define ATTN_VARLEN_SEQLEN_BAD_TOTAL 4
+#define ATTN_VARLEN_SEQLEN_OVER_MAX 8
+int attn_varlen_validate_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                                 int64_t total_q, int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t* result, void* stream);
+
+/*
  * Bytes of device workspace attn_varlen_bwd needs for these sizes. It holds the
  * fp32 row term Delta_i = sum_d dout_id * out_id per query row and head ([GUIDE]
  * Backward Kernels: the preprocess kernel) and the LSE in base 2, each

@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_error_strings():
-    assert A.attn_varlen_version() == (1, 3)
+    assert A.attn_varlen_version() == (1, 4)
     for name, code in header_enums().items():
         s = A.attn_varlen_error_string(code)
         assert s and s != "unknown error code", name
@@ -259,6 +259,22 @@ def test_python_split_and_persistent_argument_errors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):  # CPU tensors are rejected before any call
         A.attn_varlen_fwd(q, q, q, cu, cu, 4, 4, num_splits=2)
+
+
+def test_validate_seqlens_argument_errors():
+    l = _lib.lib()
+    assert l.attn_varlen_validate_seqlens(None, FAKE, 1, 4, 4, 4, 4, FAKE, None) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+    assert l.attn_varlen_validate_seqlens(FAKE, FAKE, 1, 4, 4, 4, 4, None, None) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+    assert l.attn_varlen_validate_seqlens(FAKE, FAKE, 0, 4, 4, 4, 4, FAKE, None) == E["ATTN_VARLEN_ERR_BAD_SEQLEN"]
+    assert l.attn_varlen_validate_seqlens(FAKE, FAKE, 1, -1, 4, 4, 4, FAKE, None) == E["ATTN_VARLEN_ERR_BAD_SEQLEN"]
+    assert l.attn_varlen_validate_seqlens(FAKE, FAKE, 1, 4, 4, 4, 4, FAKE + 2, None) == E["ATTN_VARLEN_ERR_MISALIGNED"]
+
+
+def test_seqlen_bits_match_header():
+    text = open(HEADER).read()
+    for bit, name in ((1, "BAD_START"), (2, "DECREASING"), (4, "BAD_TOTAL"), (8, "OVER_MAX")):
+        m = re.search(r"#define ATTN_VARLEN_SEQLEN_%s (\d+)" % name, text)
+        assert m and int(m.group(1)) == bit and bit in A.SEQLEN_BITS
 
 
 def test_sched_bytes_constant_matches_header():

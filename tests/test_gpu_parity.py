@@ -537,3 +537,30 @@ def test_edge_cases_split_and_persistent(wl, splits):
         check_out(f64(o), ref_o)
         check_lse(f64(l), ref_l)
     assert torch.equal(o2, o3) and torch.equal(l2, l3)
+
+
+@pytest.mark.parametrize("cu_q,cu_k,tq,tk,mq,mk,bits", [
+    ([0, 5, 12], [0, 3, 12], 12, 12, 7, 9, 0),          # valid
+    ([1, 5, 12], [0, 3, 12], 12, 12, 7, 9, 1),          # first entry not 0
+    ([0, 7, 5, 12], [0, 3, 4, 12], 12, 12, 7, 8, 2),    # decreasing
+    ([0, 5, 12], [0, 3, 11], 12, 12, 7, 9, 4),          # last entry != total
+    ([0, 5, 12], [0, 3, 12], 12, 12, 6, 9, 8),          # longer than max_seqlen_q
+    ([0, 7, 5, 12], [1, 3, 4, 11], 12, 12, 3, 3, 15),   # everything at once
+])
+def test_validate_seqlens(cu_q, cu_k, tq, tk, mq, mk, bits):
+    announce(f"validate seqlens {cu_q} {cu_k}")
+    cq = torch.tensor(cu_q, dtype=torch.int32, device="cuda:0")
+    ck = torch.tensor(cu_k, dtype=torch.int32, device="cuda:0")
+    assert A.attn_varlen_validate_seqlens(cq, ck, tq, tk, mq, mk) == bits
+
+
+def test_validate_env_raises_before_launch(monkeypatch):
+    wl = W.Workload("validate-env", [40, 24], 2, 1, 64, True)
+    d = to_dev(W.make_inputs(wl, with_dout=False))
+    monkeypatch.setenv("ATTN_VARLEN_VALIDATE", "1")
+    announce("validate env")
+    out = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], 40, 40)  # valid: runs
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):  # max_seqlen_q understated: rejected before any kernel runs
+        A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], 30, 40)
+    assert out.shape == d["q"].shape
