@@ -620,15 +620,6 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
 // launchers
 // ---------------------------------------------------------------------------
 
-template <typename K>
-static hipError_t set_lds_limit(K kern, size_t bytes, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 template <int D>
 static hipError_t launch_prep(const BwdArgs& a, float* delta, float* lse2) {
   const FwdArgs& f = a.f;
@@ -681,8 +672,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   if (f.total_q > 0) {
     using T = DqCfg<D>;
     auto kern = bwd_dq_kernel<D, BAND>;
-    static bool done = false;
-    hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     BwdParams pq = p;
     pq.levels = ceil_div(f.max_q, T::BM);
@@ -698,8 +689,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   if (f.total_k > 0) {
     using T = DkdvCfg<D>;
     auto kern = bwd_dkdv_kernel<D, BAND>;
-    static bool done = false;
-    hipError_t e = set_lds_limit(kern, T::LDS_BYTES, done);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     BwdParams pk = p;
     pk.levels = ceil_div(f.max_k, T::BNK);

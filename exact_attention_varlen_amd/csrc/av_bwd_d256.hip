@@ -608,15 +608,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   }
 }
 
-template <typename K>
-hipError_t set_lds_limit256(K kern, size_t bytes, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done = true;
-  return e;
-}
-
 template <bool BAND>
 hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
   const FwdArgs& f = a.f;
@@ -652,8 +643,8 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   if (f.total_k > 0) {
     using T = Dkdv256;
     auto kern = bwd_dkdv256_kernel<BAND>;
-    static bool done = false;
-    hipError_t e = set_lds_limit256(kern, T::LDS_BYTES, done);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     BwdParams pk = p;
     pk.levels = ceil_div(f.max_k, T::BNK);
@@ -680,8 +671,8 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   if (f.total_q > 0) {
     using T = Dq256;
     auto kern = bwd_dq256_kernel<BAND>;
-    static bool done = false;
-    hipError_t e = set_lds_limit256(kern, T::LDS_BYTES, done);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     BwdParams pq = p;
     pq.levels = ceil_div(f.max_q, T::BM);

@@ -13,12 +13,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   constexpr int BM = FwdBlock<D>::BM, BN = FwdBlock<D>::BN;
   using T = FwdCfg<D, BM, BN>;
   auto kern = fwd_kernel<D, BM, BN, MODE, WRITE_LSE>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   FwdParams p = fwd_params(a, T::BM);
   const int r = a.Hq / a.Hkv;

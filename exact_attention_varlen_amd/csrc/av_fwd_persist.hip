@@ -15,12 +15,10 @@ static hipError_t launch_persist_t(const FwdArgs& a, unsigned int* sched) {
   using T = FwdCfg<D, BM, BN>;
   auto kern = fwd_kernel_persistent<D, BM, BN, MODE, WRITE_LSE>;
   constexpr size_t lds = T::LDS_BYTES + 16;  // K / V buffers, then the item slot
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = lds_limit_once(kern, lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   FwdParams p = fwd_params(a, T::BM);
   p.sched = sched;

@@ -4,6 +4,8 @@
 #define AV_LAUNCH_H
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -31,6 +33,21 @@ struct FwdArgs {
   float* lse;
   void* stream;
 };
+
+// Raise a kernel's dynamic LDS limit on the current device, once per device
+// (the attribute belongs to the device's copy of the kernel); `done` holds one
+// bit per device ordinal.
+template <typename K>
+inline hipError_t lds_limit_once(K kern, size_t bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Visible band of a query row i: keys i + (Lk - Lq) - wl .. i + (Lk - Lq) + wr,
 // a negative bound meaning unbounded; causal attention caps wr at 0. `band` is
