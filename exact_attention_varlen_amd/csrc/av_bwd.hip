@@ -237,8 +237,8 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
     }
   };
 
-  load_rows(0, 0);
-  load_rows(0, 1);
+#pragma unroll
+  for (int kk = 0; kk < PF; ++kk) load_rows(0, kk);
   load_rowvals(0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
