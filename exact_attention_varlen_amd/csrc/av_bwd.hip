@@ -518,15 +518,18 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int q0 = mblk * T::BM;
+  // query blocks aligned to the end of the sequence, as in the forward: a
+  // partial block is the first one (the fewest visible keys under a causal mask)
+  const int q0 = Lq - (ceil_div(Lq, T::BM) - mblk) * T::BM;
   const int qi = q0 + wave * 32 + col;
-  const bool qvalid = qi < Lq;
+  const bool qvalid = qi >= 0 && qi < Lq;
+  const int qa = qvalid ? qi : 0;  // a valid row for address arithmetic
 
   // key tiles [t_lo, t_hi); the unmasked ones [f_lo, f_hi) lie between masked
   // ones (the band's left edge before, its right edge and the sequence end after)
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
+    const KeyRange kr = block_keys(max(q0, 0), min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
     t_lo = kr.lo / T::BN;
     t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
     f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
 
   bf16x8 qf[D / 16], df[D / 16];
   {
-    const int64_t off = ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * half;
+    const int64_t off = ((int64_t)(cq + qa) * p.Hq + h) * D + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qf[kk] = as_bf16x8(qvalid ? ld16(p.q + off + 16 * kk) : zero_u4());
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   // is exactly 0. Written for the dK / dV kernel, which runs after this one.
   float dlt, lse2;
   {
-    const int64_t off = ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * half;
+    const int64_t off = ((int64_t)(cq + qa) * p.Hq + h) * D + 8 * half;
     float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -568,7 +571,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
     }
     dlt = part + __shfl_xor(part, 32);
   }
-  const int64_t lidx = (int64_t)h * p.total_q + cq + qi;
+  const int64_t lidx = (int64_t)h * p.total_q + cq + qa;
   {
     const float l = qvalid ? p.lse[lidx] : -INFINITY;
     lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;

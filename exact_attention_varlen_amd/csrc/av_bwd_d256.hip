@@ -537,14 +537,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int q0 = mblk * T::BM;
+  // query blocks aligned to the end of the sequence, as in the forward
+  const int q0 = Lq - (ceil_div(Lq, T::BM) - mblk) * T::BM;
   const int qi = q0 + wave * 32 + col;
-  const bool qvalid = qi < Lq;
+  const bool qvalid = qi >= 0 && qi < Lq;
+  const int qa = qvalid ? qi : 0;  // a valid row for address arithmetic
 
   // key tiles [t_lo, t_hi), the unmasked ones [f_lo, f_hi)
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
+    const KeyRange kr = block_keys(max(q0, 0), min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
     t_lo = kr.lo / T::BN;
     t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
     f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
@@ -562,14 +564,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
 
   bf16x8 qf[kKK], df[kKK];
   {
-    const int64_t off = ((int64_t)(cq + qi) * p.Hq + h) * kD + 8 * half;
+    const int64_t off = ((int64_t)(cq + qa) * p.Hq + h) * kD + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
       qf[kk] = as_bf16x8(qvalid ? ld16(p.q + off + 16 * kk) : zero_u4());
       df[kk] = as_bf16x8(qvalid ? ld16(p.dout + off + 16 * kk) : zero_u4());
     }
   }
-  const int64_t lidx = (int64_t)h * p.total_q + cq + qi;
+  const int64_t lidx = (int64_t)h * p.total_q + cq + qa;
   const float lse2 = qvalid ? p.lse2[lidx] : INFINITY;
   const float dlt = qvalid ? p.delta[lidx] : 0.f;
   OperandOffsets<kD> off;

@@ -473,16 +473,19 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   x.half = lane >> 5;
-  const int q0 = mblk * T::BM;
+  // query blocks are aligned to the end of the sequence: block mblk holds rows
+  // [Lq - (nblk - mblk) BM, ...), so a partial block (rows below 0 unused) is
+  // the first one, which under a causal mask sees the fewest keys
+  const int q0 = Lq - (ceil_div(Lq, T::BM) - mblk) * T::BM;
   const int qi = q0 + x.wave * 32 + (lane & 31);  // this lane's query row (sequence-relative)
-  const bool qvalid = qi < Lq;
+  const bool qvalid = qi >= 0 && qi < Lq;
 
   // key tiles of this block, [t_lo, t_hi), and the unmasked ones among them,
   // [f_lo, f_hi): every key below Lk and inside every row's band
   constexpr bool BAND = MODE > 0;
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const KeyRange kr = block_keys(q0, min(q0 + T::BM, Lq) - 1, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
+    const KeyRange kr = block_keys(max(q0, 0), min(q0 + T::BM, Lq) - 1, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
     t_lo = kr.lo / T::BN;
     t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
     f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
@@ -554,7 +557,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   {
     // Q^T operand: 8 consecutive head-dims of this lane's query per k-step
     // (sign-flipped when the scale is negative, so the scale applied is positive)
-    const uint16_t* qrow = p.q + ((int64_t)(cq + qi) * p.Hq + h) * D + 8 * x.half;
+    const uint16_t* qrow = p.q + ((int64_t)(cq + (qvalid ? qi : 0)) * p.Hq + h) * D + 8 * x.half;
     const uint32_t flip = p.neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
