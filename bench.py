@@ -385,6 +385,15 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         flop_done += 3.5 * 4.0 * L * L * wl.head_dim * (0.5 if wl.causal else 1.0)
         h_done += 1
     sample_desc = f"sequence 0 ({L} tokens), {h_done} of {wl.n_q_heads} query heads, forward+backward"
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {
         "value": flop_done / spent / 1e12,
         "unit": "TFLOP/s",
@@ -392,6 +401,9 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         "kind": "oracle",
         "sample": sample_desc,
         "seconds": spent,
+        "cpu_model": cpu_model,
+        "host_cpus_visible": len(os.sched_getaffinity(0)),
+        "blas_threads": int(threads),
     }
 
 
