@@ -518,9 +518,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  // query blocks aligned to the end of the sequence, as in the forward: a
-  // partial block is the first one (the fewest visible keys under a causal mask)
-  const int q0 = Lq - (ceil_div(Lq, T::BM) - mblk) * T::BM;
+  // query blocks aligned toward the end of the sequence, as in the forward
+  const int q0 = mblk * T::BM - query_lead(Lq, T::BM, T::BN);
   const int qi = q0 + wave * 32 + col;
   const bool qvalid = qi >= 0 && qi < Lq;
   const int qa = qvalid ? qi : 0;  // a valid row for address arithmetic

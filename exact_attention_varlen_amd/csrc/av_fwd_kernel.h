@@ -473,10 +473,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   x.half = lane >> 5;
-  // query blocks are aligned to the end of the sequence: block mblk holds rows
-  // [Lq - (nblk - mblk) BM, ...), so a partial block (rows below 0 unused) is
-  // the first one, which under a causal mask sees the fewest keys
-  const int q0 = Lq - (ceil_div(Lq, T::BM) - mblk) * T::BM;
+  // query blocks are aligned toward the end of the sequence: the first block
+  // starts `lead` rows before row 0 (the padding of the last block rounded
+  // down to whole key tiles), so that a partial block is mostly the first one,
+  // which under a causal mask sees the fewest keys, while block starts stay on
+  // the key-tile grid (a block's causal diagonal then crosses BM / BN tiles)
+  const int q0 = mblk * T::BM - query_lead(Lq, T::BM, T::BN);
   const int qi = q0 + x.wave * 32 + (lane & 31);  // this lane's query row (sequence-relative)
   const bool qvalid = qi >= 0 && qi < Lq;
 

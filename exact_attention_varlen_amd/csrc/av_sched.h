@@ -52,6 +52,15 @@ AV_HD inline int64_t grid_for(int64_t total_q, int num_seqs, int bm, int heads, 
   return ((n + group - 1) / group) * group;
 }
 
+// Rows by which the first query block of a sequence starts before row 0: the
+// padding of ceil(Lq / bm) blocks of bm rows, rounded down to whole key tiles
+// of bn rows. Blocks start at mblk bm - lead; there are still ceil(Lq / bm) of
+// them, and the last one overhangs the sequence by less than bn rows.
+AV_HD inline int query_lead(int Lq, int bm, int bn) {
+  const int pad = (Lq + bm - 1) / bm * bm - Lq;
+  return pad / bn * bn;
+}
+
 // Visible keys of a query row, as a band around the bottom-right-aligned
 // diagonal (FlashAttention repository guide, Public API: causal,
 // window_size_left / window_size_right). Key j is visible to query i when
