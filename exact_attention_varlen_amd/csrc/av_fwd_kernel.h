@@ -51,6 +51,8 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "av_common.h"
 #include "av_launch.h"
 #include "av_tiles.h"
@@ -437,13 +439,33 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n
 // MODE 0: full attention; 1: the visible keys of a row end at a band edge
 // (causal and / or a right window bound); 2: they also start at one (a left
 // window bound), so an item may begin with masked tiles.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// The lane index, formed where it is written: a volatile asm statement is not
+// hoisted out of a loop, so no register holds the lane index across it.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // SPLIT: the workgroup runs one chunk of the item's key tiles and writes the
 // chunk's partial result (FwdParams::part_o / part_l) instead of out / lse.
 //
 // One work item: logical index L = (query block rank, key chunk) x query head,
 // heads innermost, so that the r heads of a KV group are adjacent indices.
-template <int D, int BM, int BN, int MODE, bool WRITE_LSE, bool SPLIT>
-__device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t* smem) {
+// hook() runs exactly once per call, on every path: right after the
+// prologue's wait for all of the item's loads (or, for an item without key
+// tiles, in place of it). The persistent kernel publishes its next item there,
+// from an atomic issued before the call, which by then has completed.
+// With a hook, `wave` is this wave's index in the workgroup (wave-uniform) and
+// the thread index is formed from it and the lane, so that no thread-index
+// register stays live across the persistent kernel's loop.
+template <int D, int BM, int BN, int MODE, bool WRITE_LSE, bool SPLIT, class Hook = NoHook>
+__device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t* smem, const Hook& hook = Hook(),
+                                         int wave = 0) {
   using T = FwdCfg<D, BM, BN>;
   constexpr int NA = T::NA;
 
@@ -458,7 +480,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
     rank = (int)(L / p.Hq);
   }
   int b, mblk;
-  if (!decode_rank(p.cu_q, p.num_seqs, T::BM, p.levels, rank, b, mblk)) return;
+  if (!decode_rank(p.cu_q, p.num_seqs, T::BM, p.levels, rank, b, mblk)) {
+    hook();
+    return;
+  }
   const int g = h / r;
 
   const int cq = p.cu_q[b];
@@ -469,7 +494,15 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   FwdCtx<D, BM, BN, MODE> x;
   x.lds = (const lds_char*)smem;
   x.lds0 = lds_addr((lds_char*)smem);
-  const int tid = threadIdx.x;
+  // In the persistent kernel's loop the thread index is made opaque, so that
+  // the lane-derived values below are formed per item instead of being
+  // hoisted out of the loop and held in registers through the hot loop.
+  int tid;
+  if constexpr (std::is_same<Hook, NoHook>::value) {
+    tid = threadIdx.x;
+  } else {
+    tid = wave * 64 + lane_id_here();
+  }
   x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   x.half = lane >> 5;
@@ -506,6 +539,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
         p.part_l[li] = -INFINITY;
         p.part_l[li + (int64_t)p.Hq * p.total_q] = -INFINITY;
       }
+      hook();
       return;
     }
   }
@@ -584,6 +618,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
 
   if (ntot > 0) {
     wait_vmcnt<0>();
+    hook();
     lds_barrier();
     qk_tile(x, x.lds, sa);
     if (MODE == 2 || nm <= 0) {
@@ -592,6 +627,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
     }
 #pragma unroll
     for (int a = 0; a < NA; ++a) mx = max16(sa[a], mx);
+  } else {
+    hook();
   }
 
   // S(n) lives in sa for even local index t = n - t_lo, sb for odd t; steps
@@ -679,38 +716,68 @@ __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BL
 // the same clock) take more of the work, which a fixed block-to-XCD assignment
 // cannot do. Every workgroup leaves the loop once all queues are exhausted;
 // the last one to finish returns the counters to 0 for the next call.
+// The kernel's FwdParams argument, in the kernel-argument segment (its first bytes).
+typedef const __attribute__((address_space(4))) FwdParams* KernargParams;
+
 template <int D, int BM, int BN, int MODE, bool WRITE_LSE>
 __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void
 fwd_kernel_persistent(FwdParams p, unsigned int n_items) {
   using T = FwdCfg<D, BM, BN>;
   extern __shared__ __align__(16) uint16_t smem[];
-  volatile int* slot = reinterpret_cast<volatile int*>(reinterpret_cast<char*>(smem) + T::LDS_BYTES);
+  // LDS after the K / V buffers: the current and the next item (alternating),
+  // then thread 0's count of queues found empty so far
+  // (plain LDS accesses: the barriers order them)
+  int* slot = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + T::LDS_BYTES);
   const unsigned int r = (unsigned int)(p.Hq / p.Hkv);
   const unsigned int per_queue = n_items / kNumXcd;  // items per queue (whole groups)
+  // thread 0, tested without keeping the thread index live across the loop
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto first = [&]() { return wave == 0 && lane_id_here() == 0; };
   unsigned int xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
-  unsigned int k = 0;  // queues found empty so far (meaningful in thread 0)
-  for (;;) {
-    __syncthreads();  // every wave is done with the previous item's LDS and slot
-    if (threadIdx.x == 0) {
-      int L = -1;
-      while (k < (unsigned int)kNumXcd) {
-        const unsigned int q = (xcc + k) % kNumXcd;
-        const unsigned int idx = atomicAdd(p.sched + q, 1u);
-        if (idx < per_queue) {
-          L = (int)(((idx / r) * kNumXcd + q) * r + idx % r);
-          break;
-        }
-        ++k;
-      }
-      *slot = L;
+  // Thread 0: the item behind ticket idx of queue (xcc + k) % 8, else the next
+  // queues in turn (a ticket past the end of a queue is discarded); -1 once
+  // every queue is empty. Returns the queues found empty in k.
+  // (Only lane 0 of wave 0 runs it: readfirstlane keeps the division scalar.)
+  auto resolve = [&](unsigned int idx, unsigned int& k) -> int {
+    while (k < (unsigned int)kNumXcd) {
+      const unsigned int q = (xcc + k) % kNumXcd;
+      const unsigned int i = __builtin_amdgcn_readfirstlane(idx);
+      if (i < per_queue) return (int)(((i / r) * kNumXcd + q) * r + i % r);
+      if (++k < (unsigned int)kNumXcd) idx = atomicAdd(p.sched + (xcc + k) % kNumXcd, 1u);
     }
-    __syncthreads();
-    const int L = __builtin_amdgcn_readfirstlane(*slot);  // the same in every lane
-    if (L < 0) break;
-    fwd_item<D, BM, BN, MODE, WRITE_LSE, false>(p, L, smem);
+    return -1;
+  };
+  if (first()) {
+    unsigned int k = 0;
+    slot[0] = resolve(atomicAdd(p.sched + xcc % kNumXcd, 1u), k);
+    slot[2] = (int)k;
   }
-  if (threadIdx.x == 0) {
+  __syncthreads();
+  for (int cur = 0;; cur ^= 1) {
+    const int L = __builtin_amdgcn_readfirstlane(slot[cur]);  // the same in every lane
+    if (L < 0) break;
+    // claim the next item now; fwd_item's first wait completes the atomic, and
+    // the hook publishes the item for the loop's next turn
+    unsigned int ticket = 0;
+    if (first() && slot[2] < kNumXcd) ticket = atomicAdd(p.sched + (xcc + slot[2]) % kNumXcd, 1u);
+    auto publish = [&]() {
+      if (first()) {
+        unsigned int k = (unsigned int)slot[2];
+        slot[cur ^ 1] = resolve(ticket, k);
+        slot[2] = (int)k;
+      }
+    };
+    // The item reads the parameters through a pointer the compiler cannot see
+    // through, so that it loads them inside the item, as the one-item kernel
+    // does, instead of holding all of them in scalar registers across the loop
+    // (which spills the hot loop).
+    KernargParams pi = (KernargParams)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pi));
+    fwd_item<D, BM, BN, MODE, WRITE_LSE, false>(*(const FwdParams*)pi, L, smem, publish, wave);
+    __syncthreads();  // the next item is published; every wave is done with this item's LDS
+  }
+  if (first()) {
     __threadfence();
     if (atomicAdd(p.sched + kNumXcd, 1u) == gridDim.x - 1) {
       for (int q = 0; q <= kNumXcd; ++q) atomicExch(p.sched + q, 0u);

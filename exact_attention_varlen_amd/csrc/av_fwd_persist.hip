@@ -14,7 +14,7 @@ static hipError_t launch_persist_t(const FwdArgs& a, unsigned int* sched) {
   constexpr int BM = FwdBlock<D>::BM, BN = FwdBlock<D>::BN;
   using T = FwdCfg<D, BM, BN>;
   auto kern = fwd_kernel_persistent<D, BM, BN, MODE, WRITE_LSE>;
-  constexpr size_t lds = T::LDS_BYTES + 16;  // K / V buffers, then the item slot
+  constexpr size_t lds = T::LDS_BYTES + 16;  // K / V buffers, then two item slots and a queue cursor
   static std::atomic<uint64_t> lds_set{0};
   {
     const hipError_t e = lds_limit_once(kern, lds, lds_set);
