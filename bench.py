@@ -178,6 +178,29 @@ def read_clocks():
     return {"power_w": float(power[0]) if power else None, "gfx_mhz": clks}
 
 
+def gemm_reference(n: int = 8192, reps: int = 20):
+    """Rate of a plain square bf16 GEMM (torch.mm, i.e. the vendor GEMM library)
+    on this board, back to back after a warm-up: context for the attention
+    kernels' fraction of the published MFMA peak, which the board's power limit
+    keeps out of reach of any kernel."""
+    import torch
+
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.mm(a, b, out=c)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        torch.mm(a, b, out=c)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"op": f"torch.mm bf16 {n}x{n}x{n}", "ms_median": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+
+
 def power_phase(fn, seconds: float = 4.0):
     """Run fn back to back for `seconds` and sample clocks / power from a side
     thread in the second half: the sustained operating point of this work."""
@@ -352,12 +375,7 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     import oracle.attention as O
     import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads, cpu_model = _host_cpu()
     inp = W.make_inputs(wl)
     q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
     cu = wl.cu_seqlens_q
@@ -385,15 +403,6 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         flop_done += 3.5 * 4.0 * L * L * wl.head_dim * (0.5 if wl.causal else 1.0)
         h_done += 1
     sample_desc = f"sequence 0 ({L} tokens), {h_done} of {wl.n_q_heads} query heads, forward+backward"
-    cpu_model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:  # pragma: no cover
-        pass
     return {
         "value": flop_done / spent / 1e12,
         "unit": "TFLOP/s",
@@ -559,6 +568,86 @@ def persistent_vs_grid(wl, rounds: int = 3):
             "persistent_tflops": fl / (p * 1e-3) / 1e12, "persistent_speedup": g / p}
 
 
+def _host_cpu():
+    """(BLAS threads, CPU model) of this host, for the oracle's timing lines."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return int(threads), cpu_model
+
+
+def oracle_table(budget_s: float = 4.0, max_sample_len: int = 8192, whole_flop: float = 2e10):
+    """Wall-clock of the float64 oracle, forward and forward+backward, for every
+    config: one JSON object per config on stdout. A config whose whole oracle
+    run fits the budget is timed whole ("measured"). Otherwise the sample is the
+    first sequence (cut to its first max_sample_len tokens), one query head with
+    its KV head at a time, heads added until the budget is spent; the full time
+    is the config's accounted work divided by the sample's rate ("extrapolated")."""
+    import oracle.attention as O
+    import workloads as W
+
+    threads, cpu_model = _host_cpu()
+    warm = W.make_inputs(W.tiny(True))  # first BLAS calls start the thread pool: untimed
+    O.forward(*(W.to_f64(warm[x]) for x in ("q", "k", "v")), W.tiny(True).cu_seqlens_q, W.tiny(True).cu_seqlens_k,
+              0.125, True)
+    for wl in W.all_configs() + [W.single_16k_full()]:
+        log(f"oracle timing {wl.name}")
+        inp = W.make_inputs(wl)
+        fl = wl.accounted_fwd_flop()
+        whole = 3.5 * fl < whole_flop  # by default a few seconds of fp64 BLAS on a multi-core host
+        if whole:
+            q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
+            t0 = time.perf_counter()
+            O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal)
+            t_f = time.perf_counter() - t0
+            O.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do)
+            t_b = time.perf_counter() - t0 - t_f
+            row = {"config": wl.name, "kind": "measured", "sample": "whole config", "oracle_fwd_s": t_f,
+                   "oracle_fwdbwd_s": t_f + t_b}
+        else:
+            L = min(wl.seqlens_q[0], max_sample_len)
+            r = wl.n_q_heads // wl.n_kv_heads
+            sample_fl, t_f, t_b, heads = 0.0, 0.0, 0.0, 0
+            while heads < wl.n_q_heads and (heads == 0 or t_f + t_b < budget_s):
+                h, g = heads, heads // r
+                qs = W.to_f64(inp["q"][:L, h:h + 1])
+                ks = W.to_f64(inp["k"][:L, g:g + 1])
+                vs = W.to_f64(inp["v"][:L, g:g + 1])
+                dos = W.to_f64(inp["dout"][:L, h:h + 1])
+                t0 = time.perf_counter()
+                O.forward(qs, ks, vs, [0, L], [0, L], wl.softmax_scale, wl.causal)
+                t1 = time.perf_counter()
+                O.backward(qs, ks, vs, [0, L], [0, L], wl.softmax_scale, wl.causal, dos)
+                t_f += t1 - t0
+                t_b += time.perf_counter() - t1
+                sample_fl += 4.0 * L * L * wl.head_dim * (0.5 if wl.causal else 1.0)
+                heads += 1
+            row = {"config": wl.name, "kind": "extrapolated",
+                   "sample": f"sequence 0 cut to {L} tokens, {heads} of {wl.n_q_heads} query heads",
+                   "sample_fwd_s": t_f, "sample_fwdbwd_s": t_f + t_b,
+                   "oracle_fwd_s": fl * t_f / sample_fl, "oracle_fwdbwd_s": fl * (t_f + t_b) / sample_fl}
+        row.update({"accounted_fwd_gflop": fl / 1e9,
+                    "oracle_fwd_gflops": fl / row["oracle_fwd_s"] / 1e9,
+                    "oracle_fwdbwd_gflops": 3.5 * fl / row["oracle_fwdbwd_s"] / 1e9,
+                    "threads": threads, "cpu_model": cpu_model,
+                    "host_cpus_visible": len(os.sched_getaffinity(0))})
+        print(json.dumps(row), flush=True)
+        del inp
+    return 0
+
+
 def all_configs_table(include_long: bool):
     """Forward and forward+backward time of every config (fwd with LSE; steady
     state, several calls per HIP graph): one JSON object per config on stdout."""
@@ -617,6 +706,9 @@ def main(argv=None):
     ap.add_argument("--long", action="store_true", help="with --all-configs: include the 64K and 128K sequences")
     ap.add_argument("--window-split", action="store_true",
                     help="only time the local-window and split-KV workloads (one JSON line) and exit")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="only time the float64 oracle (forward, forward+backward) for every config, whole or on a "
+                         "bounded sample with an extrapolated full time (one JSON line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
@@ -628,6 +720,8 @@ def main(argv=None):
 
     import workloads as W
 
+    if a.oracle_table:  # CPU only
+        return oracle_table()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
@@ -665,6 +759,8 @@ def main(argv=None):
         secondary["persistent_scheduler"] = persistent_vs_grid(primary)
     log("sustained clocks and power of the primary step")
     clocks = power_phase(res.pop("_step_fn"))
+    log("reference GEMM rate")
+    gemm = gemm_reference()
     # dominant kernel of the step: the one with the largest total time
     kern = res["kernels"]
     dom = max(kern, key=lambda k: kern[k]["avg_ms"]) if kern else "attn_fwd"
@@ -681,6 +777,7 @@ def main(argv=None):
         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
         "avg_ms": dom_ms,
         "flop_per_launch": flop,
+        "achieved_vs_gemm_reference": flop / (dom_ms * 1e-3) / 1e12 / gemm["tflops"],
     }
     for k, v in kern.items():
         f = kernel_flop(k, primary)
@@ -717,6 +814,7 @@ def main(argv=None):
         "timing": "HIP graph replay per step (value); per-kernel times from eager steps with library events",
         "kernels": kern,
         "roofline": roofline,
+        "gemm_reference": gemm,
         "secondary": secondary,
         "context_other_hardware": context_other_hardware(secondary),
     }
