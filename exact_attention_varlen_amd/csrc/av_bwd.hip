@@ -142,6 +142,25 @@ __device__ __forceinline__ void wait_qdo_stage(int wave) {
     wait_vmcnt<T::DMA_PER_WAVE>();
 }
 
+// S / dP products of the dK / dV kernel, written as asm so that their
+// accumulators are VGPRs, which the VALU reads next, and the K / V operand is an
+// AGPR. (At one wave per SIMD the compiler gives every MFMA an AGPR result, and
+// each score then costs a v_accvgpr_read before the VALU can use it.) The asm is
+// opaque to the compiler's hazard checks: s_fence_scores() gives the results the
+// wait states they need before any VALU instruction reads them, and has them as
+// operands so that no read moves above it. The A operand comes from an LDS read
+// (the compiler's s_waitcnt covers it), the B operand from a global load at the
+// start of the item.
+__device__ __forceinline__ void mfma_score0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_score(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void s_fence_scores(f32x16& s, f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s), "+v"(d));
+}
+
 // Scheduling hints (instruction classes for __builtin_amdgcn_sched_group_barrier).
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -252,7 +271,10 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
       if (b < NB) {
         if (j == 0 && kk + PF < KK) load_rows(b, kk + PF);
         f32x16& acc = j ? dacc[b & 1] : sacc[b & 1];
-        acc = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk], kk ? acc : zero16());
+        if (kk == 0)
+          mfma_score0(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
+        else
+          mfma_score(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
       }
       if (b >= 1) b_share(b - 1, 1, u);
       // warm the ring of C(b - 1) and the lse2 / Delta of B(b, 0) in the last units
@@ -260,6 +282,7 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
       if (b < NB && u == NU - 1) load_rowvals(b, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (b < NB) s_fence_scores(sacc[b & 1], dacc[b & 1]);
     if (b >= 1) b_tail(b - 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     // ---- Y(b): C(b - 1), B(b, 0) ----
@@ -354,6 +377,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       kf[kk] = as_bf16x8(kvalid ? ld16(p.k + off + 16 * kk) : zero_u4());
       vf[kk] = as_bf16x8(kvalid ? ld16(p.v + off + 16 * kk) : zero_u4());
     }
+    // Consumed here, in AGPRs (the score MFMAs read them from there): the
+    // compiler then waits for these loads once, before the step loop. Left
+    // pending into the loop, its wait at their first use would also wait for
+    // the next stage's Q / dO copies, issued just before, in every step.
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
   }
   OperandOffsets<D> off;
   operand_offsets<D>(off, lane);

@@ -63,6 +63,15 @@ __device__ __forceinline__ void mfma_vgpr(f32x16& acc, const bf16x8& a, const bf
 __device__ __forceinline__ void mfma_vgpr0(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
+// Operand registers loaded from memory before a tile loop are consumed here, so
+// that the compiler waits for those loads once, before the loop. Left pending
+// into the loop, its wait at their first use there would also wait for the
+// tile copies issued just before it (the copies count in the same counter),
+// in every iteration.
+__device__ __forceinline__ void settle(bf16x8 (&r)[kKK]) {
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) asm volatile("" : "+v"(r[kk]));
+}
 __device__ __forceinline__ void vgpr_fence(f32x16& a, f32x16& b) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
 }
@@ -309,6 +318,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
     const int64_t off = ((int64_t)(ck + kj) * p.Hkv + g) * kD + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) kf[kk] = as_bf16x8(kvalid ? ld16(p.k + off + 16 * kk) : zero_u4());
+    settle(kf);
   }
   // addresses of this lane's V row (key wave * 32 + col of the block) in LDS
   uint32_t vrow[8];
@@ -571,9 +581,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
       df[kk] = as_bf16x8(qvalid ? ld16(p.dout + off + 16 * kk) : zero_u4());
     }
   }
+  settle(qf);
+  settle(df);
   const int64_t lidx = (int64_t)h * p.total_q + cq + qa;
-  const float lse2 = qvalid ? p.lse2[lidx] : INFINITY;
-  const float dlt = qvalid ? p.delta[lidx] : 0.f;
+  float lse2 = qvalid ? p.lse2[lidx] : INFINITY;
+  float dlt = qvalid ? p.delta[lidx] : 0.f;
+  asm volatile("" : "+v"(lse2), "+v"(dlt));
   OperandOffsets<kD> off;
   operand_offsets<kD>(off, lane);
 
