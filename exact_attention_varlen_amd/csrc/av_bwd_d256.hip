@@ -255,12 +255,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   const int rem = (int)(L % ((int64_t)p.Hkv * S));
   const int g = rem / S;
   const int split = rem % S;
-  int b, lvl;
-  if (!decode_rank(p.cu_k, p.num_seqs, T::BNK, p.levels, rank, b, lvl)) return;
-  const int cq = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - cq;
-  const int ck = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - ck;
+  Item item;
+  if (!decode_item<true>(p.cu_q, p.cu_k, p.num_seqs, T::BNK, p.levels, rank, item)) return;
+  const int lvl = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
   const int n0 = (ceil_div(Lk, T::BNK) - 1 - lvl) * T::BNK;
 
   const int tid = threadIdx.x;
@@ -534,13 +531,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   const int64_t L = xcd_logical(blockIdx.x, r);
   const int rank = (int)(L / p.Hq);
   const int h = (int)(L % p.Hq);
-  int b, mblk;
-  if (!decode_rank(p.cu_q, p.num_seqs, T::BM, p.levels, rank, b, mblk)) return;
+  Item item;
+  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, T::BM, p.levels, rank, item)) return;
   const int g = h / r;
-  const int cq = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - cq;
-  const int ck = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - ck;
+  const int mblk = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

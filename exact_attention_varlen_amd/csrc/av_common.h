@@ -248,12 +248,12 @@ __device__ __forceinline__ int highest_bit(uint64_t m) { return 63 - __builtin_c
 
 // Returns false when `rank` is past the last block. Must be called by all 64
 // lanes of a wave (the counts are evaluated with every lane active so that the
-// cross-lane reads see defined values).
-__device__ inline bool decode_rank(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int& b_out,
-                                   int& m_out) {
+// cross-lane reads see defined values). nb_lane is the block count of sequence
+// `lane` (of sequence `base + lane` for the first 64-sequence slice).
+__device__ inline bool decode_rank_nb(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int nb_lane,
+                                      int& b_out, int& m_out) {
   const int lane = threadIdx.x & (kWave - 1);
   if (levels <= 0) return false;
-  const int nb_lane = seq_blocks(cu, lane, num_seqs, bm);
   // pass 1: lane t probes k = t * stride
   const int stride = ceil_div(levels, kWave);
   const int k1 = lane * stride;
@@ -273,7 +273,7 @@ __device__ inline bool decode_rank(const int32_t* cu, int num_seqs, int bm, int 
   const int above = count_at_least(cu, num_seqs, bm, nb_lane, kstar + 1);
   int j = rank - __builtin_amdgcn_readfirstlane(above);
   for (int base = 0; base < num_seqs; base += kWave) {
-    const int nbc = seq_blocks(cu, base + lane, num_seqs, bm);
+    const int nbc = base == 0 ? nb_lane : seq_blocks(cu, base + lane, num_seqs, bm);
     const uint64_t sel = __ballot(nbc > kstar);
     const int pc = __popcll(sel);
     if (j < pc) {
@@ -287,6 +287,52 @@ __device__ inline bool decode_rank(const int32_t* cu, int num_seqs, int bm, int 
     j -= pc;
   }
   return false;
+}
+
+__device__ inline bool decode_rank(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int& b_out,
+                                   int& m_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  return decode_rank_nb(cu, num_seqs, bm, levels, rank, seq_blocks(cu, lane, num_seqs, bm), b_out, m_out);
+}
+
+// A decoded work item: sequence b, block m of its ranked rows, and the
+// sequence's query rows [cq, cq + Lq) and key rows [ck, ck + Lk).
+struct Item {
+  int b, m, cq, Lq, ck, Lk;
+};
+
+// decode_rank plus the chosen sequence's bounds, ranking blocks of bm query
+// rows, or of key rows with BY_KEYS. With up to 64 sequences every lane loads
+// its own sequence's four bounds at once, the decode works from them, and the
+// item's bounds are read from lane b: no memory round trip follows the decode.
+template <bool BY_KEYS>
+__device__ inline bool decode_item(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int bm, int levels,
+                                   int rank, Item& it) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t* cu = BY_KEYS ? cu_k : cu_q;
+  if (num_seqs <= kWave) {
+    int q0 = 0, q1 = 0, k0 = 0, k1 = 0;
+    if (lane < num_seqs) {
+      q0 = cu_q[lane];
+      q1 = cu_q[lane + 1];
+      k0 = cu_k[lane];
+      k1 = cu_k[lane + 1];
+    }
+    const int nb = ceil_div(BY_KEYS ? k1 - k0 : q1 - q0, bm);
+    if (!decode_rank_nb(cu, num_seqs, bm, levels, rank, nb, it.b, it.m)) return false;
+    const int b = __builtin_amdgcn_readfirstlane(it.b);
+    it.cq = __builtin_amdgcn_readlane(q0, b);
+    it.Lq = __builtin_amdgcn_readlane(q1, b) - it.cq;
+    it.ck = __builtin_amdgcn_readlane(k0, b);
+    it.Lk = __builtin_amdgcn_readlane(k1, b) - it.ck;
+    return true;
+  }
+  if (!decode_rank(cu, num_seqs, bm, levels, rank, it.b, it.m)) return false;
+  it.cq = cu_q[it.b];
+  it.Lq = cu_q[it.b + 1] - it.cq;
+  it.ck = cu_k[it.b];
+  it.Lk = cu_k[it.b + 1] - it.ck;
+  return true;
 }
 
 }  // namespace av

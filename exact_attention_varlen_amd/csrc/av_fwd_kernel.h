@@ -170,7 +170,13 @@ struct FwdCtx {
   uint32_t lds0;
   i32x4 rk, rv;          // K / V rows of this (sequence, KV head), from key 0
   uint32_t tile_bytes;   // BN rows of the K / V tensor
-  uint32_t voff[T::DMA]; // this lane's source offset within a tile, per copy
+  // This lane's source offset within a tile: per copy, or (ONE_VOFF) for the
+  // first copy only, the others being whole rounds of rows further on. The
+  // latter costs an add per copy but frees registers: it is used where the
+  // kernel would otherwise spill (a right band edge at head_dim 64 / 128).
+  static constexpr bool ONE_VOFF = D <= 128 && MODE == 1;
+  uint32_t voff[ONE_VOFF ? 1 : T::DMA];
+  uint32_t round_bytes;  // ONE_VOFF: rows copied by all waves' i-th copies
   int wave, half;
   int ntiles;            // one past the item's last tile
   int kvis_lo;           // first key visible to this lane's query row
@@ -180,13 +186,24 @@ struct FwdCtx {
   bf16x8 qf[T::KK];
 };
 
-// Copy this wave's share of a 64-row tile (rows row0 ..) into LDS at `dst`.
+// Copy this wave's share of a tile (rows row0 ..) into LDS at `dst`. With
+// ONE_VOFF, copy i of wave w is the tile's copy i * WAVES + w: at head_dim 64
+// and 128 the chunk swizzle of its rows is then the same for every i, so the
+// source offsets of a lane differ by whole rounds of rows, added here (behind an
+// empty asm statement, so that the sums are not hoisted and held in registers).
 template <int D, int BM, int BN, int MODE>
 __device__ __forceinline__ void issue_tile(const FwdCtx<D, BM, BN, MODE>& x, uint32_t dst, const i32x4& rsrc, int row0) {
   using T = FwdCfg<D, BM, BN>;
   const i32x4 r = rsrc_advance(rsrc, (uint32_t)row0 * (x.tile_bytes / T::BN));
+  if constexpr (FwdCtx<D, BM, BN, MODE>::ONE_VOFF) {
+    uint32_t v = x.voff[0];
+    asm volatile("" : "+v"(v));
 #pragma unroll
-  for (int i = 0; i < T::DMA; ++i) lds_dma16(r, dst + (x.wave * T::DMA + i) * 1024, x.voff[i]);
+    for (int i = 0; i < T::DMA; ++i) lds_dma16(r, dst + (i * T::WAVES + x.wave) * 1024, v + i * x.round_bytes);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::DMA; ++i) lds_dma16(r, dst + (x.wave * T::DMA + i) * 1024, x.voff[i]);
+  }
 }
 
 // Score register v of accumulator a (a = 0: keys 0..31 of the tile, a = 1:
@@ -479,17 +496,13 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   } else {
     rank = (int)(L / p.Hq);
   }
-  int b, mblk;
-  if (!decode_rank(p.cu_q, p.num_seqs, T::BM, p.levels, rank, b, mblk)) {
+  Item item;
+  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, T::BM, p.levels, rank, item)) {
     hook();
     return;
   }
   const int g = h / r;
-
-  const int cq = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - cq;
-  const int ck = p.cu_k[b];
-  const int Lk = p.cu_k[b + 1] - ck;
+  const int mblk = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
 
   FwdCtx<D, BM, BN, MODE> x;
   x.lds = (const lds_char*)smem;
@@ -576,11 +589,19 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   const int64_t kvoff = ((int64_t)ck * p.Hkv + g) * D;
   x.rk = head_rows_rsrc<D>(p.k + kvoff, Lk, pitch);
   x.rv = head_rows_rsrc<D>(p.v + kvoff, Lk, pitch);
+  if constexpr (FwdCtx<D, BM, BN, MODE>::ONE_VOFF) {
+    static_assert(T::WAVES % 4 == 0 && (T::KV::ROWS_PER_DMA * T::WAVES) % 16 == 0,
+                  "the rows of a wave's copies must share one chunk swizzle");
+    const int row = x.wave * T::KV::ROWS_PER_DMA + lane / T::KV::CPR;
+    x.voff[0] = (uint32_t)row * pitch + (uint32_t)(((lane % T::KV::CPR) ^ swz<D>(row)) * 16);
+    x.round_bytes = (uint32_t)(T::KV::ROWS_PER_DMA * T::WAVES) * pitch;
+  } else {
 #pragma unroll
-  for (int i = 0; i < T::DMA; ++i) {
-    const int row = (x.wave * T::DMA + i) * T::KV::ROWS_PER_DMA + lane / T::KV::CPR;
-    const int cidx = (lane % T::KV::CPR) ^ swz<D>(row);
-    x.voff[i] = (uint32_t)row * pitch + (uint32_t)cidx * 16u;
+    for (int i = 0; i < T::DMA; ++i) {
+      const int row = (x.wave * T::DMA + i) * T::KV::ROWS_PER_DMA + lane / T::KV::CPR;
+      const int cidx = (lane % T::KV::CPR) ^ swz<D>(row);
+      x.voff[i] = (uint32_t)row * pitch + (uint32_t)cidx * 16u;
+    }
   }
 
   // prologue copies: K(t_lo) -> K0, V(t_lo) -> V0, K(t_lo + 1) -> K1; then Q^T

@@ -67,6 +67,26 @@ def test_parity_small(wl):
     full_parity(wl)
 
 
+# more sequences than a wave has lanes: the work-item decode then leaves its
+# one-load-per-lane path (up to 64 sequences) for the general one. Ragged
+# lengths including empty sequences, Lq != Lk, every head dim, both masks.
+def _many_lengths(n, seed):
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(0, 160, size=n)], [int(x) for x in rng.integers(0, 160, size=n)]
+
+
+MANY_SEQS = []
+for n, D, causal, seed in ((64, 128, True, 1), (65, 64, False, 2), (65, 128, True, 3), (150, 256, True, 4),
+                           (150, 128, False, 5)):
+    lq, lk = _many_lengths(n, seed)
+    MANY_SEQS.append(W.Workload(f"many{n}-d{D}-{'c' if causal else 'f'}", lq, 4, 2, D, causal, seqlens_k=lk))
+
+
+@pytest.mark.parametrize("wl", MANY_SEQS, ids=[w.name for w in MANY_SEQS])
+def test_parity_many_sequences(wl):
+    full_parity(wl)
+
+
 # local (sliding-window) attention: band (left, right) around the bottom-right
 # diagonal; causal fixes right = 0. Windows narrower than a tile, wider than a
 # sequence, zero-width, one-sided, and bands that leave rows without a key.
