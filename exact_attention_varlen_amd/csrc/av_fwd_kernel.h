@@ -173,8 +173,8 @@ struct FwdCtx {
   // This lane's source offset within a tile: per copy, or (ONE_VOFF) for the
   // first copy only, the others being whole rounds of rows further on. The
   // latter costs an add per copy but frees registers: it is used where the
-  // kernel would otherwise spill (a right band edge at head_dim 64 / 128).
-  static constexpr bool ONE_VOFF = D <= 128 && MODE == 1;
+  // kernel would otherwise spill (banded masks at head_dim 64 / 128).
+  static constexpr bool ONE_VOFF = D <= 128 && MODE >= 1;
   uint32_t voff[ONE_VOFF ? 1 : T::DMA];
   uint32_t round_bytes;  // ONE_VOFF: rows copied by all waves' i-th copies
   int wave, half;
@@ -294,7 +294,8 @@ __device__ __forceinline__ void qk_tile(const FwdCtx<D, BM, BN, MODE>& x, const 
 //  PAR   buffer parity of n;
 //  MC    tile n is masked (its scores in sc already hold -inf where invisible);
 //  NX    1: tile n + 1 exists and is unmasked; -1: tile n + 1, if there is
-//        one, is masked (tiles treated as masked may well be full).
+//        one, is masked (tiles treated as masked may well be full); -2: tile
+//        n + 1 exists and is masked.
 // On entry sc holds S(n) and mx this lane's max over it; on return sn holds
 // S(n + 1) and mx its max (when tile n + 1 exists).
 template <int D, int BM, int BN, int MODE, int PAR, bool MC, int NX>
@@ -304,7 +305,7 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n
   using T = FwdCfg<D, BM, BN>;
   constexpr int KK = T::KK, PF = T::PF, DB = T::DB, NA = T::NA, NS = T::NS, NJ = T::NJ;
   constexpr int par = PAR;
-  const bool next = NX > 0 || n + 1 < x.ntiles;
+  const bool next = NX > 0 || NX == -2 || n + 1 < x.ntiles;
 
   // every wave is done with tile n - 1; V(n) and K(n + 1) have landed
   wait_vmcnt<0>();
@@ -556,6 +557,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
       return;
     }
   }
+  if (MODE == 2 || SPLIT) {  // see below
+    t_lo = __builtin_amdgcn_readfirstlane(t_lo);
+    t_hi = __builtin_amdgcn_readfirstlane(t_hi);
+    f_lo = __builtin_amdgcn_readfirstlane(f_lo);
+    f_hi = __builtin_amdgcn_readfirstlane(f_hi);
+  }
   x.ntiles = t_hi;
   x.kvis_lo = (MODE == 2) ? band_lo(qi, Lq, Lk, p.wl) : 0;
   x.kvis_end = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
@@ -580,6 +587,14 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
         nm = nme;
       }
     }
+  }
+  // The tile counts are the same in every lane; saying so keeps the loops'
+  // control in scalar registers where the compiler does not prove it (with a
+  // left band edge or split-KV chunks; vector loop bounds there cost registers
+  // the pipeline needs, and the kernels spilled).
+  if (MODE == 2 || SPLIT) {
+    nm = __builtin_amdgcn_readfirstlane(nm);
+    nh = __builtin_amdgcn_readfirstlane(nh);
   }
   x.c = p.scale_log2;
 
@@ -658,9 +673,10 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   if (nm > 0) {
     if (MODE == 2) {
       // left-edge tiles: each step masks the next tile's scores
+      // (nh < nm <= ntot: a next tile always exists here)
       for (; t < nh; t += 2) {
-        fwd_step<D, BM, BN, MODE, 0, false, -1>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
-        fwd_step<D, BM, BN, MODE, 1, false, -1>(x, t_lo + t + 1, sb, sa, o, m_ref, l_run, l_o, mx);
+        fwd_step<D, BM, BN, MODE, 0, false, -2>(x, t_lo + t, sa, sb, o, m_ref, l_run, l_o, mx);
+        fwd_step<D, BM, BN, MODE, 1, false, -2>(x, t_lo + t + 1, sb, sa, o, m_ref, l_run, l_o, mx);
       }
     }
     // steady state, unrolled by two so the buffer parity is a constant: tiles
