@@ -15,6 +15,7 @@ from parity import announce, check_grad, check_lse, check_out, f64, to_dev
 pytestmark = pytest.mark.gpu
 
 N_CASES = 48
+N_LONG = 16
 
 
 def random_case(seed: int):
@@ -43,11 +44,40 @@ def random_case(seed: int):
     return wl, splits, persistent, backward
 
 
+def random_long_case(seed: int):
+    """Fewer heads, longer sequences (up to 2000 tokens): many key blocks and
+    query steps per sequence, end-aligned query blocks, ragged tails."""
+    rng = np.random.default_rng(5000 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2]))
+    r = int(rng.choice([1, 2, 4]))
+    nseq = int(rng.integers(1, 4))
+    lq = [int(x) for x in rng.integers(300, 2001, size=nseq)]
+    same = rng.random() < 0.7
+    lk = list(lq) if same else [int(x) for x in rng.integers(1, 2001, size=nseq)]
+    causal = bool(rng.random() < 0.6)
+    window = None
+    if rng.random() < 0.3:
+        window = (int(rng.choice([-1, 100, 700])), int(rng.choice([-1, 0, 300])))
+    splits = int(rng.choice([1, 1, 1, 3]))
+    persistent = splits == 1 and rng.random() < 0.3
+    wl = W.Workload(f"long{seed}", lq, hkv * r, hkv, D, causal, seqlens_k=lk, seed=seed, window=window)
+    return wl, splits, persistent, True
+
+
 @pytest.mark.parametrize("seed", list(range(N_CASES)))
 def test_random_case(seed):
-    wl, splits, persistent, backward = random_case(seed)
+    _run_case(f"random seed={seed}", *random_case(seed))
+
+
+@pytest.mark.parametrize("seed", list(range(N_LONG)))
+def test_random_long_case(seed):
+    _run_case(f"random long seed={seed}", *random_long_case(seed))
+
+
+def _run_case(tag, wl, splits, persistent, backward):
     win = (-1, -1) if wl.window is None else wl.window
-    announce(f"random seed={seed} seqlens_q={wl.seqlens_q} seqlens_k={wl.seqlens_k} Hq={wl.n_q_heads} "
+    announce(f"{tag} seqlens_q={wl.seqlens_q} seqlens_k={wl.seqlens_k} Hq={wl.n_q_heads} "
              f"Hkv={wl.n_kv_heads} D={wl.head_dim} causal={wl.causal} window={wl.window} splits={splits} "
              f"persistent={persistent} scale={wl.softmax_scale:.4f} backward={backward}")
     inp = W.make_inputs(wl)
