@@ -182,7 +182,7 @@ constexpr int kSchedValu = 0x002;
 // unit also issues the LDS reads one or two units ahead: the next k-steps of
 // the Q / dO rows, the transposed operands of C (a ring of RV), and the rows'
 // lse2 / Delta of the next B part.
-template <int D, bool MASK>
+template <int D, bool MASK, bool LEFT>
 __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
                                           const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
                                           f32x16* dv, float c, int m0, int rlo, int rhi, const OperandOffsets<D>& off,
@@ -229,7 +229,7 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
     float pv = pe[e];
     if (MASK) {
       const int row = 32 * b + 16 * ks + 8 * half + e;
-      pv = (row >= rl && row <= rh) ? pv : 0.f;
+      pv = (row >= rl && (!LEFT || row <= rh)) ? pv : 0.f;
     }
     pm[e] = pv;
     dsv[e] = pv * (dacc[b & 1][8 * ks + e] - dl[ks][e]);
@@ -307,7 +307,9 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
 }
 
 // BAND: the visible keys of a row form a band (causal and / or a local window).
-template <int D, bool BAND>
+// LEFT: the band has a left bound (window_left >= 0). Without one, every row
+// past a key's first visible row sees it, and masked steps test that bound only.
+template <int D, bool BAND, bool LEFT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int m0 = (sfirst + st) * T::BMQ;
     const lds_char* stg = lds + (it & 1) * T::STAGE;
     const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-    dkdv_step<D, decltype(masked)::value>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, rlo, rhi,
+    dkdv_step<D, decltype(masked)::value, LEFT>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, rlo, rhi,
                                           off, half);
     lds_barrier();
     ++it;
@@ -465,8 +467,8 @@ __device__ __forceinline__ void issue_kv_dq(uint32_t stage, const i32x4& rk, con
   }
 }
 
-// Keys klo .. khi - 1 are visible to this lane's query row.
-template <int D, bool MASK>
+// Keys klo .. khi - 1 are visible to this lane's query row (klo <= 0 unless LEFT).
+template <int D, bool MASK, bool LEFT>
 __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf, const bf16x8* df,
                                         f32x16* dq, float c, float lse2, float dlt, int n0, int klo, int khi,
                                         const OperandOffsets<D>& off, int half) {
@@ -503,7 +505,7 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
     float pe = fast_exp2(__builtin_fmaf(s[v], c, -lse2));
     if (MASK) {
       const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
-      pe = (key >= klo && key < khi) ? pe : 0.f;
+      pe = ((!LEFT || key >= klo) && key < khi) ? pe : 0.f;
     }
     dsv[v] = pe * (dp[v] - dlt);
   }
@@ -521,7 +523,9 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
 }
 
 // BAND: the visible keys of a row form a band (causal and / or a local window).
-template <int D, bool BAND>
+// LEFT: the band has a left bound (window_left >= 0). Without one, a row's
+// visible keys start at key 0, and masked tiles test only their upper bound.
+template <int D, bool BAND, bool LEFT>
 __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(BwdParams p) {
   using T = DqCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
     const lds_char* cur = lds + (n & 1) * T::STAGE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      dq_half<D, decltype(masked)::value>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c,
+      dq_half<D, decltype(masked)::value, LEFT>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c,
                                           lse2, dlt, n * T::BN + kb * 32, klo, khi, off, half);
     lds_barrier();
   };
@@ -661,7 +665,7 @@ static hipError_t launch_prep(const BwdArgs& a, float* delta, float* lse2) {
   return hipGetLastError();
 }
 
-template <int D, bool BAND>
+template <int D, bool BAND, bool LEFT>
 static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
@@ -696,7 +700,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   // dQ first: it also writes the Delta / lse2 rows that dK / dV reads
   if (f.total_q > 0) {
     using T = DqCfg<D>;
-    auto kern = bwd_dq_kernel<D, BAND>;
+    auto kern = bwd_dq_kernel<D, BAND, LEFT>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -713,7 +717,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   }
   if (f.total_k > 0) {
     using T = DkdvCfg<D>;
-    auto kern = bwd_dkdv_kernel<D, BAND>;
+    auto kern = bwd_dkdv_kernel<D, BAND, LEFT>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -746,7 +750,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     return launch_bwd_main_d256(a, lse2, splits > 1 ? reinterpret_cast<float*>(part) : nullptr,
                                 splits > 1 ? reinterpret_cast<float*>(part + pb) : nullptr, splits);
   } else {
-    return band_of(a.f).band ? launch_bwd_t<D, true>(a, lse2) : launch_bwd_t<D, false>(a, lse2);
+    const Band bd = band_of(a.f);
+    if (!bd.band) return launch_bwd_t<D, false, false>(a, lse2);
+    return bd.wl >= 0 ? launch_bwd_t<D, true, true>(a, lse2) : launch_bwd_t<D, true, false>(a, lse2);
   }
 }
 

@@ -134,7 +134,7 @@ __device__ __forceinline__ uint4 v_operand(const lds_char* lds, const uint32_t* 
   return lds_ld16(lds + vrow[kk % 8] + 256 * (kk / 8));
 }
 
-template <bool MASK>
+template <bool MASK, bool LEFT>
 __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char* Qs, const lds_char* dOs,
                                              const float* lse2_s, const float* dlt_s, const bf16x8* kf,
                                              const uint32_t* vrow, f32x16 (&dk)[kDB], f32x16 (&dv)[kDB], float c,
@@ -203,7 +203,7 @@ __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char
     float pv = pe[e];
     if (MASK) {
       const int row = 16 * ks + 8 * half + e;
-      pv = (row >= rlo && row <= rhi) ? pv : 0.f;
+      pv = (row >= rlo && (!LEFT || row <= rhi)) ? pv : 0.f;
     }
     pm[e] = pv;
     dsv[e] = pv * (dp[8 * ks + e] - dl[ks][e]);
@@ -239,7 +239,9 @@ __device__ __forceinline__ void dkdv256_step(const lds_char* lds, const lds_char
 }
 
 // BAND: the visible keys of a row form a band (causal and / or a local window).
-template <bool BAND>
+// LEFT: the band has a left bound (window_left >= 0); without one, masked steps
+// test only a key's first visible row.
+template <bool BAND, bool LEFT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   using T = Dkdv256;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
     const int m0 = (sfirst + st) * T::BMQ;
     const lds_char* stg = lds + (it & 1) * T::STAGE;
     const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
-    dkdv256_step<decltype(masked)::value>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, rlo - m0,
+    dkdv256_step<decltype(masked)::value, LEFT>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, rlo - m0,
                                           rhi - m0, off, half);
     lds_barrier();
     ++it;
@@ -459,7 +461,7 @@ __device__ __forceinline__ void issue_kv_dq256(uint32_t stage, const i32x4& rk, 
 // One 32-key tile: S^T = K Q^T and dP^T = V dO^T (two chains), dS, then
 // dQ^T += K^T dS^T one (k-step, head-dim block) unit at a time.
 // Keys klo .. khi - 1 are visible to this lane's query row.
-template <bool MASK>
+template <bool MASK, bool LEFT>
 __device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* Vs, const bf16x8* qf,
                                            const bf16x8* df, f32x16 (&dq)[kDB], float c, float lse2, float dlt,
                                            int n0, int klo, int khi, const OperandOffsets<kD>& off, int half) {
@@ -500,7 +502,7 @@ __device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* V
     float pe = fast_exp2(__builtin_fmaf(s[v], c, -lse2));
     if (MASK) {
       const int key = n0 + 16 * (v >> 3) + 8 * half + (v & 7);
-      pe = (key >= klo && key < khi) ? pe : 0.f;
+      pe = ((!LEFT || key >= klo) && key < khi) ? pe : 0.f;
     }
     dsv[v] = pe * (dp[v] - dlt);
   }
@@ -521,7 +523,9 @@ __device__ __forceinline__ void dq256_tile(const lds_char* Ks, const lds_char* V
   }
 }
 
-template <bool BAND>
+// LEFT: the band has a left bound (window_left >= 0); without one, a row's
+// visible keys start at key 0 and masked tiles test only their upper bound.
+template <bool BAND, bool LEFT>
 __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   using T = Dq256;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   auto tile = [&](int n, auto masked) {
     stage_in(n);
     const lds_char* cur = lds + (n & 1) * T::STAGE;
-    dq256_tile<decltype(masked)::value>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, klo, khi, off, half);
+    dq256_tile<decltype(masked)::value, LEFT>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, klo, khi, off, half);
     lds_barrier();
   };
   for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   }
 }
 
-template <bool BAND>
+template <bool BAND, bool LEFT>
 hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
@@ -651,7 +655,7 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
 
   if (f.total_k > 0) {
     using T = Dkdv256;
-    auto kern = bwd_dkdv256_kernel<BAND>;
+    auto kern = bwd_dkdv256_kernel<BAND, LEFT>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -679,7 +683,7 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   }
   if (f.total_q > 0) {
     using T = Dq256;
-    auto kern = bwd_dq256_kernel<BAND>;
+    auto kern = bwd_dq256_kernel<BAND, LEFT>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -700,8 +704,10 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
 }  // namespace
 
 hipError_t launch_bwd_main_d256(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
-  return band_of(a.f).band ? launch_main_t<true>(a, lse2, part_dk, part_dv, splits)
-                            : launch_main_t<false>(a, lse2, part_dk, part_dv, splits);
+  const Band bd = band_of(a.f);
+  if (!bd.band) return launch_main_t<false, false>(a, lse2, part_dk, part_dv, splits);
+  return bd.wl >= 0 ? launch_main_t<true, true>(a, lse2, part_dk, part_dv, splits)
+                    : launch_main_t<true, false>(a, lse2, part_dk, part_dv, splits);
 }
 
 }  // namespace av
