@@ -23,7 +23,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_common(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
                  int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t max_q, int32_t max_k, int32_t Hq,
                  int32_t Hkv, int32_t D, float scale, int32_t causal) {
-  if (!q || !k || !v || !cu_q || !cu_k) return ATTN_VARLEN_ERR_NULL_POINTER;
+  // data pointers may be NULL when their tensors are empty (no rows)
+  if (!cu_q || !cu_k) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if ((total_q > 0 && !q) || (total_k > 0 && (!k || !v))) return ATTN_VARLEN_ERR_NULL_POINTER;
   if (D != 64 && D != 128 && D != 256) return ATTN_VARLEN_ERR_BAD_HEAD_DIM;
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return ATTN_VARLEN_ERR_BAD_HEADS;
   if (num_seqs < 1 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return ATTN_VARLEN_ERR_BAD_SEQLEN;
@@ -88,7 +90,7 @@ int attn_varlen_fwd_window(const void* q, const void* k, const void* v, const in
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
-  if (!out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (total_q > 0 && !out) return ATTN_VARLEN_ERR_NULL_POINTER;
   if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return ATTN_VARLEN_ERR_MISALIGNED;
   if (total_q == 0) return ATTN_VARLEN_OK;
   av::FwdArgs a = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
@@ -117,7 +119,7 @@ int attn_varlen_fwd_splitkv(const void* q, const void* k, const void* v, const i
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
-  if (!out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (total_q > 0 && !out) return ATTN_VARLEN_ERR_NULL_POINTER;
   if (!aligned(out, 16) || (lse && !aligned(lse, 4))) return ATTN_VARLEN_ERR_MISALIGNED;
   if (num_splits < 1 || num_splits > ATTN_VARLEN_MAX_SPLITS) return ATTN_VARLEN_ERR_BAD_SPLITS;
   // the split grid multiplies the forward's (query block x head) units by num_splits
@@ -146,7 +148,7 @@ int attn_varlen_fwd_persistent(const void* q, const void* k, const void* v, cons
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
-  if (!out) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (total_q > 0 && !out) return ATTN_VARLEN_ERR_NULL_POINTER;
   if (!sched) return ATTN_VARLEN_ERR_WORKSPACE;
   if (!aligned(out, 16) || (lse && !aligned(lse, 4)) || !aligned(sched, 4)) return ATTN_VARLEN_ERR_MISALIGNED;
   if (total_q == 0) return ATTN_VARLEN_OK;
@@ -189,12 +191,13 @@ int attn_varlen_bwd_window(const void* q, const void* k, const void* v, const in
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
-  if (!dout || !out || !lse || !dq || !dk || !dv) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if ((total_q > 0 && (!dout || !out || !lse || !dq)) || (total_k > 0 && (!dk || !dv)))
+    return ATTN_VARLEN_ERR_NULL_POINTER;
   if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4))
     return ATTN_VARLEN_ERR_MISALIGNED;
   const size_t need = av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
-  if (!workspace || workspace_bytes < need) return ATTN_VARLEN_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_VARLEN_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
   if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;
   av::BwdArgs a;

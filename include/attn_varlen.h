@@ -38,7 +38,10 @@
  *
  * Ownership: the caller allocates every buffer (device memory) and keeps it alive
  * until the work on `stream` is done. The library allocates nothing, frees
- * nothing and keeps no pointer after a call returns.
+ * nothing and keeps no pointer after a call returns. A pointer to a tensor with
+ * no rows may be NULL: q, out, dout, dq and the LSE of the backward when
+ * total_q = 0, and k, v, dk and dv when total_k = 0. A workspace may be NULL
+ * when its size is 0. The cu_seqlens arrays are never NULL.
  *
  * Execution: calls are asynchronous on `stream` (a hipStream_t, passed as void*;
  * NULL is the default stream) and never synchronise the host. They are
@@ -69,7 +72,7 @@ enum {
   ATTN_VARLEN_ERR_BAD_SEQLEN = -4,        /* num_seqs < 1, negative totals/max, max > total, or too large */
   ATTN_VARLEN_ERR_MISALIGNED = -5,        /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   ATTN_VARLEN_ERR_BAD_SCALE = -6,         /* softmax_scale is not finite */
-  ATTN_VARLEN_ERR_WORKSPACE = -7,         /* workspace NULL or smaller than attn_varlen_bwd_workspace_size() */
+  ATTN_VARLEN_ERR_WORKSPACE = -7,         /* workspace NULL or smaller than the size its call needs */
   ATTN_VARLEN_ERR_BAD_FLAG = -8,          /* causal not 0 or 1 */
   ATTN_VARLEN_ERR_HIP = -9,               /* the HIP runtime reported an error at launch */
   ATTN_VARLEN_ERR_BAD_SPLITS = -10        /* num_splits outside [1, ATTN_VARLEN_MAX_SPLITS] */

@@ -100,6 +100,33 @@ def test_fwd_empty_problem_is_a_no_op():
     assert fwd_call(D=64, total_q=0, max_q=0) == 0
 
 
+def test_null_pointers_of_empty_tensors_are_accepted():
+    # A tensor without rows may be passed as NULL. Each call below gets past the
+    # pointer checks and stops at a later check (head_dim 96, a misaligned
+    # pointer) or at the empty-problem return, so nothing is launched.
+    assert fwd_call(k=None, v=None, total_k=0, max_k=0) == E["ATTN_VARLEN_ERR_BAD_HEAD_DIM"]
+    assert fwd_call(q=None, out=None, total_q=0, max_q=0) == E["ATTN_VARLEN_ERR_BAD_HEAD_DIM"]
+    assert fwd_call(D=64, q=None, out=None, total_q=0, max_q=0) == 0
+    assert bwd_call(D=64, k=None, v=None, dk=None, dv=None, total_k=0, max_k=0,
+                    dq=FAKE + 8) == E["ATTN_VARLEN_ERR_MISALIGNED"]
+    assert bwd_call(D=64, q=None, dout=None, out=None, lse=None, dq=None, total_q=0, max_q=0,
+                    dk=FAKE + 8) == E["ATTN_VARLEN_ERR_MISALIGNED"]
+    # nothing to do at all: every data pointer and the (zero-byte) workspace NULL
+    assert bwd_call(D=64, q=None, k=None, v=None, dout=None, out=None, lse=None, dq=None, dk=None, dv=None,
+                    total_q=0, max_q=0, total_k=0, max_k=0, ws=None, ws_bytes=0) == 0
+
+
+@pytest.mark.parametrize("over", [dict(k=None), dict(v=None), dict(q=None)])
+def test_null_pointers_of_tensors_with_rows_are_rejected(over):
+    assert fwd_call(**over) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+    assert bwd_call(**over) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+
+
+@pytest.mark.parametrize("over", [dict(dq=None), dict(dk=None), dict(out=None), dict(lse=None)])
+def test_null_backward_outputs_with_rows_are_rejected(over):
+    assert bwd_call(D=64, **over) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+
+
 @pytest.mark.parametrize("over,code", [
     (dict(D=96), "ATTN_VARLEN_ERR_BAD_HEAD_DIM"),
     (dict(D=64, dout=None), "ATTN_VARLEN_ERR_NULL_POINTER"),

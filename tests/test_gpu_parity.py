@@ -559,6 +559,50 @@ def test_edge_cases_split_and_persistent(wl, splits):
     assert torch.equal(o2, o3) and torch.equal(l2, l3)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_no_keys_or_no_queries_at_all(D, causal):
+    """A batch without any key (total_k = 0) or without any query (total_q = 0):
+    the empty tensors come with NULL data pointers, which the library accepts.
+    Rows that see no key give O = 0 and LSE = -inf (and dQ = 0); keys that no
+    row sees give dK = dV = 0."""
+    nok = W.Workload(f"nokeys-d{D}", [37, 5], 4, 2, D, causal, seqlens_k=[0, 0])
+    inp = W.make_inputs(nok)
+    d = to_dev(inp)
+    assert d["k"].numel() == 0
+    q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+    ref_o, ref_l = O.forward(q, k, v, nok.cu_seqlens_q, nok.cu_seqlens_k, nok.softmax_scale, causal)
+    args = (d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], nok.max_seqlen_q, nok.max_seqlen_k,
+            nok.softmax_scale, causal)
+    announce(f"no keys D={D} causal={causal}: plain, split-KV, persistent, backward")
+    outs = [A.attn_varlen_fwd(*args, return_lse=True),
+            A.attn_varlen_fwd(*args, return_lse=True, num_splits=3),
+            A.attn_varlen_fwd(*args, return_lse=True, persistent=True)]
+    o, l = outs[0]
+    dq, dk, dv = A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], o, l, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                   nok.max_seqlen_q, nok.max_seqlen_k, nok.softmax_scale, causal)
+    torch.cuda.synchronize()
+    assert np.all(ref_o == 0.0) and np.all(np.isneginf(ref_l))
+    for oi, li in outs:
+        assert int(torch.count_nonzero(oi)) == 0
+        assert bool(torch.all(torch.isneginf(li)))
+    assert dq.shape == d["q"].shape and int(torch.count_nonzero(dq)) == 0
+    assert dk.numel() == 0 and dv.numel() == 0
+
+    noq = W.Workload(f"noqueries-d{D}", [0, 0], 4, 2, D, causal, seqlens_k=[40, 9])
+    d = to_dev(W.make_inputs(noq))
+    assert d["q"].numel() == 0
+    announce(f"no queries D={D} causal={causal}: forward, backward")
+    o, l = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], noq.max_seqlen_q,
+                             noq.max_seqlen_k, noq.softmax_scale, causal, return_lse=True)
+    dq, dk, dv = A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], o, l, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                   noq.max_seqlen_q, noq.max_seqlen_k, noq.softmax_scale, causal)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0
+    assert dk.shape == d["k"].shape and int(torch.count_nonzero(dk)) == 0
+    assert dv.shape == d["v"].shape and int(torch.count_nonzero(dv)) == 0
+
+
 @pytest.mark.parametrize("cu_q,cu_k,tq,tk,mq,mk,bits", [
     ([0, 5, 12], [0, 3, 12], 12, 12, 7, 9, 0),          # valid
     ([1, 5, 12], [0, 3, 12], 12, 12, 7, 9, 1),          # first entry not 0
