@@ -8,8 +8,8 @@ import torch
 import exact_attention_varlen_amd as A
 import oracle.attention as O
 import workloads as W
-from parity import (announce, check_grad, check_lse, check_out, f64, gpu_bwd, gpu_fwd, sample_rows, to_dev,
-                    window_of)
+from parity import (announce, check_grad, check_lse, check_out, check_out_rounded, f64, gpu_bwd, gpu_fwd,
+                    sample_rows, to_dev, window_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -557,6 +557,37 @@ def test_edge_cases_split_and_persistent(wl, splits):
         check_out(f64(o), ref_o)
         check_lse(f64(l), ref_l)
     assert torch.equal(o2, o3) and torch.equal(l2, l3)
+
+
+# Sharply peaked attention (a scale several times D^-1/2 on unit-variance data):
+# a row's output is nearly one V row, |O| reaches 4 and more, and there half a
+# bf16 spacing (1/64) is above the 1e-2 absolute bound. Outputs are held to
+# 1e-2 beyond that rounding (check_out_rounded); LSE and gradients to the usual
+# bounds.
+PEAKED = []
+for D in (64, 128, 256):
+    for c, sc in ((False, 0.5), (True, -0.4)):
+        PEAKED.append(W.Workload(f"peaked-d{D}-{'c' if c else 'f'}-s{sc}", [900, 33, 400], 8, 2, D, c,
+                                 softmax_scale=sc))
+
+
+@pytest.mark.parametrize("wl", PEAKED, ids=[w.name for w in PEAKED])
+def test_parity_peaked_attention(wl):
+    inp = W.make_inputs(wl)
+    d = to_dev(inp)
+    announce(f"peaked {wl.name}")
+    out, lse = gpu_fwd(wl, d)
+    dq, dk, dv = gpu_bwd(wl, d, out, lse)
+    torch.cuda.synchronize()
+    q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
+    ref_o, ref_l = O.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal)
+    assert np.abs(ref_o).max() >= 3.5  # the regime this test is for
+    check_out_rounded(f64(out), ref_o)
+    check_lse(f64(lse), ref_l)
+    rq, rk, rv = O.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do)
+    check_grad(f64(dq), rq, "dq")
+    check_grad(f64(dk), rk, "dk")
+    check_grad(f64(dv), rv, "dv")
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
