@@ -35,14 +35,33 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def warm_gpu(seconds: float = 1.0):
+def warm_gpu(min_s: float = 0.5, max_s: float = 3.0, tol: float = 0.02):
+    """Bring the chip to its loaded operating point before timing (the pages warm
+    up with bf16 matrix products before their timed runs: "[FA4/B200]
+    return_lse=True ..." repro script, GPU warm-up). Here: batches of eight
+    4096^3 bf16 products, each batch timed with device events, until three
+    batches in a row agree within `tol` (the clock has settled) and at least
+    `min_s` has passed, or `max_s` is reached. Returns the number of batches."""
     import torch
 
-    x = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
-    t_end = time.perf_counter() + seconds
-    while time.perf_counter() < t_end:
-        torch.mm(x, x)
-    torch.cuda.synchronize()
+    a = torch.randn(4096, 4096, device="cuda:0", dtype=torch.bfloat16)
+    c = torch.empty_like(a)
+    t0 = time.perf_counter()
+    recent = []
+    batches = 0
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(8):
+            torch.mm(a, a, out=c)
+        e1.record()
+        e1.synchronize()
+        batches += 1
+        recent = (recent + [e0.elapsed_time(e1)])[-3:]
+        elapsed = time.perf_counter() - t0
+        settled = len(recent) == 3 and (max(recent) - min(recent)) <= tol * min(recent)
+        if (settled and elapsed >= min_s) or elapsed >= max_s:
+            return batches
 
 
 def kernel_flop(name: str, wl) -> float:
@@ -342,12 +361,15 @@ def run_workload(wl, steps, warmup, profile=True):
     # 2) the same work replayed from HIP graphs: no host launch overhead
     fwd_ms, fwd_per = time_graph(fwd, steps, warmup)
     step_ms, step_per = time_graph(step, steps, warmup)
-    res["fwd_ms_steady"] = time_graph_steady(fwd)
-    res["fwd_tflops_steady"] = fwd_flop / (res["fwd_ms_steady"] * 1e-3) / 1e12
+    # the forward figure: event-timed, ten forwards back to back in one graph
+    # (per call, median of five rounds), free of the per-launch dispatch gap
+    # that a single-kernel graph replay adds
+    res["fwd_ms"] = time_graph_steady(fwd)
+    res["fwd_tflops"] = fwd_flop / (res["fwd_ms"] * 1e-3) / 1e12
     res["_step_fn"] = step
-    res["fwd_ms"] = fwd_ms
-    res["fwd_ms_median"] = statistics.median(fwd_per)
-    res["fwd_tflops"] = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    res["fwd_ms_single_replay"] = fwd_ms
+    res["fwd_ms_single_replay_median"] = statistics.median(fwd_per)
+    res["fwd_tflops_single_replay"] = fwd_flop / (fwd_ms * 1e-3) / 1e12
     res["step_ms"] = step_ms
     res["step_ms_median"] = statistics.median(step_per)
     res["fwdbwd_tflops"] = 3.5 * fwd_flop / (step_ms * 1e-3) / 1e12
@@ -416,9 +438,20 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     }
 
 
+def named_workload(name: str):
+    """A workload of the benchmark set by name (`--workload`)."""
+    import workloads as W
+
+    known = {wl.name: wl for wl in W.all_configs() + [W.single_16k_full()]}
+    if name not in known:
+        raise SystemExit(f"unknown workload {name!r}; known: {sorted(known)}")
+    return known[name]
+
+
 def eager_only(wl, steps: int, warmup: int):
-    """warmup + steps eager forward+backward steps, no graphs and no extra timing
-    machinery: the command profilers wrap."""
+    """warmup + steps eager forward+backward steps (forward only for a
+    forward-only workload), no graphs and no extra timing machinery: the command
+    profilers wrap."""
     import torch
 
     import exact_attention_varlen_amd as A
@@ -428,6 +461,8 @@ def eager_only(wl, steps: int, warmup: int):
     for i in range(warmup + steps):
         out, lse = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
                                      wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=True)
+        if not wl.backward:
+            continue
         A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
                           wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
     torch.cuda.synchronize()
@@ -692,6 +727,47 @@ def all_configs_table(include_long: bool):
     return 0
 
 
+def fwd_table():
+    """Steady-state forward time (with and without the LSE) of one workload per
+    head dim, for comparing builds of the library (ATTN_VARLEN_LIBRARY selects a
+    variant, e.g. one that computes a share of the exponentials on the FMA pipe):
+    one JSON line naming the library file and its exponential setting."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import exact_attention_varlen_amd._lib as L
+    import workloads as W
+
+    one = np.zeros(1, dtype=np.float32)
+    emu = L.lib().attn_varlen_exp2_fma_host(one.ctypes.data_as(ctypes.c_void_p), one.ctypes.data_as(ctypes.c_void_p),
+                                            1)
+    rows = {}
+    for wl in (W.hd64_mha(), W.single_16k_full(), W.packed_16k(), W.hd256_gqa(2, 16384, False)):
+        d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl, with_dout=False).items()}
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+        fl = wl.accounted_fwd_flop()
+        row = {}
+        for with_lse in (True, False):
+            def fwd():
+                A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
+                                  wl.max_seqlen_k, wl.softmax_scale, wl.causal, out=out,
+                                  lse=lse if with_lse else None)
+            ms = time_graph_steady(fwd, 10, 5)
+            tag = "lse" if with_lse else "no_lse"
+            row[f"fwd_ms_{tag}"] = ms
+            row[f"fwd_tflops_{tag}"] = fl / (ms * 1e-3) / 1e12
+        rows[wl.name] = row
+        del d, out, lse
+        torch.cuda.empty_cache()
+    print(json.dumps({"library": os.path.basename(L.LIB_PATH), "exp2_emulated_every": emu, "forward": rows}),
+          flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -701,6 +777,8 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true", help="skip the extra workloads")
     ap.add_argument("--eager-only", action="store_true",
                     help="only run warmup + steps eager fwd+bwd steps of the main workload (for profilers) and exit")
+    ap.add_argument("--workload", default=None,
+                    help="with --eager-only: the workload to run (a config name; default: the packed 16K batch)")
     ap.add_argument("--all-configs", action="store_true",
                     help="only time forward and forward+backward of every config (one JSON line each) and exit")
     ap.add_argument("--long", action="store_true", help="with --all-configs: include the 64K and 128K sequences")
@@ -709,6 +787,9 @@ def main(argv=None):
     ap.add_argument("--oracle-table", action="store_true",
                     help="only time the float64 oracle (forward, forward+backward) for every config, whole or on a "
                          "bounded sample with an extrapolated full time (one JSON line each) and exit")
+    ap.add_argument("--fwd-table", action="store_true",
+                    help="only time the forward (with and without the LSE) of one workload per head dim for the "
+                         "loaded library build (one JSON line) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
@@ -728,17 +809,20 @@ def main(argv=None):
     if a.copy_calibration:
         return copy_calibration()
     if a.all_configs:
-        warm_gpu(1.0)
+        warm_gpu()
         return all_configs_table(a.long)
+    if a.fwd_table:
+        warm_gpu()
+        return fwd_table()
     if a.window_split:
-        warm_gpu(1.0)
+        warm_gpu()
         print(json.dumps(window_split_secondary()), flush=True)
         return 0
     if a.eager_only:
-        return eager_only(W.packed_16k(), a.steps, a.warmup)
+        return eager_only(named_workload(a.workload) if a.workload else W.packed_16k(), a.steps, a.warmup)
     primary = W.packed_16k()
     log(f"device {torch.cuda.get_device_name(0)}; warming up")
-    warm_gpu(1.0)
+    warm_gpu()
     log(f"primary workload {primary.name}")
     res = run_workload(primary, a.steps, a.warmup, profile=True)
     secondary = {}
@@ -748,7 +832,7 @@ def main(argv=None):
             r = run_workload(wl, max(3, a.steps // 4), 2, profile=True)
             secondary[wl.name] = {
                 "fwd_tflops": r["fwd_tflops"], "fwdbwd_tflops": r["fwdbwd_tflops"], "fwd_ms": r["fwd_ms"],
-                "fwd_ms_steady": r["fwd_ms_steady"], "fwd_tflops_steady": r["fwd_tflops_steady"],
+                "fwd_ms_single_replay": r["fwd_ms_single_replay"],
                 "step_ms": r["step_ms"], "frac_fwd": r["fwd_tflops"] / PEAK_BF16_TFLOPS,
                 "frac_fwdbwd": r["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
                 "kernels": r["kernels"],
@@ -799,19 +883,25 @@ def main(argv=None):
         "config": {"workload": primary.name, **primary.describe(), "pass": "fwd (with LSE) + bwd"},
         "fwd_tflops": res["fwd_tflops"],
         "fwd_ms": res["fwd_ms"],
+        "fwd_timing": ("fwd_ms / fwd_tflops (the forward figure, against which the forward share of the peak "
+                       "is judged): HIP events around one graph of ten back-to-back forwards with the LSE, per "
+                       "call, median of five rounds. fwd_ms_single_replay: host wall clock over graph replays "
+                       "of one forward each, which adds the per-launch dispatch gap"),
         "frac_of_peak_fwd": res["fwd_tflops"] / PEAK_BF16_TFLOPS,
         "frac_of_peak_fwdbwd": res["fwdbwd_tflops"] / PEAK_BF16_TFLOPS,
-        "fwd_ms_steady": res["fwd_ms_steady"],
-        "fwd_tflops_steady": res["fwd_tflops_steady"],
+        "fwd_ms_single_replay": res["fwd_ms_single_replay"],
+        "fwd_tflops_single_replay": res["fwd_tflops_single_replay"],
         "clocks": clocks,
         # the published peak assumes 2400 MHz; this is the peak at the clock the
         # chip held (power-limited) while running the step
         "frac_of_peak_fwdbwd_at_sclk": (res["fwdbwd_tflops"] / (PEAK_BF16_TFLOPS * clocks["sclk_mhz_mean"] / 2400.0)
                                         if "sclk_mhz_mean" in clocks else None),
         "step_ms_median": res["step_ms_median"],
-        "fwd_ms_median": res["fwd_ms_median"],
+        "fwd_ms_single_replay_median": res["fwd_ms_single_replay_median"],
         "eager_step_ms": res["eager_step_ms"],
-        "timing": "HIP graph replay per step (value); per-kernel times from eager steps with library events",
+        "timing": ("value: HIP graph replays of one step (forward with LSE, then backward), host wall clock over "
+                   "the timed replays bracketed by synchronizations; per-kernel times from eager steps with "
+                   "library events on the launch stream"),
         "kernels": kern,
         "roofline": roofline,
         "gemm_reference": gemm,

@@ -46,6 +46,7 @@ __all__ = [
     "attn_varlen_version",
     "attn_varlen_schedule_host",
     "attn_varlen_schedule_device",
+    "attn_varlen_tile_plan_host",
     "attn_varlen_func",
     "attn_varlen_profile_enable",
     "attn_varlen_profile_records",
@@ -150,6 +151,8 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     ``persistent=True`` runs the persistent scheduler (``attn_varlen_fwd_persistent``,
     one split only); ``sched`` is its zeroed scratch (``SCHED_BYTES`` bytes),
     allocated per call when not given."""
+    if persistent and num_splits != 1:  # num_splits = 0 (library choice) may pick several
+        raise ValueError("the persistent scheduler runs the one-pass forward: num_splits must be 1")
     dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     total_q, Hq, D = q.shape
     total_k, Hkv, _ = k.shape
@@ -184,8 +187,6 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
             raise AttnVarlenError(rc, "attn_varlen_fwd_splitkv")
         return (out, lse) if lse is not None else out
     if persistent:
-        if num_splits != 1:
-            raise ValueError("the persistent scheduler runs the one-pass forward (num_splits=1)")
         if sched is None:
             sched = torch.zeros(SCHED_BYTES, dtype=torch.uint8, device=dev)
         elif sched.device != dev or sched.numel() * sched.element_size() < SCHED_BYTES:
@@ -197,10 +198,17 @@ def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         if rc != 0:
             raise AttnVarlenError(rc, "attn_varlen_fwd_persistent")
         return (out, lse) if lse is not None else out
-    rc = lib().attn_varlen_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                                      cu_seqlens_q.numel() - 1, total_q, total_k, int(max_seqlen_q),
-                                      int(max_seqlen_k), Hq, Hkv, D, float(softmax_scale), int(bool(causal)), wl, wr,
-                                      _ptr(out), _ptr(lse), _stream(dev))
+    if wl < 0 and wr < 0:  # no window: the plain entry point
+        rc = lib().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
+                                   total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
+                                   float(softmax_scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev))
+        if rc != 0:
+            raise AttnVarlenError(rc, "attn_varlen_fwd")
+        return (out, lse) if lse is not None else out
+    rc = lib().attn_varlen_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
+                                      total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
+                                      float(softmax_scale), int(bool(causal)), wl, wr, _ptr(out), _ptr(lse),
+                                      _stream(dev))
     if rc != 0:
         raise AttnVarlenError(rc, "attn_varlen_fwd_window")
     return (out, lse) if lse is not None else out
@@ -275,6 +283,15 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     wl, wr = (int(window_size[0]), int(window_size[1]))
+    if wl < 0 and wr < 0:  # no window: the plain entry point
+        rc = lib().attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
+                                   total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
+                                   float(softmax_scale), int(bool(causal)), _ptr(dout), _ptr(out), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(dev))
+        if rc != 0:
+            raise AttnVarlenError(rc, "attn_varlen_bwd")
+        return dq, dk, dv
     rc = lib().attn_varlen_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
                                       total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
                                       float(softmax_scale), int(bool(causal)), wl, wr, _ptr(dout), _ptr(out),
@@ -299,6 +316,23 @@ def attn_varlen_schedule_host(cu_seqlens_q, block_m: int):
                                          seq.ctypes.data_as(ctypes.c_void_p), blk.ctypes.data_as(ctypes.c_void_p), n)
     assert n2 == n
     return list(zip(seq[:n].tolist(), blk[:n].tolist()))
+
+
+PLAN_FWD, PLAN_DQ, PLAN_DKDV = 0, 1, 2  # ATTN_VARLEN_PLAN_*
+
+
+def attn_varlen_tile_plan_host(kind: int, head_dim: int, seqlen_q: int, seqlen_k: int, causal: bool,
+                               window_left: int, window_right: int, block: int):
+    """Tile plan of one work item (host only): dict with the block's first row or
+    key, its size, the tile size, the visited tiles [lo, hi), the unmasked tiles
+    [full_lo, full_hi) and, for the forward with a left bound, the left-edge tiles."""
+    plan = (ctypes.c_int32 * 8)()
+    rc = lib().attn_varlen_tile_plan_host(int(kind), int(head_dim), int(seqlen_q), int(seqlen_k), int(bool(causal)),
+                                          int(window_left), int(window_right), int(block), plan)
+    if rc != 0:
+        raise AttnVarlenError(rc, "attn_varlen_tile_plan_host")
+    keys = ("start", "size", "tile", "lo", "hi", "full_lo", "full_hi", "left_edge")
+    return dict(zip(keys, list(plan)))
 
 
 def attn_varlen_schedule_device(cu_seqlens_q: torch.Tensor, max_seqlen_q: int, block_m: int, count: int):

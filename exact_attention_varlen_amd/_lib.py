@@ -10,7 +10,12 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libattn_varlen.so")
+# ATTN_VARLEN_LIBRARY names another build of the same library in this directory
+# (a variant built with `build.py --out NAME --extra -D...`, for comparisons)
+_LIB_FILE = os.environ.get("ATTN_VARLEN_LIBRARY", "libattn_varlen.so")
+if os.path.basename(_LIB_FILE) != _LIB_FILE or not _LIB_FILE.endswith(".so"):
+    raise ValueError("ATTN_VARLEN_LIBRARY must name a .so file in the package directory")
+LIB_PATH = os.path.join(HERE, _LIB_FILE)
 
 _lock = threading.Lock()
 _lib = None
@@ -45,6 +50,8 @@ _SIGNATURES = {
     "attn_varlen_version": (ctypes.c_int, []),
     "attn_varlen_schedule_host": (c_i64, [c_vp, c_i32, c_i32, c_vp, c_vp, c_i64]),
     "attn_varlen_schedule_device": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp]),
+    "attn_varlen_tile_plan_host": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "attn_varlen_exp2_fma_host": (ctypes.c_int, [c_vp, c_vp, c_i64]),
     "attn_varlen_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "attn_varlen_profile_count": (ctypes.c_int, []),
     "attn_varlen_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(c_f32)]),

@@ -55,8 +55,8 @@ def _filter(log: str) -> str:
     return "\n".join(keep)
 
 
-def _compile(src: str, extra, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, verbose: bool, build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -72,21 +72,26 @@ def _compile(src: str, extra, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False, extra_flags=()) -> str:
-    """Compile all sources for gfx950 and link ``libattn_varlen.so``. Returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 0, verbose: bool = False, extra_flags=(), out: str = LIB_NAME) -> str:
+    """Compile all sources for gfx950 and link ``libattn_varlen.so`` (or a variant
+    named ``out`` in the same directory, built with ``extra_flags``). Returns its path."""
+    if os.path.basename(out) != out or not out.endswith(".so"):
+        raise ValueError("out must be a .so file name in the package directory")
+    lib_path = os.path.join(HERE, out)
+    build_dir = BUILD_DIR if out == LIB_NAME else os.path.join(BUILD_DIR, os.path.splitext(out)[0])
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags), verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags), verbose, build_dir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking {LIB_NAME} failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}", flush=True)
-    return LIB_PATH
+        print(f"built {lib_path}", flush=True)
+    return lib_path
 
 
 def main(argv=None) -> int:
@@ -94,8 +99,9 @@ def main(argv=None) -> int:
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--extra", action="append", default=[], help="extra hipcc flag (repeatable)")
+    ap.add_argument("--out", default=LIB_NAME, help="library file name (a variant build; default the library)")
     a = ap.parse_args(argv)
-    build(a.jobs, a.verbose, a.extra)
+    build(a.jobs, a.verbose, a.extra, a.out)
     return 0
 
 

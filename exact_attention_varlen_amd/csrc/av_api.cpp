@@ -9,13 +9,14 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "av_exp2.h"
 #include "av_launch.h"
 #include "av_sched.h"
 
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 4;
+constexpr int kVersionMinor = 5;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -76,6 +77,37 @@ av::FwdArgs make_fwd_args(const void* q, const void* k, const void* v, const int
   a.lse = nullptr;
   a.stream = stream;
   return a;
+}
+
+int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+                const void* dout, const void* out, const float* lse, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                        n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
+  if (rc != ATTN_VARLEN_OK) return rc;
+  if ((total_q > 0 && (!dout || !out || !lse || !dq)) || (total_k > 0 && (!dk || !dv)))
+    return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return ATTN_VARLEN_ERR_MISALIGNED;
+  const size_t need = av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_VARLEN_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;
+  av::BwdArgs a;
+  a.f = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, stream);
+  a.dout = dout;
+  a.out = out;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  return av::launch_bwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
 }
 
 }  // namespace
@@ -188,29 +220,9 @@ int attn_varlen_bwd_window(const void* q, const void* k, const void* v, const in
                            int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
                            int32_t window_right, const void* dout, const void* out, const float* lse, void* dq,
                            void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
-                        n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
-  if (rc != ATTN_VARLEN_OK) return rc;
-  if ((total_q > 0 && (!dout || !out || !lse || !dq)) || (total_k > 0 && (!dk || !dv)))
-    return ATTN_VARLEN_ERR_NULL_POINTER;
-  if (!aligned(dout, 16) || !aligned(out, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4))
-    return ATTN_VARLEN_ERR_MISALIGNED;
-  const size_t need = av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_VARLEN_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
-  if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;
-  av::BwdArgs a;
-  a.f = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
-                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, stream);
-  a.dout = dout;
-  a.out = out;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.delta = static_cast<float*>(workspace);
-  return av::launch_bwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
+  return bwd_checked(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                     n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, dout, out, lse,
+                     dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -281,6 +293,72 @@ int attn_varlen_schedule_device(const int32_t* cu_seqlens_q, int32_t num_seqs, i
                                    stream) == hipSuccess
              ? ATTN_VARLEN_OK
              : ATTN_VARLEN_ERR_HIP;
+}
+
+int attn_varlen_tile_plan_host(int32_t kind, int32_t head_dim, int32_t seqlen_q, int32_t seqlen_k, int32_t causal,
+                               int32_t window_left, int32_t window_right, int32_t block, int32_t* plan) {
+  if (!plan) return ATTN_VARLEN_ERR_NULL_POINTER;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_VARLEN_ERR_BAD_HEAD_DIM;
+  if (causal != 0 && causal != 1) return ATTN_VARLEN_ERR_BAD_FLAG;
+  if (seqlen_q < 0 || seqlen_k < 0) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  const int Lq = seqlen_q, Lk = seqlen_k;
+  // the window as the launchers see it for a one-sequence batch (make_fwd_args,
+  // band_of): sides wider than the sequence are unbounded; causal caps the right
+  const int wl = (window_left < 0 || window_left >= Lk) ? -1 : window_left;
+  const int wr0 = (window_right < 0 || window_right >= Lq) ? -1 : window_right;
+  const int wr = causal ? 0 : wr0;
+  const bool band = wl >= 0 || wr >= 0;
+  for (int i = 0; i < 8; ++i) plan[i] = 0;
+  if (kind == ATTN_VARLEN_PLAN_FWD || kind == ATTN_VARLEN_PLAN_DQ) {
+    const int bm = av::kQueryBlock, bn = av::key_tile(head_dim);
+    if (block < 0 || block >= av::ceil_div(Lq, bm)) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+    const int q0 = block * bm - av::query_lead(Lq, bm, bn);
+    // the kernels' ranges: plain attention visits every key tile and masks the
+    // partial last one; a band takes the tile span of the block's rows
+    av::TileSpan t{0, av::ceil_div(Lk, bn), 0, Lk / bn};
+    if (band) {
+      const int r0 = q0 > 0 ? q0 : 0, r1 = (q0 + bm < Lq ? q0 + bm : Lq) - 1;
+      // the forward's causal / right-bound path (no left bound) leaves the
+      // left side open, as its launcher does
+      t = av::key_tiles(r0, r1, bn, Lq, Lk, (kind == ATTN_VARLEN_PLAN_FWD && wl < 0) ? -1 : wl, wr);
+    }
+    int nh = 0, lo_unmasked = t.full_lo, hi_unmasked = t.full_hi;
+    if (kind == ATTN_VARLEN_PLAN_FWD) {
+      // the forward runs its unmasked tiles first: [0, f_hi) without a left
+      // bound; with one, nh left-edge tiles, then unmasked ones up to nm
+      lo_unmasked = t.lo;
+      hi_unmasked = t.full_hi;
+      if (wl >= 0) {
+        int nm = 0;
+        av::left_edge_tiles(t.lo, t.hi, t.full_lo, t.full_hi, wl, bn, nh, nm);
+        lo_unmasked = t.lo + nh;
+        hi_unmasked = t.lo + nm;
+      }
+    } else if (hi_unmasked < lo_unmasked) {
+      hi_unmasked = lo_unmasked;
+    }
+    const int32_t v[8] = {q0, bm, bn, t.lo, t.hi, lo_unmasked, hi_unmasked, nh};
+    for (int i = 0; i < 8; ++i) plan[i] = v[i];
+    return ATTN_VARLEN_OK;
+  }
+  if (kind == ATTN_VARLEN_PLAN_DKDV) {
+    const int bnk = av::kKeyBlock, bmq = av::query_step(head_dim);
+    if (block < 0 || block >= av::ceil_div(Lk, bnk)) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+    const int n0 = block * bnk;
+    av::TileSpan s{0, av::ceil_div(Lq, bmq), 0, av::ceil_div(Lq, bmq)};
+    if (band) s = av::query_steps(n0, (n0 + bnk < Lk ? n0 + bnk : Lk) - 1, bmq, Lq, Lk, wl, wr);
+    const int32_t v[8] = {n0, bnk, bmq, s.lo, s.hi, s.full_lo, s.full_hi, 0};
+    for (int i = 0; i < 8; ++i) plan[i] = v[i];
+    return ATTN_VARLEN_OK;
+  }
+  return ATTN_VARLEN_ERR_BAD_FLAG;
+}
+
+int attn_varlen_exp2_fma_host(const float* x, float* y, int64_t n) {
+  if (n < 0) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+  if (n > 0 && (!x || !y)) return ATTN_VARLEN_ERR_NULL_POINTER;
+  for (int64_t i = 0; i < n; ++i) y[i] = av::exp2_fma(x[i]);
+  return AV_EXP2_EMU;
 }
 
 int attn_varlen_profile_enable(int enable) { return av::prof_enable(enable); }

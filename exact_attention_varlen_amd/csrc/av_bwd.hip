@@ -111,6 +111,7 @@ struct DkdvCfg {
   static constexpr size_t LDS_BYTES = 2 * STAGE;
   static constexpr int DMA_PER_WAVE = 2 * QT::DMAS / 4;  // Q and dO copies
   static constexpr int F32_DMAS = BMQ / 64;              // 64-row fp32 copies per array
+  static_assert(D > 128 || (BNK == kKeyBlock && BMQ == query_step(D)), "tile shapes of the host-side plan");
 };
 
 template <int D>
@@ -340,15 +341,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // every key of the block (rows past Lq read as zero and add nothing)
   int sfirst = 0, nsteps = ceil_div(Lq, T::BMQ), s_full_lo = 0, s_full_hi = nsteps;
   if (BAND) {
-    const RowRange rr = block_rows(n0, min(n0 + T::BNK, Lk) - 1, Lq, Lk, p.wl, p.wr);
-    sfirst = rr.lo / T::BMQ;
-    const int slast = (rr.hi > rr.lo) ? ceil_div(rr.hi, T::BMQ) : sfirst;
-    nsteps = slast - sfirst;
-    s_full_lo = max(sfirst, ceil_div(rr.full_lo, T::BMQ));
-    s_full_hi = (rr.full_hi >= Lq) ? slast : min(slast, rr.full_hi / T::BMQ);
-    s_full_hi = max(s_full_lo, s_full_hi);
-    s_full_lo -= sfirst;
-    s_full_hi -= sfirst;
+    const TileSpan ts = query_steps(n0, min(n0 + T::BNK, Lk) - 1, T::BMQ, Lq, Lk, p.wl, p.wr);
+    sfirst = ts.lo;
+    nsteps = ts.hi - ts.lo;
+    s_full_lo = ts.full_lo - sfirst;
+    s_full_hi = ts.full_hi - sfirst;
   }
   const int total = (nsteps > 0) ? nsteps * r : 0;
 
@@ -453,6 +450,7 @@ struct DqCfg {
   static constexpr size_t LDS_BYTES = 2 * STAGE;
   static constexpr int DMA_PER_WAVE = 2 * KV::DMAS / 4;
   static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
+  static_assert(D > 128 || (BM == kQueryBlock && BN == key_tile(D)), "tile shapes of the host-side plan");
 };
 
 template <int D>
@@ -555,11 +553,11 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   // ones (the band's left edge before, its right edge and the sequence end after)
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const KeyRange kr = block_keys(max(q0, 0), min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
-    t_lo = kr.lo / T::BN;
-    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
-    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
-    f_hi = max(f_lo, min(t_hi, kr.full_hi / T::BN));
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
+    t_lo = ts.lo;
+    t_hi = ts.hi;
+    f_lo = ts.full_lo;
+    f_hi = max(f_lo, ts.full_hi);
   }
   const int klo = BAND ? band_lo(qi, Lq, Lk, p.wl) : 0;
   const int khi = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;

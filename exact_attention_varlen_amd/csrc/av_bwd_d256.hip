@@ -91,6 +91,7 @@ struct Dkdv256 {
   static constexpr int NT = 256;
   static constexpr int BNK = 128;  // keys per workgroup (32 per wave)
   static constexpr int BMQ = 32;   // query rows per step
+  static_assert(BNK == kKeyBlock && BMQ == query_step(kD), "tile shapes of the host-side plan");
   using QT = RowTile<kD, BMQ>;
   static constexpr int ROW = QT::ROW;
   static constexpr int TILE = QT::BYTES;     // 16 KB
@@ -276,15 +277,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   // and among them the unmasked ones [s_full_lo, s_full_hi) (relative)
   int sfirst = 0, nsteps = ceil_div(Lq, T::BMQ), s_full_lo = 0, s_full_hi = nsteps;
   if (BAND) {
-    const RowRange rr = block_rows(n0, min(n0 + T::BNK, Lk) - 1, Lq, Lk, p.wl, p.wr);
-    sfirst = rr.lo / T::BMQ;
-    const int slast = (rr.hi > rr.lo) ? ceil_div(rr.hi, T::BMQ) : sfirst;
-    nsteps = slast - sfirst;
-    s_full_lo = max(sfirst, ceil_div(rr.full_lo, T::BMQ));
-    s_full_hi = (rr.full_hi >= Lq) ? slast : min(slast, rr.full_hi / T::BMQ);
-    s_full_hi = max(s_full_lo, s_full_hi);
-    s_full_lo -= sfirst;
-    s_full_hi -= sfirst;
+    const TileSpan ts = query_steps(n0, min(n0 + T::BNK, Lk) - 1, T::BMQ, Lq, Lk, p.wl, p.wr);
+    sfirst = ts.lo;
+    nsteps = ts.hi - ts.lo;
+    s_full_lo = ts.full_lo - sfirst;
+    s_full_hi = ts.full_hi - sfirst;
   }
   const int total = (nsteps > 0) ? nsteps * hper : 0;
 
@@ -436,6 +433,7 @@ struct Dq256 {
   static constexpr int NT = 256;
   static constexpr int BM = 128;  // query rows per workgroup (32 per wave)
   static constexpr int BN = 32;   // keys per tile
+  static_assert(BM == kQueryBlock && BN == key_tile(kD), "tile shapes of the host-side plan");
   using KV = RowTile<kD, BN>;
   static constexpr int ROW = KV::ROW;
   static constexpr int TILE = KV::BYTES;  // 16 KB
@@ -554,11 +552,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   // key tiles [t_lo, t_hi), the unmasked ones [f_lo, f_hi)
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const KeyRange kr = block_keys(max(q0, 0), min(q0 + T::BM, Lq) - 1, Lq, Lk, p.wl, p.wr);
-    t_lo = kr.lo / T::BN;
-    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
-    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
-    f_hi = max(f_lo, min(t_hi, kr.full_hi / T::BN));
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
+    t_lo = ts.lo;
+    t_hi = ts.hi;
+    f_lo = ts.full_lo;
+    f_hi = max(f_lo, ts.full_hi);
   }
   const int klo = BAND ? band_lo(qi, Lq, Lk, p.wl) : 0;
   const int khi = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;

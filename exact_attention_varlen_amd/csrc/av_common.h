@@ -254,20 +254,25 @@ __device__ inline bool decode_rank_nb(const int32_t* cu, int num_seqs, int bm, i
                                       int& b_out, int& m_out) {
   const int lane = threadIdx.x & (kWave - 1);
   if (levels <= 0) return false;
-  // pass 1: lane t probes k = t * stride
-  const int stride = ceil_div(levels, kWave);
+  // C(k) falls as k grows; the level of `rank` is the largest k < levels with
+  // C(k) > rank. Pass 1: lane t probes k = t * stride.
+  int stride = ceil_div(levels, kWave);
   const int k1 = lane * stride;
   const int c1 = count_at_least(cu, num_seqs, bm, nb_lane, k1);
   const uint64_t mask = __ballot((k1 < levels) && (c1 > rank));
   if (mask == 0) return false;
-  const int t1 = highest_bit(mask);
-  int kstar = t1 * stride;
-  if (stride > 1) {
-    // pass 2: lane t probes k = t1 * stride + t inside the segment
-    const int k2 = t1 * stride + lane;
+  int kstar = highest_bit(mask) * stride;
+  // Then narrow the segment [kstar, kstar + stride), where C(kstar) > rank, by a
+  // factor of 64 per pass until it is one level wide: lane t probes
+  // kstar + t * sub. One pass when levels <= 4096 (block counts up to 2^12),
+  // at most three more up to 2^24 levels.
+  while (stride > 1) {
+    const int sub = ceil_div(stride, kWave);
+    const int k2 = kstar + lane * sub;
     const int c2 = count_at_least(cu, num_seqs, bm, nb_lane, k2);
-    const uint64_t mask2 = __ballot((lane < stride) && (k2 < levels) && (c2 > rank));
-    kstar = t1 * stride + highest_bit(mask2);
+    const uint64_t mask2 = __ballot((lane * sub < stride) && (k2 < levels) && (c2 > rank));
+    kstar += highest_bit(mask2) * sub;  // lane 0 probes kstar itself, so mask2 != 0
+    stride = sub;
   }
   // rank within level kstar: subtract the number of blocks of higher index
   const int above = count_at_least(cu, num_seqs, bm, nb_lane, kstar + 1);

@@ -54,6 +54,7 @@
 #include <type_traits>
 
 #include "av_common.h"
+#include "av_exp2.h"
 #include "av_launch.h"
 #include "av_tiles.h"
 
@@ -95,6 +96,7 @@ template <int D>
 struct FwdBlock {
   static constexpr int BM = 128;
   static constexpr int BN = (D <= 128) ? 64 : 32;
+  static_assert(BM == kQueryBlock && BN == key_tile(D), "tile shapes of the host-side plan");
 };
 
 struct FwdParams {
@@ -233,8 +235,10 @@ __device__ __forceinline__ float max16(const f32x16& s, float m) {
 // score of a pair, packs the pair to bf16 (and, on masked tiles, splits it
 // into hi / lo parts). Issuing the exponentials one MFMA ahead of their use
 // hides the latency of the transcendental unit.
+template <bool EMU = false>
 __device__ __forceinline__ void exp_issue(const f32x16* sc, int i, float c, float nm, float* pe) {
-  pe[i] = fast_exp2(__builtin_fmaf(sc[i >> 4][i & 15], c, nm));
+  const float t = __builtin_fmaf(sc[i >> 4][i & 15], c, nm);
+  pe[i] = EMU ? exp2_fma(t) : fast_exp2(t);
 }
 
 template <bool SPLIT>
@@ -381,7 +385,10 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n
     } else {
       // this share's exponentials, and the sums / packing of the previous share's
 #pragma unroll
-      for (int i = SB * m / NB; i < SB * (m + 1) / NB; ++i) exp_issue(sc, i, x.c, nm, pe);
+      for (int i = SB * m / NB; i < SB * (m + 1) / NB; ++i) {
+        if (exp2_emulated(i)) exp_issue<true>(sc, i, x.c, nm, pe);
+        else exp_issue(sc, i, x.c, nm, pe);
+      }
       if (m > 0) {
 #pragma unroll
         for (int i = SB * (m - 1) / NB; i < SB * m / NB; ++i) exp_finish<MC>(i, l_run, l_o, pe, ph, pl);
@@ -426,7 +433,10 @@ __device__ __forceinline__ void fwd_step(const FwdCtx<D, BM, BN, MODE>& x, int n
     } else if (u <= UC) {
       if (u < UC) {
 #pragma unroll
-        for (int i = SB + (NS - SB) * u / UC; i < SB + (NS - SB) * (u + 1) / UC; ++i) exp_issue(sc, i, x.c, nm, pe);
+        for (int i = SB + (NS - SB) * u / UC; i < SB + (NS - SB) * (u + 1) / UC; ++i) {
+          if (exp2_emulated(i)) exp_issue<true>(sc, i, x.c, nm, pe);
+          else exp_issue(sc, i, x.c, nm, pe);
+        }
       }
       const int f0 = u ? SB + (NS - SB) * (u - 1) / UC : SB * (NB - 1) / NB;
       const int f1 = u ? SB + (NS - SB) * u / UC : SB;
@@ -534,11 +544,11 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   constexpr bool BAND = MODE > 0;
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const KeyRange kr = block_keys(max(q0, 0), min(q0 + T::BM, Lq) - 1, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
-    t_lo = kr.lo / T::BN;
-    t_hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, T::BN) : t_lo;
-    f_lo = max(t_lo, ceil_div(kr.full_lo, T::BN));
-    f_hi = min(t_hi, kr.full_hi / T::BN);
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
+    t_lo = ts.lo;
+    t_hi = ts.hi;
+    f_lo = ts.full_lo;
+    f_hi = ts.full_hi;
   }
   if (SPLIT) {
     // chunk `split` of the item's tiles: ceil(n / splits) tiles each, the last
@@ -576,18 +586,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   const int ntot = t_hi - t_lo;
   int nh = 0;
   int nm = SPLIT ? max(0, min(f_hi, t_hi) - t_lo) : f_hi;
-  if (MODE == 2) {
-    nm = 0;
-    if (p.wl >= T::BN) {
-      const int nme = max(0, min(f_hi, t_hi) - t_lo);
-      int hh = max(0, min(min(f_lo, f_hi), t_hi) - t_lo);
-      hh += hh & 1;
-      if (hh < nme) {
-        nh = hh;
-        nm = nme;
-      }
-    }
-  }
+  if (MODE == 2) left_edge_tiles(t_lo, t_hi, f_lo, f_hi, p.wl, T::BN, nh, nm);
   // The tile counts are the same in every lane; saying so keeps the loops'
   // control in scalar registers where the compiler does not prove it (with a
   // left band edge or split-KV chunks; vector loop bounds there cost registers

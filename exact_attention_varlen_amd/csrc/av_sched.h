@@ -108,6 +108,76 @@ AV_HD inline RowRange block_rows(int c0, int c1, int Lq, int Lk, int wl, int wr)
   return r;
 }
 
+// Tiles of a work item, in units of whole tiles: the tiles [lo, hi) that hold
+// some visible (row, key) pair of the item, and among them [full_lo, full_hi)
+// (empty when full_hi <= full_lo), the tiles whose every pair is visible, which
+// the kernels run without a mask.
+struct TileSpan {
+  int lo, hi, full_lo, full_hi;
+};
+
+// Key tiles of bn keys met by the query rows [r0, r1] (inclusive, in range) of
+// a query block. A partial last tile (keys past Lk) is never full.
+AV_HD inline TileSpan key_tiles(int r0, int r1, int bn, int Lq, int Lk, int wl, int wr) {
+  const KeyRange kr = block_keys(r0, r1, Lq, Lk, wl, wr);
+  TileSpan t;
+  t.lo = kr.lo / bn;
+  t.hi = (kr.hi > kr.lo) ? ceil_div(kr.hi, bn) : t.lo;
+  t.full_lo = t.lo > ceil_div(kr.full_lo, bn) ? t.lo : ceil_div(kr.full_lo, bn);
+  t.full_hi = t.hi < kr.full_hi / bn ? t.hi : kr.full_hi / bn;
+  return t;
+}
+
+// Query steps of bmq rows that meet the keys [c0, c1] (inclusive, in range) of
+// a key block. Rows past Lq read as zero and add nothing to dK / dV, so a last
+// partial step counts as full when every row of the sequence in it sees every
+// key of the block.
+AV_HD inline TileSpan query_steps(int c0, int c1, int bmq, int Lq, int Lk, int wl, int wr) {
+  const RowRange rr = block_rows(c0, c1, Lq, Lk, wl, wr);
+  TileSpan s;
+  s.lo = rr.lo / bmq;
+  s.hi = (rr.hi > rr.lo) ? ceil_div(rr.hi, bmq) : s.lo;
+  s.full_lo = s.lo > ceil_div(rr.full_lo, bmq) ? s.lo : ceil_div(rr.full_lo, bmq);
+  s.full_hi = (rr.full_hi >= Lq) ? s.hi : (s.hi < rr.full_hi / bmq ? s.hi : rr.full_hi / bmq);
+  if (s.full_hi < s.full_lo) s.full_hi = s.full_lo;
+  return s;
+}
+
+// With a left band edge, the forward splits an item's key tiles [t_lo, t_hi)
+// (unmasked ones [f_lo, f_hi)) into: nh left-edge tiles that cross some row's
+// left edge but lie left of every row's right edge, then unmasked tiles up to
+// nm, then masked ones (local indices from t_lo). The left-edge tiles have
+// their scores masked by the step before them and then take the unmasked
+// probability path; that needs every row that reaches them to see at least a
+// tile of keys, which a window of at least bn keys left of the diagonal gives.
+// nh is even (the steady-state loop runs tiles in pairs); when the left-edge
+// tiles do not end before the unmasked ones do, every tile runs masked
+// (nh = nm = 0).
+AV_HD inline void left_edge_tiles(int t_lo, int t_hi, int f_lo, int f_hi, int wl, int bn, int& nh, int& nm) {
+  nh = 0;
+  nm = 0;
+  if (wl < bn) return;
+  const int fe = f_hi < t_hi ? f_hi : t_hi;
+  const int nme = fe - t_lo > 0 ? fe - t_lo : 0;
+  int he = f_lo < f_hi ? f_lo : f_hi;
+  he = he < t_hi ? he : t_hi;
+  int hh = he - t_lo > 0 ? he - t_lo : 0;
+  hh += hh & 1;
+  if (hh < nme) {
+    nh = hh;
+    nm = nme;
+  }
+}
+
+// Tile shapes of the kernels, shared with the host-side plan inspection: the
+// forward and dQ kernels take query blocks of kQueryBlock rows against key
+// tiles of key_tile(D) keys; the dK / dV kernels take key blocks of kKeyBlock
+// keys against query steps of query_step(D) rows.
+constexpr int kQueryBlock = 128;
+constexpr int kKeyBlock = 128;
+AV_HD constexpr int key_tile(int D) { return D <= 128 ? 64 : 32; }
+AV_HD constexpr int query_step(int D) { return D <= 128 ? 128 : 32; }
+
 // Host reference of the ranking: enumerate (b, m) in rank order.
 inline int64_t rank_enumerate_host(const int32_t* cu, int num_seqs, int bm, int32_t* seq_out,
                                    int32_t* block_out, int64_t capacity) {

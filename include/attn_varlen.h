@@ -302,6 +302,54 @@ int attn_varlen_schedule_device(const int32_t* cu_seqlens_q, int32_t num_seqs, i
                                 void* stream);
 
 /*
+ * Tile plan inspection (host, no GPU needed): which tiles a kernel visits for
+ * one work item of a one-sequence batch, and which of them it runs without a
+ * mask ([GUIDE] Core Abstractions: the block-info helper that gives the range
+ * of key blocks a query block meets under causal and local masks). Visiting
+ * every tile that holds a visible (query, key) pair and masking every tile
+ * that holds a hidden one is what makes the kernels exact; the tests check
+ * both by enumerating every pair of small sequences.
+ *   kind        ATTN_VARLEN_PLAN_FWD  query block `block` of the forward kernel
+ *               ATTN_VARLEN_PLAN_DQ   query block `block` of the dQ kernel
+ *               ATTN_VARLEN_PLAN_DKDV key block `block` of the dK / dV kernel
+ *   head_dim    64, 128 or 256 (tile shapes depend on it)
+ *   seqlen_q, seqlen_k, causal, window_left, window_right
+ *               the sequence and its mask, as in attn_varlen_fwd_window
+ *   plan        int32[8], written:
+ *               [0] first row (query blocks; may be negative: the blocks are
+ *                   aligned toward the sequence end) or first key (key blocks)
+ *               [1] rows (query blocks) or keys (key blocks) per block
+ *               [2] keys per key tile (FWD, DQ) or rows per query step (DKDV)
+ *               [3], [4] the tiles visited, [lo, hi)
+ *               [5], [6] the tiles run without a mask, [lo, hi) (empty if hi <= lo)
+ *               [7] FWD with a left window bound: the left-edge tiles [lo, lo + [7])
+ *                   whose scores are masked but whose probabilities take the
+ *                   unmasked path; 0 otherwise
+ *               A tile index t covers keys (or query rows) [t * plan[2], (t + 1) * plan[2]).
+ * Errors: ATTN_VARLEN_ERR_NULL_POINTER, ATTN_VARLEN_ERR_BAD_HEAD_DIM,
+ * ATTN_VARLEN_ERR_BAD_FLAG (causal or kind), ATTN_VARLEN_ERR_BAD_SEQLEN
+ * (negative lengths, block out of range).
+ */
+#define ATTN_VARLEN_PLAN_FWD 0
+#define ATTN_VARLEN_PLAN_DQ 1
+#define ATTN_VARLEN_PLAN_DKDV 2
+int attn_varlen_tile_plan_host(int32_t kind, int32_t head_dim, int32_t seqlen_q, int32_t seqlen_k, int32_t causal,
+                               int32_t window_left, int32_t window_right, int32_t block, int32_t* plan);
+
+/*
+ * The forward's FMA-pipe exponential, evaluated on the host for testing
+ * ([HD256] Observations: exp2 emulation on FMA units; [GUIDE] Other Components,
+ * fast_math): y[i] = 2^x[i] by range reduction x = n + f (n = rint(x)) and a
+ * degree-3 minimax polynomial for 2^f, relative error <= 7.5e-5 plus float32
+ * rounding for x >= -125, exactly 0 below (and for -inf). The forward kernel
+ * uses it for every K-th score of an unmasked tile when the library is built
+ * with AV_EXP2_EMU = K (0, the default: the hardware exponential only).
+ * Returns K (>= 0), or ATTN_VARLEN_ERR_BAD_SEQLEN (n < 0) /
+ * ATTN_VARLEN_ERR_NULL_POINTER.
+ */
+int attn_varlen_exp2_fma_host(const float* x, float* y, int64_t n);
+
+/*
  * Per-launch timing, for benchmarks. While enabled, every kernel the library
  * launches is bracketed by two HIP events recorded on the launch's stream (the
  * events belong to the library and are reused). attn_varlen_profile_enable(1)

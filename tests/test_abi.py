@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_error_strings():
-    assert A.attn_varlen_version() == (1, 4)
+    assert A.attn_varlen_version() == (1, 5)
     for name, code in header_enums().items():
         s = A.attn_varlen_error_string(code)
         assert s and s != "unknown error code", name
@@ -351,3 +351,16 @@ def test_schedule_host_random():
         bm = int(rng.choice([32, 64, 128]))
         cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
         assert A.attn_varlen_schedule_host(cu, bm) == brute_force_schedule(lengths, bm)
+
+
+@pytest.mark.parametrize("splits", [0, 2, 64])
+def test_persistent_rejects_split_counts(splits):
+    """The persistent scheduler runs the one-pass forward only: a split count
+    other than 1 (including 0, the library's choice, which may pick several) is
+    an error, raised before any tensor is looked at."""
+    import torch
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError, match="num_splits must be 1"):
+        A.attn_varlen_fwd(q, q, q, cu, cu, 4, 4, num_splits=splits, persistent=True)
+

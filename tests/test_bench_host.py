@@ -48,3 +48,10 @@ def test_oracle_table_lines(monkeypatch, capsys):
             # the full time is the config's work at the sample's rate
             assert r["oracle_fwd_s"] == pytest.approx(r["sample_fwd_s"] * fl / sample_fl)
             assert r["oracle_fwdbwd_s"] == pytest.approx(r["sample_fwdbwd_s"] * fl / sample_fl)
+
+
+def test_named_workloads_for_profiling():
+    assert bench.named_workload("2x16384-mha16-d64-full").backward is False
+    assert bench.named_workload("single-16384-gqa32/8-d128-full").head_dim == 128
+    with pytest.raises(SystemExit):
+        bench.named_workload("no-such-workload")

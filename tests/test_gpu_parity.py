@@ -1,12 +1,15 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle on
 the same seeded inputs, element by element, plus the bitwise and structural
 checks of the kernels. Tolerances are in tests/parity.py."""
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import exact_attention_varlen_amd as A
 import oracle.attention as O
+import oracle_pool as OP
 import workloads as W
 from parity import (announce, check_grad, check_lse, check_out, check_out_rounded, f64, gpu_bwd, gpu_fwd,
                     sample_rows, to_dev, window_of)
@@ -190,44 +193,96 @@ def test_splitkv_one_split_is_the_plain_call_and_deterministic():
 # full-size workloads
 # --------------------------------------------------------------------------
 
-def test_parity_single_4096_gqa_d128():
-    full_parity(W.a100_shape(4096))
+def pooled_parity(wl: W.Workload, backward: bool = True, lse_off_too: bool = False):
+    """Full-size GPU run in the bench's launch configuration; the whole output,
+    LSE and gradients compared element by element with the float64 oracle (run
+    per (sequence, query head) in host threads, tests/oracle_pool.py)."""
+    inp = W.make_inputs(wl, with_dout=backward)
+    d = to_dev(inp)
+    announce(f"fwd {wl.name} (full size, full tensors)")
+    out, lse = gpu_fwd(wl, d)
+    out_nolse = gpu_fwd(wl, d, return_lse=False) if lse_off_too else None
+    grads = None
+    if backward:
+        announce(f"bwd {wl.name} (full size, full tensors)")
+        grads = gpu_bwd(wl, d, out, lse)
+    torch.cuda.synchronize()
+    q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+    ref_o, ref_l = OP.forward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal,
+                              window=wl.window)
+    check_out(f64(out), ref_o)
+    check_lse(f64(lse), ref_l)
+    if out_nolse is not None:
+        check_out(f64(out_nolse), ref_o, "out (no LSE)")
+    if not backward:
+        return
+    do = W.to_f64(inp["dout"])
+    rq, rk, rv = OP.backward(q, k, v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.softmax_scale, wl.causal, do,
+                             window=wl.window)
+    for x, ref, name in zip(grads, (rq, rk, rv), ("dq", "dk", "dv")):
+        check_grad(f64(x), ref, name)
 
 
-def test_parity_packed16k_causal_d128():
-    full_parity(W.packed_16k())
+# Full tensors: the A100 issue's shape, the packed document batch, the head_dim
+# 64 pair with and without the LSE, every head_dim 256 batch of 32K tokens in
+# both masks, the single 16K sequence, and windowed variants.
+FULL_TENSOR = [
+    (W.a100_shape(4096), True, False),
+    (W.packed_16k(), True, False),
+    (W.hd64_mha(), False, True),
+    (W.hd256_gqa(8, 4096, False), True, False),
+    (W.hd256_gqa(8, 4096, True), True, False),
+    (W.hd256_gqa(2, 16384, False), True, False),
+    (W.hd256_gqa(2, 16384, True), True, False),
+    (W.hd256_gqa(1, 32768, False), True, False),
+    (W.hd256_gqa(1, 32768, True), True, False),
+    (W.single_16k_full(), True, False),
+    (W.Workload("single-4096-gqa32/8-d128-full-w512_512", [4096], 32, 8, 128, False, window=(512, 512)), True,
+     False),
+    (W.Workload("packed16k-docs-gqa32/8-d128-causal-w1024", list(W.PACKED_16K_DOC_LENGTHS), 32, 8, 128, True,
+                window=(1024, -1)), True, False),
+    (W.Workload("8x4096-gqa8/1-d256-causal-w1000", [4096] * 8, 8, 1, 256, True, window=(1000, -1)), True, False),
+]
 
 
-def sampled_parity(wl: W.Workload, dkdv_mode: str):
-    """Full-size GPU run; oracle on sampled rows (O, LSE, dQ; dK/dV per dkdv_mode)."""
-    inp = W.make_inputs(wl, with_dout=wl.backward)
+@pytest.mark.parametrize("wl,backward,lse_off", FULL_TENSOR, ids=[w.name for w, _, _ in FULL_TENSOR])
+def test_parity_full_size_full_tensors(wl, backward, lse_off):
+    pooled_parity(wl, backward, lse_off)
+
+
+def sampled_parity(wl: W.Workload):
+    """Sequences of 64K and more: the GPU runs the whole problem; the oracle checks
+    O, LSE and dQ on sampled query rows; dK and dV on the last 256 keys of each
+    causal sequence (cheap) and on stored rows (the first 256 keys, which every
+    query row sees, plus 64 random ones) written by tests/golden/make_dkdv_golden.py;
+    and the any-size sums of dK and dV."""
+    inp = W.make_inputs(wl, with_dout=True)
+    golden = np.load(GOLDEN_DKDV[wl.name])
+    assert str(golden["workload"]) == wl.name
+    assert str(golden["input_sha256"]) == W.inputs_sha256(inp), "stored dK/dV rows were made for other inputs"
     d = to_dev(inp)
     cu_q, cu_k = wl.cu_seqlens_q, wl.cu_seqlens_k
     announce(f"fwd {wl.name} (full size, sampled oracle)")
     out, lse = gpu_fwd(wl, d)
-    dq = dk = dv = None
-    if wl.backward:
-        announce(f"bwd {wl.name} (full size, sampled oracle)")
-        dq, dk, dv = gpu_bwd(wl, d, out, lse)
+    announce(f"bwd {wl.name} (full size, sampled oracle)")
+    dq, dk, dv = gpu_bwd(wl, d, out, lse)
     torch.cuda.synchronize()
-    q, k, v = (W.to_f64(inp[x]) for x in ("q", "k", "v"))
+    q, k, v, do = (W.to_f64(inp[x]) for x in ("q", "k", "v", "dout"))
     rows = sample_rows(cu_q, extra=64)
     r, ro, rl = O.forward_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, rows, window=wl.window)
     check_out(f64(out[torch.as_tensor(r)]), ro)
     check_lse(f64(lse[:, torch.as_tensor(r)]), rl)
-    if not wl.backward:
-        return
-    do = W.to_f64(inp["dout"])
     r, rdq = O.backward_dq_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, rows, window=wl.window)
     check_grad(f64(dq[torch.as_tensor(r)]), rdq, "dq(sampled rows)")
-    if dkdv_mode in ("tail", "spread"):
-        krows = sample_rows(cu_k, extra=32, tail_only=(dkdv_mode == "tail"))
-        if dkdv_mode == "spread":  # keep the oracle cost bounded: keys of the first two sequences only
-            krows = krows[krows < cu_k[min(2, len(cu_k) - 1)]]
-        r, rdk, rdv = O.backward_dkdv_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, krows,
-                                           window=wl.window)
-        check_grad(f64(dk[torch.as_tensor(r)]), rdk, "dk(sampled rows)")
-        check_grad(f64(dv[torch.as_tensor(r)]), rdv, "dv(sampled rows)")
+    if wl.causal:
+        krows = sample_rows(cu_k, extra=32, tail_only=True)
+        r, rdk, rdv = OP.backward_dkdv_rows(q, k, v, cu_q, cu_k, wl.softmax_scale, wl.causal, do, krows,
+                                            window=wl.window)
+        check_grad(f64(dk[torch.as_tensor(r)]), rdk, "dk(last keys)")
+        check_grad(f64(dv[torch.as_tensor(r)]), rdv, "dv(last keys)")
+    gr = torch.as_tensor(golden["key_rows"])
+    check_grad(f64(dk[gr]), golden["dk"].astype(np.float64), "dk(stored rows)")
+    check_grad(f64(dv[gr]), golden["dv"].astype(np.float64), "dv(stored rows)")
     check_gradient_sums(wl, d, dk, dv)
 
 
@@ -256,28 +311,18 @@ def check_gradient_sums(wl, d, dk, dv):
             assert float((sv - want).norm() / (scale_v * sv.numel() ** 0.5 + 1e-30)) < 0.05, "sum of dV mismatch"
 
 
-FULL_SIZE = [
-    (W.long_65k(), "tail"),
-    (W.hd64_mha(), "none"),
-    (W.hd256_gqa(8, 4096, False), "spread"),
-    (W.hd256_gqa(8, 4096, True), "tail"),
-    (W.hd256_gqa(2, 16384, False), "none"),
-    (W.hd256_gqa(2, 16384, True), "tail"),
-    (W.hd256_gqa(1, 32768, False), "none"),
-    (W.hd256_gqa(1, 32768, True), "tail"),
-    (W.hd256_gqa(1, 131072, False), "none"),
-    (W.hd256_gqa(1, 131072, True), "tail"),
-    (W.single_16k_full(), "none"),
-    (W.Workload("single-4096-gqa32/8-d128-full-w512_512", [4096], 32, 8, 128, False, window=(512, 512)), "spread"),
-    (W.Workload("packed16k-docs-gqa32/8-d128-causal-w1024", list(W.PACKED_16K_DOC_LENGTHS), 32, 8, 128, True,
-                window=(1024, -1)), "tail"),
-    (W.Workload("8x4096-gqa8/1-d256-causal-w1000", [4096] * 8, 8, 1, 256, True, window=(1000, -1)), "tail"),
-]
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+GOLDEN_DKDV = {
+    W.long_65k().name: os.path.join(GOLDEN_DIR, "dkdv_single-65536-gqa32-8-d128-causal.npz"),
+    W.hd256_gqa(1, 131072, False).name: os.path.join(GOLDEN_DIR, "dkdv_1x131072-gqa8-1-d256-full.npz"),
+    W.hd256_gqa(1, 131072, True).name: os.path.join(GOLDEN_DIR, "dkdv_1x131072-gqa8-1-d256-causal.npz"),
+}
+SAMPLED = [W.long_65k(), W.hd256_gqa(1, 131072, False), W.hd256_gqa(1, 131072, True)]
 
 
-@pytest.mark.parametrize("wl,mode", FULL_SIZE, ids=[w.name for w, _ in FULL_SIZE])
-def test_parity_full_size_sampled(wl, mode):
-    sampled_parity(wl, mode)
+@pytest.mark.parametrize("wl", SAMPLED, ids=[w.name for w in SAMPLED])
+def test_parity_full_size_sampled(wl):
+    sampled_parity(wl)
 
 
 # query chunks against long keys (few items per launch): the split-KV forward
@@ -414,19 +459,27 @@ def test_no_writes_outside_outputs():
     assert torch.all(torch.isneginf(lse[:, 130:]))
 
 
-@pytest.mark.parametrize("lengths,bm", [
-    ([200, 312], 128),
-    (W.PACKED_16K_DOC_LENGTHS, 128),
-    ([0, 5, 0, 130, 1, 128, 129, 0], 64),
-    ([131072], 128),
-    (list(range(0, 9000, 97)), 128),
+# The device decode searches the block levels (ceil(max_seqlen_q / bm) of them)
+# 64 at a time; more than 4096 levels take further narrowing passes: long
+# sequences, and inflated max_seqlen bounds over short ones.
+@pytest.mark.parametrize("lengths,bm,max_q", [
+    ([200, 312], 128, None),
+    (W.PACKED_16K_DOC_LENGTHS, 128, None),
+    ([0, 5, 0, 130, 1, 128, 129, 0], 64, None),
+    ([131072], 128, None),
+    (list(range(0, 9000, 97)), 128, None),
+    ([600000], 128, None),
+    ([9000, 100], 128, 600000),
+    ([3, 0, 700000, 5], 64, 2000000),
+    ([600000, 1, 4096], 32, None),
 ])
-def test_device_schedule_matches_host(lengths, bm):
+def test_device_schedule_matches_host(lengths, bm, max_q):
     cu = W.cu_from_lengths(lengths)
     host = A.attn_varlen_schedule_host(cu, bm)
-    announce(f"schedule decode {len(lengths)} seqs bm={bm}")
+    max_q = max(lengths) if max_q is None else max_q
+    announce(f"schedule decode {len(lengths)} seqs bm={bm} max_seqlen_q={max_q}")
     cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda:0")
-    seq, blk = A.attn_varlen_schedule_device(cu_d, max(lengths), bm, len(host) + 5)
+    seq, blk = A.attn_varlen_schedule_device(cu_d, max_q, bm, len(host) + 5)
     torch.cuda.synchronize()
     seq, blk = seq.cpu().tolist(), blk.cpu().tolist()
     assert list(zip(seq[:len(host)], blk[:len(host)])) == host

@@ -136,6 +136,40 @@ def check_row_sums(mod, causal):
                 assert np.all(np.triu(p, 1) == 0)
 
 
+def check_probabilities(mod, causal, window=None):
+    """The attention matrix against torch's float64 softmax of the masked,
+    scaled scores (K/V heads repeated with repeat_interleave; the mask built
+    from tril/triu at the bottom-right diagonal), and P V against the forward's
+    output and log-sum-exp of the same scores against its LSE."""
+    q, k, v, do, cu_q, cu_k = rand_problem([9, 14, 5], 6, 2, 8, seed=21, seqlens_k=[12, 14, 3])
+    scale = 0.6
+    out, lse = mod.forward(q, k, v, cu_q, cu_k, scale, causal, window=window)
+    kr = torch.tensor(k).repeat_interleave(3, dim=1)
+    vr = torch.tensor(v).repeat_interleave(3, dim=1)
+    for b in range(3):
+        Lq, Lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        ones = torch.ones(Lq, Lk, dtype=torch.bool)
+        keep = ones.clone()
+        if causal:
+            keep &= torch.tril(ones, diagonal=Lk - Lq)
+        if window is not None and window[1] >= 0:
+            keep &= torch.tril(ones, diagonal=Lk - Lq + window[1])
+        if window is not None and window[0] >= 0:
+            keep &= torch.triu(ones, diagonal=Lk - Lq - window[0])
+        for h in range(6):
+            qh = torch.tensor(q[cu_q[b]:cu_q[b + 1], h])
+            kh = kr[cu_k[b]:cu_k[b + 1], h]
+            s = (qh @ kh.T) * scale
+            s = s.masked_fill(~keep, float("-inf"))
+            want = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0).numpy()
+            p = mod.probabilities(q, k, cu_q, cu_k, scale, causal, b, h, window=window)
+            np.testing.assert_allclose(p, want, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(p @ vr[cu_k[b]:cu_k[b + 1], h].numpy(), out[cu_q[b]:cu_q[b + 1], h],
+                                       rtol=0, atol=1e-13)
+            np.testing.assert_allclose(torch.logsumexp(s, dim=-1).numpy(), lse[h, cu_q[b]:cu_q[b + 1]],
+                                       rtol=0, atol=1e-13)
+
+
 def sdpa_reference(q, k, v, cu_q, cu_k, scale, causal, Hq, Hkv, requires_grad=False):
     """Per-sequence torch float64 SDPA with the library's own GQA grouping."""
     outs, lses, leaves = [], [], []
@@ -419,6 +453,19 @@ def test_permutation_equivariance():
 @pytest.mark.parametrize("causal", [False, True])
 def test_row_sums(causal):
     check_row_sums(O, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [None, (3, 1), (0, -1), (-1, 2)])
+def test_probabilities_against_torch_softmax(causal, window):
+    check_probabilities(O, causal, window)
+
+
+def test_mutation_probabilities_scale_and_grouping_are_caught():
+    def unscaled(q, k, cu_q, cu_k, scale, causal, b, h, window=None):
+        return O.probabilities(q, k, cu_q, cu_k, 1.0, causal, b, h, window=window)
+    assert _fails(check_probabilities, _mutant(probabilities=unscaled), False)
+    assert _fails(check_probabilities, _mutant(kv_head_of=lambda h, hq, hkv: h % hkv), True)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -38,3 +38,25 @@ def test_check_out_rounded_accepts_rounding_and_rejects_more():
     worse[3, 2, 1] += 0.04
     with pytest.raises(AssertionError):
         check_out_rounded(worse, ref)
+
+
+def test_gradient_column_check_catches_a_few_bad_columns():
+    """Errors confined to 4 of 256 head-dim columns (the footprint of a stale
+    accumulator register) stay under the whole-tensor bound but fail the
+    per-column one; spread-out rounding-sized errors pass both."""
+    import pytest
+    from parity import GRAD_REL_FRO, check_grad, rel_fro
+
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((300, 2, 256))
+    noisy = ref * (1 + 3e-3 * rng.standard_normal(ref.shape))
+    check_grad(noisy, ref, "spread")
+    bad = noisy.copy()
+    bad[..., [250, 251, 254, 255]] *= 1.15
+    assert rel_fro(bad, ref) <= GRAD_REL_FRO
+    with pytest.raises(AssertionError, match="head-dim column 25"):
+        check_grad(bad, ref, "columns")
+    # an exactly-zero tensor must come out zero up to rounding
+    with pytest.raises(AssertionError, match="exactly zero"):
+        check_grad(np.full((3, 1, 64), 1e-3), np.zeros((3, 1, 64)), "zero tensor")
+    check_grad(np.full((3, 1, 64), 1e-7), np.zeros((3, 1, 64)), "zero tensor, rounding only")

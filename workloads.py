@@ -158,6 +158,21 @@ def make_inputs(wl: Workload, with_dout: bool = True, seed: Optional[int] = None
     return out
 
 
+def inputs_sha256(inp) -> str:
+    """Checksum of a workload's drawn inputs (q, k, v, dout and the packing), so
+    that values stored for them can be checked against the inputs in use."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("cu_seqlens_q", "cu_seqlens_k", "q", "k", "v", "dout"):
+        if name in inp:
+            t = inp[name].contiguous()
+            h.update(name.encode())
+            h.update(str(tuple(t.shape)).encode())
+            h.update(t.view(torch.int16).numpy().tobytes() if t.dtype == torch.bfloat16 else t.numpy().tobytes())
+    return h.hexdigest()
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact bf16 -> float64 numpy conversion."""
     return t.to(torch.float64).numpy()
