@@ -36,6 +36,8 @@ __all__ = [
     "attn_varlen_fwd_window",
     "attn_varlen_bwd_window",
     "attn_varlen_bwd_workspace_size",
+    "attn_varlen_bwd_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "attn_varlen_fwd_splitkv",
     "attn_varlen_fwd_splitkv_workspace_size",
     "attn_varlen_fwd_num_splits",
@@ -299,6 +301,47 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
                                       workspace.numel() * workspace.element_size(), _stream(dev))
     if rc != 0:
         raise AttnVarlenError(rc, "attn_varlen_bwd_window")
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_VARLEN_NOALLOC_SCRATCH_BYTES
+
+
+def attn_varlen_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            out: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                            cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                            softmax_scale: Optional[float] = None, causal: bool = False,
+                            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                            dv: Optional[torch.Tensor] = None):
+    """``attn_varlen_bwd`` through the allocation-free C entry point: the library's
+    static device scratch holds the workspace (calls on one GPU must not overlap).
+    Pass ``dq``, ``dk``, ``dv`` to allocate nothing here either."""
+    dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _check_bf16("dout", dout, dev)
+    _check_bf16("out", out, dev)
+    if dout.shape != q.shape or out.shape != q.shape:
+        raise ValueError("dout and out must have the shape of q")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, _ = k.shape
+    if lse.dtype != torch.float32 or lse.shape != (Hq, total_q) or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError(f"lse must be contiguous float32 ({Hq}, {total_q}) on {dev}")
+    if softmax_scale is None:
+        softmax_scale = D ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_bf16(n, t, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
+    num_seqs = cu_seqlens_q.numel() - 1
+    _maybe_validate(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)
+    rc = lib().attn_varlen_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
+                                       total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
+                                       float(softmax_scale), int(bool(causal)), _ptr(dout), _ptr(out), _ptr(lse),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _stream(dev))
+    if rc != 0:
+        raise AttnVarlenError(rc, "attn_varlen_bwd_noalloc")
     return dq, dk, dv
 
 

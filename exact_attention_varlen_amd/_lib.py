@@ -45,6 +45,9 @@ _SIGNATURES = {
     "attn_varlen_bwd_workspace_size": (c_size, [c_i32, c_i64, c_i64, c_i32, c_i32, c_i32]),
     "attn_varlen_bwd": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
                                        c_i32, c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "attn_varlen_bwd_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                               c_i32, c_i32, c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                               c_vp]),
     "attn_varlen_validate_seqlens": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "attn_varlen_error_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_varlen_version": (ctypes.c_int, []),

@@ -84,7 +84,7 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
                 int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
                 int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
                 const void* dout, const void* out, const float* lse, void* dq, void* dk, void* dv,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, bool static_scratch, void* stream) {
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
@@ -94,9 +94,16 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
       !aligned(lse, 4))
     return ATTN_VARLEN_ERR_MISALIGNED;
   const size_t need = av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_VARLEN_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
+  if (static_scratch) {
+    if (need > av::noalloc_scratch_bytes()) return ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL;
+  } else {
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_VARLEN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
+  }
   if (total_q == 0 && total_k == 0) return ATTN_VARLEN_OK;
+  if (static_scratch && need > 0) {
+    if (av::noalloc_scratch(&workspace) != hipSuccess) return ATTN_VARLEN_ERR_HIP;
+  }
   av::BwdArgs a;
   a.f = make_fwd_args(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                       n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, stream);
@@ -222,7 +229,7 @@ int attn_varlen_bwd_window(const void* q, const void* k, const void* v, const in
                            void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_checked(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, dout, out, lse,
-                     dq, dk, dv, workspace, workspace_bytes, stream);
+                     dq, dk, dv, workspace, workspace_bytes, false, stream);
 }
 
 int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -234,6 +241,16 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* 
   return attn_varlen_bwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q,
                                 max_seqlen_k, n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, -1, -1, dout,
                                 out, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+int attn_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, float softmax_scale, int32_t causal, const void* dout,
+                            const void* out, const float* lse, void* dq, void* dk, void* dv, void* stream) {
+  return bwd_checked(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                     n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, -1, -1, dout, out, lse, dq, dk, dv,
+                     nullptr, 0, true, stream);
 }
 
 int attn_varlen_validate_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
@@ -268,6 +285,8 @@ const char* attn_varlen_error_string(int code) {
     case ATTN_VARLEN_ERR_BAD_FLAG: return "causal must be 0 or 1";
     case ATTN_VARLEN_ERR_HIP: return "HIP runtime error at kernel launch";
     case ATTN_VARLEN_ERR_BAD_SPLITS: return "num_splits must be in [1, ATTN_VARLEN_MAX_SPLITS]";
+    case ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL:
+      return "the problem needs more workspace than the static scratch of the allocation-free call holds";
     default: return "unknown error code";
   }
 }

@@ -105,6 +105,10 @@ constexpr int kSchedWords = 9;
 hipError_t launch_fwd_persistent(const FwdArgs& a, void* sched);
 int fwd_num_splits(int num_seqs, int64_t total_q, int max_q, int max_k, int Hq, int Hkv, int D);
 hipError_t launch_bwd(const BwdArgs& a);
+// The allocation-free backward's device scratch (av_noalloc.hip): its size, and
+// its address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_schedule_probe(const int32_t* cu_q, int num_seqs, int max_q, int block_m, int32_t* seq_out,
                                  int32_t* block_out, int count, void* stream);
 

@@ -75,7 +75,9 @@ enum {
   ATTN_VARLEN_ERR_WORKSPACE = -7,         /* workspace NULL or smaller than the size its call needs */
   ATTN_VARLEN_ERR_BAD_FLAG = -8,          /* causal not 0 or 1 */
   ATTN_VARLEN_ERR_HIP = -9,               /* the HIP runtime reported an error at launch */
-  ATTN_VARLEN_ERR_BAD_SPLITS = -10        /* num_splits outside [1, ATTN_VARLEN_MAX_SPLITS] */
+  ATTN_VARLEN_ERR_BAD_SPLITS = -10,       /* num_splits outside [1, ATTN_VARLEN_MAX_SPLITS] */
+  ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL = -11 /* attn_varlen_bwd_noalloc: the problem's workspace exceeds
+                                             ATTN_VARLEN_NOALLOC_SCRATCH_BYTES */
 };
 
 #define ATTN_VARLEN_MAX_SPLITS 64
@@ -274,6 +276,40 @@ int attn_varlen_bwd_window(const void* q, const void* k, const void* v,
                            const void* dout, const void* out, const float* lse,
                            void* dq, void* dk, void* dv,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The same computation, arguments and results as attn_varlen_bwd
+ * (bit-identical: the same kernels), without the workspace arguments: the
+ * workspace lives in a device array inside the library,
+ * ATTN_VARLEN_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which each GPU the
+ * library runs on holds until the process ends. The call allocates nothing and
+ * frees nothing; the caller still passes every input and output.
+ *   Limit: problems whose workspace (attn_varlen_bwd_workspace_size) exceeds
+ *   the scratch are rejected with ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL before any
+ *   HIP call. The row terms take 8 bytes per (query row, query head), so up to
+ *   4M query row-heads (e.g. 32 heads x 128K tokens) fit at head_dim 64 / 128;
+ *   at head_dim 256 the partial dK / dV sums of problems with few key blocks per
+ *   KV head also count.
+ *   Sharing: every call on one GPU uses that GPU's one scratch array, which keeps
+ *   the last call's contents (nothing in it needs to start at zero). Calls on
+ *   one GPU must therefore not overlap: calls on different streams, or from
+ *   several host threads, that may run at the same time race on the scratch.
+ *   Calls ordered on one stream are fine.
+ * Errors: those of attn_varlen_bwd except ATTN_VARLEN_ERR_WORKSPACE, plus
+ * ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL, and ATTN_VARLEN_ERR_HIP if the scratch's
+ * device address cannot be looked up.
+ */
+#define ATTN_VARLEN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_varlen_bwd_noalloc(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t num_seqs, int64_t total_q, int64_t total_k,
+                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            float softmax_scale, int32_t causal,
+                            const void* dout, const void* out, const float* lse,
+                            void* dq, void* dk, void* dv, void* stream);
 
 /* Static description of an error code. Never NULL. */
 const char* attn_varlen_error_string(int code);

@@ -364,3 +364,35 @@ def test_persistent_rejects_split_counts(splits):
     with pytest.raises(ValueError, match="num_splits must be 1"):
         A.attn_varlen_fwd(q, q, q, cu, cu, 4, 4, num_splits=splits, persistent=True)
 
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_VARLEN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == A.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("Hq,total,D,ok", [
+    (32, 131072, 128, True),     # row terms 2 x 32 x 131072 x 4 B = 32 MiB: fits exactly
+    (32, 131073, 128, False),    # one row more does not
+    (8, 32768, 256, False),      # head_dim 256 with few key blocks: partial dK / dV sums too
+])
+def test_noalloc_rejects_problems_beyond_the_scratch(Hq, total, D, ok):
+    """The allocation-free backward checks its workspace need against the static
+    scratch before any HIP call (no GPU needed to see the rejection)."""
+    l = _lib.lib()
+    need = A.attn_varlen_bwd_workspace_size(1, total, total, Hq, 1 if D == 256 else 8, D)
+    assert (need <= A.NOALLOC_SCRATCH_BYTES) == ok
+    if ok:
+        return  # a fitting problem would launch kernels
+    rc = l.attn_varlen_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, total, total, total, total, Hq,
+                                   1 if D == 256 else 8, D, 0.1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == E["ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL"]
+    assert "static scratch" in A.attn_varlen_error_string(rc)
+
+
+def test_noalloc_argument_errors_come_first():
+    l = _lib.lib()
+    assert l.attn_varlen_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 64, 4, 2, 96, 0.1, 0, FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, None) == E["ATTN_VARLEN_ERR_BAD_HEAD_DIM"]
+    assert l.attn_varlen_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 64, 4, 2, 64, 0.1, 0, None,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, None) == E["ATTN_VARLEN_ERR_NULL_POINTER"]

@@ -1,0 +1,36 @@
+"""The allocation-free backward (attn_varlen_bwd_noalloc, static device scratch)
+against the allocating one (attn_varlen_bwd) through the C ABI: bit-identical
+gradients, over calls in a row on one GPU whose problems shrink, so that each
+call finds the previous call's contents in the scratch."""
+import pytest
+import torch
+
+import exact_attention_varlen_amd as A
+import workloads as W
+from parity import announce, gpu_fwd, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CALLS = [
+    W.Workload("noalloc-d128-c", [700, 33, 1200, 0, 400], 8, 2, 128, True),
+    W.Workload("noalloc-d256-gqa-f", [300, 190], 8, 1, 256, False),  # partial dK / dV sums in the scratch
+    W.Workload("noalloc-d64-f", [150, 77], 4, 4, 64, False),
+]
+
+
+def test_noalloc_backward_matches_the_allocating_one():
+    for wl in CALLS:
+        need = A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k, wl.n_q_heads,
+                                                wl.n_kv_heads, wl.head_dim)
+        assert 0 < need <= A.NOALLOC_SCRATCH_BYTES
+        d = to_dev(W.make_inputs(wl))
+        announce(f"noalloc backward {wl.name}")
+        out, lse = gpu_fwd(wl, d)
+        ref = A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
+        got = A.attn_varlen_bwd_noalloc(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"],
+                                        d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale,
+                                        wl.causal)
+        torch.cuda.synchronize()
+        for a, b, name in zip(got, ref, ("dq", "dk", "dv")):
+            assert torch.equal(a, b), f"{wl.name}: {name} differs from attn_varlen_bwd"
