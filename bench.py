@@ -67,29 +67,33 @@ def warm_gpu(min_s: float = 0.5, max_s: float = 3.0, tol: float = 0.02):
 def kernel_flop(name: str, wl) -> float:
     """Algorithmic flop of one launch of the named kernel (MFMA work it must do)."""
     pairs = sum(a * b for a, b in zip(wl.seqlens_q, wl.seqlens_k)) * (0.5 if wl.causal else 1.0)
-    per_pair = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6}.get(name)
+    per_pair = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6, "attn_bwd_dq_ds": 2}.get(name)
     if per_pair is None:
         return 0.0
     return per_pair * pairs * wl.n_q_heads * wl.head_dim
 
 
-def kernel_bytes(name: str, wl) -> float:
-    """Algorithmic HBM bytes of one launch (each tensor read or written once)."""
+def kernel_bytes(name: str, wl, stored_ds: bool = False) -> float:
+    """Algorithmic HBM bytes of one launch (each tensor read or written once; the
+    stored dS, bf16 per visible (query, key) pair and query head, written by dK / dV
+    and read by the stored-dS dQ kernel)."""
     tq, tk, hq, hkv, d = wl.total_q, wl.total_k, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
     q = 2 * tq * hq * d
     kv = 2 * tk * hkv * d
     rows = 4 * tq * hq
+    ds = 2 * sum(a * b for a, b in zip(wl.seqlens_q, wl.seqlens_k)) * (0.5 if wl.causal else 1.0) * hq
     return {
         "attn_fwd": q + 2 * kv + q + rows,
         "attn_bwd_prep": 2 * q + 3 * rows,
-        "attn_bwd_dkdv": 2 * q + 2 * kv + 2 * rows + 2 * kv,
+        "attn_bwd_dkdv": 2 * q + 2 * kv + 2 * rows + 2 * kv + (ds if stored_ds else 0),
         "attn_bwd_dq": 2 * q + 2 * kv + 2 * rows + q,
+        "attn_bwd_dq_ds": ds + kv + q,
     }.get(name, 0.0)
 
 
 # library event name -> kernel symbol stem used in the profiler summaries
 KERNEL_SYMBOL = {"attn_fwd": "fwd_kernel", "attn_bwd_prep": "bwd_prep_kernel", "attn_bwd_dkdv": "bwd_dkdv_kernel",
-                 "attn_bwd_dq": "bwd_dq_kernel"}
+                 "attn_bwd_dq": "bwd_dq_kernel", "attn_bwd_dq_ds": "bwd_dq_ds_kernel"}
 
 
 def measured_traffic(kernel: str, workload_tag: str):
@@ -321,7 +325,16 @@ def lse_ratio(wl, rounds: int = 5, reps: int = 10):
             "no_lse_tflops": fl / (no * 1e-3) / 1e12, "with_lse_tflops": fl / (wi * 1e-3) / 1e12}
 
 
-def run_workload(wl, steps, warmup, profile=True):
+def bwd_ws_bytes(wl, stored_ds=False) -> int:
+    """Backward workspace for a workload: the recomputing backward's, or the
+    stored-dS one's (attn_varlen_bwd_stored_ds)."""
+    import exact_attention_varlen_amd as A
+
+    return A.bwd_workspace_bytes(len(wl.seqlens_q), wl.total_q, wl.total_k, wl.max_seqlen_q, wl.max_seqlen_k,
+                                 wl.n_q_heads, wl.n_kv_heads, wl.head_dim, stored_ds)
+
+
+def run_workload(wl, steps, warmup, profile=True, stored_ds=False):
     import torch
 
     import exact_attention_varlen_amd as A
@@ -335,9 +348,7 @@ def run_workload(wl, steps, warmup, profile=True):
     dq = torch.empty_like(d["q"])
     dk = torch.empty_like(d["k"])
     dv = torch.empty_like(d["v"])
-    ws = torch.empty(max(16, A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k,
-                                                              wl.n_q_heads, wl.n_kv_heads, wl.head_dim)),
-                     dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(max(16, bwd_ws_bytes(wl, stored_ds)), dtype=torch.uint8, device="cuda:0")
 
     def fwd():
         A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk, wl.softmax_scale,
@@ -346,9 +357,10 @@ def run_workload(wl, steps, warmup, profile=True):
     def step():
         fwd()
         A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
-                          wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+                          wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws, stored_ds=stored_ds)
 
     res = {}
+    res["stored_ds"] = bool(stored_ds)
     fwd_flop = wl.accounted_fwd_flop()
     # 1) eager calls with per-launch event timing inside the library
     if profile:
@@ -555,9 +567,7 @@ def window_split_secondary():
             row[key + "_tflops"] = flop / (ms * 1e-3) / 1e12
         if kind == "window":
             dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-            wsb = torch.empty(max(16, A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k,
-                                                                       wl.n_q_heads, wl.n_kv_heads, wl.head_dim)),
-                              dtype=torch.uint8, device="cuda:0")
+            wsb = torch.empty(max(16, bwd_ws_bytes(wl)), dtype=torch.uint8, device="cuda:0")
 
             def step():
                 A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
@@ -573,6 +583,53 @@ def window_split_secondary():
         del d, out, lse
         torch.cuda.empty_cache()
     return out_rows
+
+
+def bwd_paths(wl, rounds: int = 3):
+    """The step (forward with LSE + backward) with dS stored for dQ against the
+    recomputing dQ, steady state, alternating rounds, with per-kernel times of
+    eager steps for each."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+    mq, mk = wl.max_seqlen_q, wl.max_seqlen_k
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    ws = {s: torch.empty(max(16, bwd_ws_bytes(wl, s)), dtype=torch.uint8, device="cuda:0") for s in (True, False)}
+
+    def step(s):
+        def f():
+            A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk, wl.softmax_scale,
+                              wl.causal, out=out, lse=lse)
+            A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                              mq, mk, wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws[s], stored_ds=s)
+        return f
+
+    times = {True: [], False: []}
+    for _ in range(rounds):
+        for s in (True, False):
+            times[s].append(time_graph_steady(step(s), 5, 1))
+    row = {"workload": wl.name}
+    for s, tag in ((True, "stored_ds"), (False, "recompute")):
+        A.attn_varlen_profile_enable(True)
+        for _ in range(3):
+            step(s)()
+        torch.cuda.synchronize()
+        A.attn_varlen_profile_enable(False)
+        recs = A.attn_varlen_profile_records()
+        per = {}
+        for name, ms in recs[len(recs) // 3:]:
+            per.setdefault(name, []).append(ms)
+        ms = statistics.median(times[s])
+        row[tag] = {"step_ms": ms, "fwdbwd_tflops": wl.accounted_fwdbwd_flop() / (ms * 1e-3) / 1e12,
+                    "kernels_ms": {k: sum(v) / len(v) for k, v in per.items()},
+                    "workspace_bytes": ws[s].numel()}
+    row["stored_ds_speedup"] = row["recompute"]["step_ms"] / row["stored_ds"]["step_ms"]
+    return row
 
 
 def persistent_vs_grid(wl, rounds: int = 3):
@@ -701,9 +758,7 @@ def all_configs_table(include_long: bool):
         out = torch.empty_like(d["q"])
         lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
         dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-        ws = torch.empty(max(16, A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k,
-                                                                  wl.n_q_heads, wl.n_kv_heads, wl.head_dim)),
-                         dtype=torch.uint8, device="cuda:0")
+        ws = torch.empty(max(16, bwd_ws_bytes(wl)), dtype=torch.uint8, device="cuda:0")
 
         def fwd():
             A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk,
@@ -787,6 +842,9 @@ def main(argv=None):
     ap.add_argument("--oracle-table", action="store_true",
                     help="only time the float64 oracle (forward, forward+backward) for every config, whole or on a "
                          "bounded sample with an extrapolated full time (one JSON line each) and exit")
+    ap.add_argument("--bwd-paths", action="store_true",
+                    help="only time the step with dS stored for dQ against the recomputing dQ on workloads of "
+                         "every head dim <= 128 (one JSON line each) and exit")
     ap.add_argument("--fwd-table", action="store_true",
                     help="only time the forward (with and without the LSE) of one workload per head dim for the "
                          "loaded library build (one JSON line) and exit")
@@ -814,6 +872,16 @@ def main(argv=None):
     if a.fwd_table:
         warm_gpu()
         return fwd_table()
+    if a.bwd_paths:
+        warm_gpu()
+        for wl in (W.packed_16k(), W.a100_shape(4096), W.single_16k_full(),
+                   W.Workload("packed16k-docs-gqa32/8-d64-causal", list(W.PACKED_16K_DOC_LENGTHS), 32, 8, 64, True),
+                   W.Workload("2x16384-mha16-d64-full-bwd", [16384, 16384], 16, 16, 64, False),
+                   W.Workload("packed16k-docs-gqa32/8-d128-full", list(W.PACKED_16K_DOC_LENGTHS), 32, 8, 128,
+                              False)):
+            log(f"backward paths {wl.name}")
+            print(json.dumps(bwd_paths(wl)), flush=True)
+        return 0
     if a.window_split:
         warm_gpu()
         print(json.dumps(window_split_secondary()), flush=True)
@@ -841,6 +909,8 @@ def main(argv=None):
         secondary["lse_ratio"] = lse_ratio(W.hd64_mha())
         secondary["window_and_split_kv"] = window_split_secondary()
         secondary["persistent_scheduler"] = persistent_vs_grid(primary)
+        log("backward with stored dS against the recomputing dQ")
+        secondary["backward_paths"] = {wl.name: bwd_paths(wl) for wl in (primary, W.single_16k_full())}
     log("sustained clocks and power of the primary step")
     clocks = power_phase(res.pop("_step_fn"))
     log("reference GEMM rate")
@@ -866,7 +936,7 @@ def main(argv=None):
     for k, v in kern.items():
         f = kernel_flop(k, primary)
         v["tflops"] = f / (v["avg_ms"] * 1e-3) / 1e12 if f else None
-        v["gbs"] = kernel_bytes(k, primary) / (v["avg_ms"] * 1e-3) / 1e9
+        v["gbs"] = kernel_bytes(k, primary, res["stored_ds"]) / (v["avg_ms"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": res["fwdbwd_tflops"],
@@ -880,7 +950,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": primary.name, **primary.describe(), "pass": "fwd (with LSE) + bwd"},
+        "config": {"workload": primary.name, **primary.describe(), "pass": "fwd (with LSE) + bwd",
+                   "backward": "dS stored for dQ" if res["stored_ds"] else "dQ recomputes S, P, dP"},
         "fwd_tflops": res["fwd_tflops"],
         "fwd_ms": res["fwd_ms"],
         "fwd_timing": ("fwd_ms / fwd_tflops (the forward figure, against which the forward share of the peak "

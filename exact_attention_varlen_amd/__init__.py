@@ -36,6 +36,9 @@ __all__ = [
     "attn_varlen_fwd_window",
     "attn_varlen_bwd_window",
     "attn_varlen_bwd_workspace_size",
+    "attn_varlen_bwd_ds_workspace_size",
+    "bwd_workspace_bytes",
+    "attn_varlen_bwd_stored_ds",
     "attn_varlen_bwd_noalloc",
     "NOALLOC_SCRATCH_BYTES",
     "attn_varlen_fwd_splitkv",
@@ -252,15 +255,39 @@ def attn_varlen_bwd_workspace_size(num_seqs: int, total_q: int, total_k: int, n_
     return int(lib().attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, n_q_heads, n_kv_heads, head_dim))
 
 
+def attn_varlen_bwd_ds_workspace_size(num_seqs: int, total_q: int, total_k: int, max_seqlen_q: int,
+                                      max_seqlen_k: int, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    """Workspace bytes with which the backward stores dS for dQ (0: not available)."""
+    return int(lib().attn_varlen_bwd_ds_workspace_size(num_seqs, total_q, total_k, int(max_seqlen_q),
+                                                       int(max_seqlen_k), n_q_heads, n_kv_heads, head_dim))
+
+
+def bwd_workspace_bytes(num_seqs: int, total_q: int, total_k: int, max_seqlen_q: int, max_seqlen_k: int,
+                        n_q_heads: int, n_kv_heads: int, head_dim: int, stored_ds: bool = False) -> int:
+    """Workspace bytes of the backward: the recomputing one's, or with ``stored_ds``
+    the stored-dS one's (``attn_varlen_bwd_stored_ds``)."""
+    if stored_ds:
+        ds = attn_varlen_bwd_ds_workspace_size(num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k, n_q_heads,
+                                               n_kv_heads, head_dim)
+        if ds == 0 and total_q > 0 and total_k > 0:
+            raise ValueError("the stored-dS backward is not available for this problem")
+        if ds:
+            return ds
+    return attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, n_q_heads, n_kv_heads, head_dim)
+
+
 def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                     lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                     max_seqlen_k: int, softmax_scale: Optional[float] = None, causal: bool = False,
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                     dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                    window_size: Tuple[int, int] = (-1, -1)):
+                    window_size: Tuple[int, int] = (-1, -1), stored_ds: bool = False):
     """Backward pass: returns ``(dq, dk, dv)`` for the loss ``sum(dout * out)``.
 
-    ``window_size`` must be the forward's (``attn_varlen_bwd_window``)."""
+    ``window_size`` must be the forward's (``attn_varlen_bwd_window``).
+    ``stored_ds=True`` runs ``attn_varlen_bwd_stored_ds`` (dS written by the
+    dK / dV kernel and read by dQ instead of recomputed; head dims 64 / 128,
+    slower on MI355X at every measured shape)."""
     dev = _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
     _check_bf16("dout", dout, dev)
     _check_bf16("out", out, dev)
@@ -281,24 +308,33 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
             raise ValueError(f"{n} must have shape {tuple(ref.shape)}")
     num_seqs = cu_seqlens_q.numel() - 1
     _maybe_validate(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)
-    ws_bytes = attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, Hq, Hkv, D)
     if workspace is None:
+        ws_bytes = bwd_workspace_bytes(num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hkv, D, stored_ds)
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_given = workspace.numel() * workspace.element_size()
     wl, wr = (int(window_size[0]), int(window_size[1]))
+    if stored_ds:
+        rc = lib().attn_varlen_bwd_stored_ds(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                             num_seqs, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq,
+                                             Hkv, D, float(softmax_scale), int(bool(causal)), wl, wr, _ptr(dout),
+                                             _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                             ws_given, _stream(dev))
+        if rc != 0:
+            raise AttnVarlenError(rc, "attn_varlen_bwd_stored_ds")
+        return dq, dk, dv
     if wl < 0 and wr < 0:  # no window: the plain entry point
         rc = lib().attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
                                    total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
                                    float(softmax_scale), int(bool(causal)), _ptr(dout), _ptr(out), _ptr(lse),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(dev))
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_given, _stream(dev))
         if rc != 0:
             raise AttnVarlenError(rc, "attn_varlen_bwd")
         return dq, dk, dv
     rc = lib().attn_varlen_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs,
                                       total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
                                       float(softmax_scale), int(bool(causal)), wl, wr, _ptr(dout), _ptr(out),
-                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), _stream(dev))
+                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_given,
+                                      _stream(dev))
     if rc != 0:
         raise AttnVarlenError(rc, "attn_varlen_bwd_window")
     return dq, dk, dv
@@ -420,6 +456,13 @@ def attn_varlen_fwd_window(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
     """``attn_varlen_fwd`` with a local window (the C entry point of the same name)."""
     return attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
                            window_size=(window_left, window_right), **kw)
+
+
+def attn_varlen_bwd_stored_ds(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              softmax_scale=None, causal=False, window_left=-1, window_right=-1, **kw):
+    """``attn_varlen_bwd`` with dS stored for dQ (the C entry point of the same name)."""
+    return attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                           softmax_scale, causal, window_size=(window_left, window_right), stored_ds=True, **kw)
 
 
 def attn_varlen_bwd_window(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,

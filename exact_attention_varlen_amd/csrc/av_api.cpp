@@ -16,7 +16,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 5;
+constexpr int kVersionMinor = 6;
 constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;  // grid x block must stay below 2^32 work-items
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -84,7 +84,7 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
                 int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
                 int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
                 const void* dout, const void* out, const float* lse, void* dq, void* dk, void* dv,
-                void* workspace, size_t workspace_bytes, bool static_scratch, void* stream) {
+                void* workspace, size_t workspace_bytes, bool static_scratch, bool stored_ds, void* stream) {
   int rc = check_common(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                         n_q_heads, n_kv_heads, head_dim, softmax_scale, causal);
   if (rc != ATTN_VARLEN_OK) return rc;
@@ -94,6 +94,18 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
       !aligned(lse, 4))
     return ATTN_VARLEN_ERR_MISALIGNED;
   const size_t need = av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
+  if (stored_ds) {
+    // the stored-dS dQ: head dims 64 / 128 and a dS buffer within 32-bit offsets
+    if (head_dim > 128) return ATTN_VARLEN_ERR_BAD_HEAD_DIM;
+    if (total_q > 0 && total_k > 0) {
+      const size_t need_ds = av::bwd_ds_workspace_bytes(total_q, total_k, max_seqlen_q, max_seqlen_k, n_q_heads,
+                                                        n_kv_heads, head_dim);
+      if (need_ds == 0) return ATTN_VARLEN_ERR_BAD_SEQLEN;
+      if (!workspace || workspace_bytes < need_ds) return ATTN_VARLEN_ERR_WORKSPACE;
+    } else {
+      stored_ds = false;  // nothing to store: the plain path handles empty problems
+    }
+  }
   if (static_scratch) {
     if (need > av::noalloc_scratch_bytes()) return ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL;
   } else {
@@ -114,6 +126,8 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.ds = stored_ds ? static_cast<char*>(workspace) + need : nullptr;
+  a.ds_pitch = stored_ds ? av::bwd_ds_pitch(max_seqlen_q) : 0;
   return av::launch_bwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
 }
 
@@ -221,6 +235,17 @@ size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t
   return av::bwd_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim);
 }
 
+size_t attn_varlen_bwd_ds_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k, int32_t max_seqlen_q,
+                                         int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                                         int32_t head_dim) {
+  (void)num_seqs;
+  if (total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || n_q_heads <= 0 || n_kv_heads <= 0 ||
+      n_q_heads % n_kv_heads != 0)
+    return 0;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return 0;
+  return av::bwd_ds_workspace_bytes(total_q, total_k, max_seqlen_q, max_seqlen_k, n_q_heads, n_kv_heads, head_dim);
+}
+
 int attn_varlen_bwd_window(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
                            int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
@@ -229,7 +254,7 @@ int attn_varlen_bwd_window(const void* q, const void* k, const void* v, const in
                            void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_checked(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, dout, out, lse,
-                     dq, dk, dv, workspace, workspace_bytes, false, stream);
+                     dq, dk, dv, workspace, workspace_bytes, false, false, stream);
 }
 
 int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -243,6 +268,17 @@ int attn_varlen_bwd(const void* q, const void* k, const void* v, const int32_t* 
                                 out, lse, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
+int attn_varlen_bwd_stored_ds(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                              int32_t window_right, const void* dout, const void* out, const float* lse, void* dq,
+                              void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_checked(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                     n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, dout, out, lse,
+                     dq, dk, dv, workspace, workspace_bytes, false, true, stream);
+}
+
 int attn_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_k, int32_t num_seqs, int64_t total_q, int64_t total_k,
                             int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_q_heads, int32_t n_kv_heads,
@@ -250,7 +286,7 @@ int attn_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const i
                             const void* out, const float* lse, void* dq, void* dk, void* dv, void* stream) {
   return bwd_checked(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k,
                      n_q_heads, n_kv_heads, head_dim, softmax_scale, causal, -1, -1, dout, out, lse, dq, dk, dv,
-                     nullptr, 0, true, stream);
+                     nullptr, 0, true, false, stream);
 }
 
 int attn_varlen_validate_seqlens(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,

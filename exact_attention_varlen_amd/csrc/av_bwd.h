@@ -26,6 +26,8 @@ struct BwdParams {
   uint16_t* dv;
   float* part_dk;    // fp32 partial dK / dV per head split (head dim 256 with splits > 1)
   float* part_dv;
+  uint16_t* ds;      // stored dS^T, bf16 [Hq][total_k][ds_pitch] (head dims 64 / 128), or null
+  int ds_pitch;      // elements per key row of ds: kDsLead + max_seqlen_q rounded up to 128
   int num_seqs;
   int total_q;
   int total_k;
@@ -69,6 +71,26 @@ inline int dkdv_splits(int64_t total_k, int Hq, int Hkv, int D) {
     if (r % s == 0 && base * s >= 2048) return s;
   }
   return r > 0 ? r : 1;
+}
+
+// Stored dS (head dims 64 / 128): the dK / dV kernel writes dS = P (dP - Delta)
+// in bf16 as it forms it, and the dQ kernel then only multiplies it by K instead
+// of recomputing S, P, dP and dS. Layout: one row per (query head, key),
+// [Hq][total_k][ds_pitch], query rows of the key's sequence along the row,
+// starting at column kDsLead (the dQ kernel's query blocks, aligned toward the
+// sequence end, start up to 64 rows before row 0). Entries of (query, key)
+// pairs that no dK / dV step visits are never written; the dQ kernel masks every
+// pair it does not know to be visible.
+constexpr int kDsLead = 64;
+inline int ds_pitch_of(int max_q) { return kDsLead + (max_q + 127) / 128 * 128; }
+// Bytes of the dS buffer, or 0 when this path does not apply: head dim 256, an
+// empty problem, or one key sequence's rows spanning 2 GiB or more of the buffer
+// (32-bit offsets within a sequence).
+inline size_t ds_buffer_bytes(int64_t total_q, int64_t total_k, int max_q, int max_k, int Hq, int D) {
+  if (D > 128 || total_q <= 0 || total_k <= 0 || max_q <= 0 || max_k <= 0) return 0;
+  const int64_t pitch_bytes = 2 * (int64_t)ds_pitch_of(max_q);
+  if ((int64_t)(max_k + 64) * pitch_bytes >= ((int64_t)1 << 31)) return 0;
+  return ws_pad((size_t)Hq * (size_t)total_k * (size_t)pitch_bytes);
 }
 
 inline size_t ws_part_bytes(int64_t total_k, int Hkv, int D, int splits) {

@@ -51,6 +51,13 @@ size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, in
   return 2 * ws_plane_bytes(total_q, Hq) + 2 * ws_part_bytes(total_k, Hkv, D, splits);
 }
 
+size_t bwd_ds_workspace_bytes(int64_t total_q, int64_t total_k, int max_q, int max_k, int Hq, int Hkv, int D) {
+  const size_t ds = ds_buffer_bytes(total_q, total_k, max_q, max_k, Hq, D);
+  return ds ? bwd_workspace_bytes(total_q, total_k, Hq, Hkv, D) + ds : 0;
+}
+
+int bwd_ds_pitch(int max_q) { return ds_pitch_of(max_q); }
+
 // ---------------------------------------------------------------------------
 // 1. preprocess
 // ---------------------------------------------------------------------------
@@ -183,11 +190,14 @@ constexpr int kSchedValu = 0x002;
 // unit also issues the LDS reads one or two units ahead: the next k-steps of
 // the Q / dO rows, the transposed operands of C (a ring of RV), and the rows'
 // lse2 / Delta of the next B part.
-template <int D, bool MASK, bool LEFT>
+// STORE: the first two units of Y(b) also write dS of block b - 1 (16 bytes per
+// lane and k-step: this lane's key, 8 consecutive query rows) to the stored-dS
+// row `dsrow` (this lane's key, query row m0 + 8 half), for the dQ kernel.
+template <int D, bool MASK, bool LEFT, bool STORE>
 __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
                                           const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
                                           f32x16* dv, float c, int m0, int rlo, int rhi, const OperandOffsets<D>& off,
-                                          int half) {
+                                          int half, uint16_t* dsrow, bool kvalid) {
   using T = DkdvCfg<D>;
   constexpr int KK = D / 16, DB = D / 32, NB = T::BMQ / 32, PF = 2, RV = 3;
   constexpr int NU = 2 * KK;  // MFMA units per phase
@@ -289,6 +299,10 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
     // ---- Y(b): C(b - 1), B(b, 0) ----
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      if (STORE && b >= 1 && u < 2 && kvalid) {
+        const uint32_t* w = sw[(b - 1) & 1][u];
+        *reinterpret_cast<uint4*>(dsrow + 32 * (b - 1) + 16 * u) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
       if (b >= 1) {
         if (u + RV - 1 < NU) load_tr(b - 1, u + RV - 1);
         const int ks = u / (2 * DB), db = (u / 2) % DB;
@@ -310,7 +324,8 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
 // BAND: the visible keys of a row form a band (causal and / or a local window).
 // LEFT: the band has a left bound (window_left >= 0). Without one, every row
 // past a key's first visible row sees it, and masked steps test that bound only.
-template <int D, bool BAND, bool LEFT>
+// STORE: also write dS to the stored-dS buffer p.ds (bwd_dq_ds_kernel reads it).
+template <int D, bool BAND, bool LEFT, bool STORE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -408,20 +423,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     lds_barrier();
   };
   int it = 0;
-  auto step = [&](int st, auto masked) {
+  // stored dS: this lane's key row of query head g r (the group's first head),
+  // at query row 8 half; each head adds a plane of total_k rows, each step m0
+  uint16_t* ds_key = nullptr;
+  int64_t ds_plane = 0;
+  if (STORE) {
+    ds_key = p.ds + ((int64_t)g * r * p.total_k + ck + (kvalid ? kj : 0)) * p.ds_pitch + kDsLead + 8 * half;
+    ds_plane = (int64_t)p.total_k * p.ds_pitch;
+  }
+  auto step = [&](int hg, int st, auto masked) {
     stage_in(it);
     const int m0 = (sfirst + st) * T::BMQ;
     const lds_char* stg = lds + (it & 1) * T::STAGE;
     const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
-    dkdv_step<D, decltype(masked)::value, LEFT>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0, rlo, rhi,
-                                          off, half);
+    dkdv_step<D, decltype(masked)::value, LEFT, STORE>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0,
+                                                      rlo, rhi, off, half,
+                                                      STORE ? ds_key + hg * ds_plane + m0 : nullptr, kvalid);
     lds_barrier();
     ++it;
   };
   for (int hg = 0; hg < (total > 0 ? r : 0); ++hg) {
-    for (int st = 0; st < s_full_lo; ++st) step(st, std::true_type());
-    for (int st = s_full_lo; st < s_full_hi; ++st) step(st, std::false_type());
-    for (int st = s_full_hi; st < nsteps; ++st) step(st, std::true_type());
+    for (int st = 0; st < s_full_lo; ++st) step(hg, st, std::true_type());
+    for (int st = s_full_lo; st < s_full_hi; ++st) step(hg, st, std::false_type());
+    for (int st = s_full_hi; st < nsteps; ++st) step(hg, st, std::true_type());
   }
 
   if (kvalid) {
@@ -644,6 +668,193 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
 }
 
 // ---------------------------------------------------------------------------
+// 3b. query-stationary dQ from the stored dS: dQ = scale * dS K
+// ---------------------------------------------------------------------------
+// With the stored-dS buffer filled by the dK / dV kernel, the dQ of a query
+// block is one product per visible key tile: no S, P or dP to recompute, no
+// exponentials. A workgroup owns 128 query rows of one head (32 per wave) and
+// walks the visible 64-key tiles in ascending order, staging the K tile and the
+// dS^T tile (the 64 keys' rows of the buffer, 128 query columns from the
+// block's first row) HBM -> LDS by range-checked DMA, double-buffered; both
+// MFMA operands are transposing LDS reads of row-major tiles:
+//   dQ^T (32 head-dims x 32 queries) += K^T (head-dims x 16 keys) dS^T (16 keys x queries).
+// Tiles that hold hidden pairs (band edges, the sequence's last partial tile)
+// mask the dS operand per (query, key): the buffer holds nothing meaningful for
+// pairs no dK / dV step visited.
+
+template <int D>
+struct DqDsCfg {
+  using KV = RowTile<D, 64>;    // K tile: 64 keys
+  using DS = RowTile<128, 64>;  // dS^T tile: 64 keys x 128 query columns
+  static constexpr int NT = 256;
+  static constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+  static constexpr int BN = 64;   // keys per tile
+  static constexpr int STAGE = KV::BYTES + DS::BYTES;
+  static constexpr size_t LDS_BYTES = 2 * STAGE;
+  static constexpr int DMA_PER_WAVE = (KV::DMAS + DS::DMAS) / 4;
+  static_assert((KV::DMAS + DS::DMAS) % 4 == 0, "copies spread evenly over the 4 waves");
+  static_assert(BM == kQueryBlock && BN == key_tile(D), "tile shapes of the host-side plan");
+};
+
+template <int D>
+__device__ __forceinline__ void issue_k_ds(uint32_t stage, const i32x4& rk, uint32_t pitch_k, const i32x4& rds,
+                                           uint32_t pitch_ds, int n0, int wave, int lane) {
+  using T = DqDsCfg<D>;
+#pragma unroll
+  for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+    const int qd = wave * T::DMA_PER_WAVE + i;  // wave-uniform
+    if (qd < T::KV::DMAS)
+      tile_dma<D, 64>(stage, rk, pitch_k, n0, qd, lane);
+    else
+      tile_dma<128, 64>(stage + T::KV::BYTES, rds, pitch_ds, n0, qd - T::KV::DMAS, lane);
+  }
+}
+
+// LDS offsets of the transposing reads of query-column block `blk` (32 columns)
+// of a 128-column tile: the tr_operand<128> offsets of head-dim block blk.
+__device__ __forceinline__ void tr_block_offsets128(int lane, int blk, uint32_t& t0, uint32_t& t1) {
+  constexpr int ROW = 256;
+  const int half = lane >> 5;
+  const int grp = lane >> 4;
+  const int i = lane & 15;
+  const int j = i >> 2;
+  const int cc = i & 3;
+  const int r0 = 8 * half + j;
+  const int r1 = r0 + 4;
+  const int chunk = blk * 4 + 2 * (grp & 1) + (cc >> 1);
+  t0 = r0 * ROW + ((chunk ^ swz<128>(r0)) << 4) + (cc & 1) * 8;
+  t1 = r1 * ROW + ((chunk ^ swz<128>(r1)) << 4) + (cc & 1) * 8;
+}
+
+// Zero the dS values of keys key0 .. key0 + 7 (one B-operand k-group) that this
+// lane's query row does not see: klo <= key < khi (klo only with LEFT).
+template <bool LEFT>
+__device__ __forceinline__ bf16x8 mask_key_group(const bf16x8& v, int key0, int klo, int khi) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    const int k = key0 + 2 * pr;
+    const bool a = (!LEFT || k >= klo) && k < khi;
+    const bool b = (!LEFT || k + 1 >= klo) && k + 1 < khi;
+    w[pr] &= (a ? 0x0000ffffu : 0u) | (b ? 0xffff0000u : 0u);
+  }
+  return as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// One 64-key tile: 4 k-steps of 16 keys, the operands of k-step s + 1 read
+// while k-step s multiplies.
+template <int D, bool MASK, bool LEFT>
+__device__ __forceinline__ void dq_ds_tile(const lds_char* Ks, const lds_char* Ds, f32x16* dq, int n0, int klo,
+                                           int khi, const OperandOffsets<D>& off, uint32_t ds0, uint32_t ds1,
+                                           int half) {
+  using T = DqDsCfg<D>;
+  constexpr int DB = D / 32, NS = T::BN / 16;
+  bf16x8 ka[2][DB], sb[2];
+  auto load = [&](int s, int slot) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) ka[slot][db] = tr_operand<D>(Ks + 16 * s * T::KV::ROW, off, db);
+    const uint2 lo = lds_read_tr4(Ds + 16 * s * T::DS::ROW + ds0);
+    const uint2 hi = lds_read_tr4(Ds + 16 * s * T::DS::ROW + ds1);
+    sb[slot] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
+  load(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s + 1 < NS) load(s + 1, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 b = MASK ? mask_key_group<LEFT>(sb[s & 1], n0 + 16 * s + 8 * half, klo, khi) : sb[s & 1];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = mfma32x32x16(ka[s & 1][db], b, dq[db]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D, bool BAND, bool LEFT>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(BwdParams p) {
+  using T = DqDsCfg<D>;
+  extern __shared__ __align__(16) uint16_t smem[];
+  lds_char* lds = (lds_char*)smem;
+
+  const int r = p.Hq / p.Hkv;
+  const int64_t L = xcd_logical(blockIdx.x, r);
+  const int rank = (int)(L / p.Hq);
+  const int h = (int)(L % p.Hq);
+  Item item;
+  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, T::BM, p.levels, rank, item)) return;
+  const int g = h / r;
+  const int mblk = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  // query blocks aligned toward the end of the sequence, as in the forward
+  const int q0 = mblk * T::BM - query_lead(Lq, T::BM, T::BN);
+  const int qi = q0 + wave * 32 + col;
+  const bool qvalid = qi >= 0 && qi < Lq;
+
+  // key tiles [t_lo, t_hi); the unmasked ones [f_lo, f_hi) lie between masked
+  // ones (the band's left edge before, its right edge and the sequence end after)
+  int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
+  if (BAND) {
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
+    t_lo = ts.lo;
+    t_hi = ts.hi;
+    f_lo = ts.full_lo;
+    f_hi = max(f_lo, ts.full_hi);
+  }
+  const int klo = BAND ? band_lo(qi, Lq, Lk, p.wl) : 0;
+  const int khi = BAND ? band_hi(qi, Lq, Lk, p.wr) : Lk;
+
+  const uint32_t pitch_k = (uint32_t)p.Hkv * D * 2;
+  const i32x4 rk = head_rows_rsrc<D>(p.k + ((int64_t)ck * p.Hkv + g) * D, Lk, pitch_k);
+  // dS^T rows of this head and sequence, columns from the block's first query row
+  const uint32_t pitch_ds = (uint32_t)p.ds_pitch * 2;
+  const i32x4 rds =
+      head_rows_rsrc<128>(p.ds + ((int64_t)h * p.total_k + ck) * p.ds_pitch + kDsLead + q0, Lk, pitch_ds);
+  const uint32_t lds0 = lds_addr(lds);
+  if (t_hi > t_lo) issue_k_ds<D>(lds0 + (t_lo & 1) * T::STAGE, rk, pitch_k, rds, pitch_ds, t_lo * T::BN, wave, lane);
+
+  OperandOffsets<D> off;
+  operand_offsets<D>(off, lane);
+  uint32_t ds0, ds1;
+  tr_block_offsets128(lane, wave, ds0, ds1);
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = zero16();
+
+  auto stage_in = [&](int n) {
+    if (n + 1 < t_hi) {
+      issue_k_ds<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, pitch_k, rds, pitch_ds, (n + 1) * T::BN, wave, lane);
+      wait_vmcnt<T::DMA_PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+  };
+  auto tile = [&](int n, auto masked) {
+    stage_in(n);
+    const lds_char* cur = lds + (n & 1) * T::STAGE;
+    dq_ds_tile<D, decltype(masked)::value, LEFT>(cur, cur + T::KV::BYTES, dq, n * T::BN, klo, khi, off, ds0, ds1,
+                                                half);
+    lds_barrier();
+  };
+  for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
+  for (int n = f_lo; n < f_hi; ++n) tile(n, std::false_type());
+  for (int n = f_hi; n < t_hi; ++n) tile(n, std::true_type());
+
+  if (qvalid) {
+    uint16_t* row = p.dq + ((int64_t)(cq + qi) * p.Hq + h) * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) store_acc_row(row + db * 32, dq[db], p.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -695,27 +906,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
   p.scale = f.scale;
   p.scale_log2 = f.scale * kLog2e;
 
-  // dQ first: it also writes the Delta / lse2 rows that dK / dV reads
-  if (f.total_q > 0) {
-    using T = DqCfg<D>;
-    auto kern = bwd_dq_kernel<D, BAND, LEFT>;
-    static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
-    if (e != hipSuccess) return e;
-    BwdParams pq = p;
-    pq.levels = ceil_div(f.max_q, T::BM);
-    const int64_t grid = grid_for(f.total_q, f.num_seqs, T::BM, f.Hq, f.Hq / f.Hkv);
-    if (grid > 0 && pq.levels > 0) {
-      prof_begin("attn_bwd_dq", stream);
-      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pq);
-      prof_end(stream);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  if (f.total_k > 0) {
+  p.ds = static_cast<uint16_t*>(a.ds);
+  p.ds_pitch = a.ds_pitch;
+
+  auto run_dkdv = [&](auto store) -> hipError_t {
     using T = DkdvCfg<D>;
-    auto kern = bwd_dkdv_kernel<D, BAND, LEFT>;
+    auto kern = bwd_dkdv_kernel<D, BAND, LEFT, decltype(store)::value>;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
@@ -727,9 +923,42 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
       prof_end(stream);
       e = hipGetLastError();
-      if (e != hipSuccess) return e;
     }
+    return e;
+  };
+  auto run_dq = [&](auto kern, size_t lds_bytes, std::atomic<uint64_t>& lds_set, const char* name) -> hipError_t {
+    hipError_t e = lds_limit_once(kern, lds_bytes, lds_set);
+    if (e != hipSuccess) return e;
+    BwdParams pq = p;
+    pq.levels = ceil_div(f.max_q, kQueryBlock);
+    const int64_t grid = grid_for(f.total_q, f.num_seqs, kQueryBlock, f.Hq, f.Hq / f.Hkv);
+    if (grid > 0 && pq.levels > 0) {
+      prof_begin(name, stream);
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, stream, pq);
+      prof_end(stream);
+      e = hipGetLastError();
+    }
+    return e;
+  };
+
+  if (p.ds) {
+    // stored dS (both totals > 0 here): the row terms, then dK / dV, which also
+    // writes dS, then dQ = scale * dS K from the stored values
+    hipError_t e = launch_prep<D>(a, a.delta, lse2);
+    if (e == hipSuccess) e = run_dkdv(std::true_type());
+    static std::atomic<uint64_t> lds_set{0};
+    if (e == hipSuccess)
+      e = run_dq(bwd_dq_ds_kernel<D, BAND, LEFT>, DqDsCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq_ds");
+    return e;
   }
+  // recomputing dQ: the dQ kernel first, which also writes the Delta / lse2 rows
+  // that dK / dV reads
+  if (f.total_q > 0) {
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = run_dq(bwd_dq_kernel<D, BAND, LEFT>, DqCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq");
+    if (e != hipSuccess) return e;
+  }
+  if (f.total_k > 0) return run_dkdv(std::false_type());
   return hipSuccess;
 }
 

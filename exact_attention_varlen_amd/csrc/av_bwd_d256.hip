@@ -624,6 +624,8 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
   BwdParams p;
+  p.ds = nullptr;  // the stored-dS path is for head dims 64 / 128
+  p.ds_pitch = 0;
   p.q = static_cast<const uint16_t*>(f.q);
   p.k = static_cast<const uint16_t*>(f.k);
   p.v = static_cast<const uint16_t*>(f.v);

@@ -73,6 +73,8 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;  // workspace (Delta, lse2, partial dK / dV): see av_bwd.h
+  void* ds;      // stored-dS buffer in the workspace (head dims 64 / 128), or null: dQ recomputes dS
+  int ds_pitch;  // its elements per key row
 };
 
 // Packing-array check (av_validate.hip): bits of the result word.
@@ -121,6 +123,10 @@ int prof_get(int i, char* name, int cap, float* ms);
 
 int64_t fwd_grid_size(int64_t total_q, int num_seqs, int Hq, int Hkv);
 size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D);
+// Workspace of the stored-dS backward (bwd_workspace_bytes plus the dS buffer),
+// 0 when that path does not apply; and the dS buffer's row pitch (elements).
+size_t bwd_ds_workspace_bytes(int64_t total_q, int64_t total_k, int max_q, int max_k, int Hq, int Hkv, int D);
+int bwd_ds_pitch(int max_q);
 
 }  // namespace av
 

@@ -238,6 +238,17 @@ size_t attn_varlen_bwd_workspace_size(int32_t num_seqs, int64_t total_q, int64_t
                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim);
 
 /*
+ * Bytes of device workspace attn_varlen_bwd_stored_ds needs, or 0 where that
+ * call is not available (head dim 256, an empty problem, or one sequence's rows
+ * of its dS buffer spanning 2 GiB or more): attn_varlen_bwd_workspace_size()
+ * plus n_q_heads * total_k * (64 + 128 * ceil(max_seqlen_q / 128)) * 2 bytes,
+ * rounded up to 256.
+ */
+size_t attn_varlen_bwd_ds_workspace_size(int32_t num_seqs, int64_t total_q, int64_t total_k,
+                                         int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim);
+
+/*
  * Backward pass: gradients of sum(dout * out) with respect to q, k, v for the
  * forward defined above ([A100] benchmark script `fb`: forward then
  * out.backward(dout); [GUIDE] Backward Kernels). Arguments up to `causal` are
@@ -276,6 +287,36 @@ int attn_varlen_bwd_window(const void* q, const void* k, const void* v,
                            const void* dout, const void* out, const float* lse,
                            void* dq, void* dk, void* dv,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward with dS stored for dQ instead of recomputed (head dims 64 / 128).
+ * The main kernel ([GUIDE] Backward Kernels) forms dS = P * (dP - Delta) for
+ * dK; here it also writes dS in bf16 (the value its dK product uses) to a
+ * buffer in the workspace, one row per (query head, key) of max_seqlen_q
+ * rounded up to 128, plus 64, columns, and the dQ kernel forms dQ =
+ * softmax_scale * dS K from it: one product per visible key tile instead of
+ * recomputing S, P and dP. The trade is two bf16 passes over every visible
+ * (query, key, head) through HBM for 4 * head_dim flop per pair; on MI355X the
+ * recomputing attn_varlen_bwd_window is faster at every measured shape (packed
+ * 16K documents, 4K and 16K sequences, head dims 64 and 128), so this call is
+ * an alternative, not the default. Same arguments and results as
+ * attn_varlen_bwd_window (deterministic; dQ and dK can differ from it by
+ * rounding: the row term Delta is summed in another order), plus:
+ *   workspace          at least attn_varlen_bwd_ds_workspace_size() bytes, 16-byte aligned
+ * Errors: those of attn_varlen_bwd_window; ATTN_VARLEN_ERR_BAD_HEAD_DIM for head
+ * dim 256; ATTN_VARLEN_ERR_BAD_SEQLEN when the size call returns 0 for a
+ * non-empty problem.
+ */
+int attn_varlen_bwd_stored_ds(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t num_seqs, int64_t total_q, int64_t total_k,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              float softmax_scale, int32_t causal,
+                              int32_t window_left, int32_t window_right,
+                              const void* dout, const void* out, const float* lse,
+                              void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Allocation-free backward, for callers that cannot allocate device memory

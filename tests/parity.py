@@ -53,10 +53,20 @@ def gpu_fwd(wl: W.Workload, d: Dict[str, torch.Tensor], return_lse: bool = True)
                              window_size=window_of(wl))
 
 
-def gpu_bwd(wl: W.Workload, d: Dict[str, torch.Tensor], out, lse):
+def gpu_bwd(wl: W.Workload, d: Dict[str, torch.Tensor], out, lse, stored_ds: bool = False):
+    """The backward through the C ABI: attn_varlen_bwd (dQ recomputes dS), or with
+    stored_ds attn_varlen_bwd_stored_ds."""
     return A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
                              wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
-                             window_size=window_of(wl))
+                             window_size=window_of(wl), stored_ds=stored_ds)
+
+
+def bwd_paths(wl: W.Workload):
+    """Backward paths to check for a workload: the recomputing dQ (the default),
+    plus the stored-dS one where it is available (head dims 64 / 128)."""
+    ds = A.attn_varlen_bwd_ds_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k, wl.max_seqlen_q,
+                                             wl.max_seqlen_k, wl.n_q_heads, wl.n_kv_heads, wl.head_dim)
+    return [False, True] if ds > 0 else [False]
 
 
 def f64(t: torch.Tensor) -> np.ndarray:

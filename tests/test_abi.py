@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_error_strings():
-    assert A.attn_varlen_version() == (1, 5)
+    assert A.attn_varlen_version() == (1, 6)
     for name, code in header_enums().items():
         s = A.attn_varlen_error_string(code)
         assert s and s != "unknown error code", name
@@ -396,3 +396,32 @@ def test_noalloc_argument_errors_come_first():
                                      FAKE, FAKE, FAKE, FAKE, FAKE, None) == E["ATTN_VARLEN_ERR_BAD_HEAD_DIM"]
     assert l.attn_varlen_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 64, 4, 2, 64, 0.1, 0, None,
                                      FAKE, FAKE, FAKE, FAKE, FAKE, None) == E["ATTN_VARLEN_ERR_NULL_POINTER"]
+
+
+def test_stored_ds_workspace_size():
+    """The stored-dS backward's workspace: the recomputing one's plus one bf16 row
+    of 64 + 128 * ceil(max_seqlen_q / 128) columns per (query head, key), rounded
+    up to 256 bytes; 0 where the path does not apply."""
+    plain = A.attn_varlen_bwd_workspace_size(10, 16384, 16384, 32, 8, 128)
+    got = A.attn_varlen_bwd_ds_workspace_size(10, 16384, 16384, 3523, 3523, 32, 8, 128)
+    ds = 32 * 16384 * (64 + 128 * 28) * 2
+    assert got == plain + (ds + 255) // 256 * 256
+    assert A.attn_varlen_bwd_ds_workspace_size(1, 100, 90, 100, 90, 4, 2, 64) == (
+        A.attn_varlen_bwd_workspace_size(1, 100, 90, 4, 2, 64) + (4 * 90 * (64 + 128) * 2 + 255) // 256 * 256)
+    assert A.attn_varlen_bwd_ds_workspace_size(8, 32768, 32768, 4096, 4096, 8, 1, 256) == 0  # head dim 256
+    assert A.attn_varlen_bwd_ds_workspace_size(1, 0, 100, 0, 100, 4, 2, 64) == 0              # no queries
+    assert A.attn_varlen_bwd_ds_workspace_size(1, 65536, 65536, 65536, 65536, 32, 8, 128) == 0  # rows >= 2 GiB
+    assert A.attn_varlen_bwd_ds_workspace_size(1, 100, 100, 100, 100, 4, 3, 64) == 0          # bad heads
+
+
+def test_stored_ds_call_argument_errors():
+    """attn_varlen_bwd_stored_ds: head dim 256 has no stored-dS path, and the
+    workspace must hold the dS buffer; both are checked before any HIP call."""
+    l = _lib.lib()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 64, 4, 2]
+    tail = [0.1, 0, -1, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert l.attn_varlen_bwd_stored_ds(*args, 256, *tail, FAKE, 1 << 30, None) == E["ATTN_VARLEN_ERR_BAD_HEAD_DIM"]
+    need = A.attn_varlen_bwd_ds_workspace_size(1, 64, 64, 64, 64, 4, 2, 128)
+    assert need > A.attn_varlen_bwd_workspace_size(1, 64, 64, 4, 2, 128)
+    assert l.attn_varlen_bwd_stored_ds(*args, 128, *tail, FAKE, need - 16, None) == E["ATTN_VARLEN_ERR_WORKSPACE"]
+    assert l.attn_varlen_bwd_stored_ds(*args, 128, *tail, None, need, None) == E["ATTN_VARLEN_ERR_WORKSPACE"]

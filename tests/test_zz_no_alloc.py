@@ -1,5 +1,6 @@
 """The allocation-free backward (attn_varlen_bwd_noalloc, static device scratch)
-against the allocating one (attn_varlen_bwd) through the C ABI: bit-identical
+against the allocating one (attn_varlen_bwd with the recomputing backward's
+workspace) through the C ABI: bit-identical
 gradients, over calls in a row on one GPU whose problems shrink, so that each
 call finds the previous call's contents in the scratch."""
 import pytest
@@ -26,8 +27,10 @@ def test_noalloc_backward_matches_the_allocating_one():
         d = to_dev(W.make_inputs(wl))
         announce(f"noalloc backward {wl.name}")
         out, lse = gpu_fwd(wl, d)
+        # attn_varlen_bwd with the recomputing backward's workspace (the path the
+        # allocation-free call takes)
         ref = A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
-                                wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
+                                wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal, stored_ds=False)
         got = A.attn_varlen_bwd_noalloc(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"],
                                         d["cu_seqlens_k"], wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale,
                                         wl.causal)
