@@ -782,6 +782,55 @@ def all_configs_table(include_long: bool):
     return 0
 
 
+def kernel_times(rounds: int = 3, steps: int = 8):
+    """Per-kernel times (library events, eager forward+backward steps) of one
+    workload per head dim, for comparing builds of the library: one JSON line
+    naming the library file, with each kernel's median over rounds of its mean
+    over steps."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import exact_attention_varlen_amd._lib as L
+    import workloads as W
+
+    rows = {}
+    for wl in (W.packed_16k(), W.single_16k_full(), W.Workload("2x16384-mha16-d64-full-bwd", [16384, 16384], 16, 16,
+                                                                64, False), W.hd256_gqa(2, 16384, True)):
+        d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+        mq, mk = wl.max_seqlen_q, wl.max_seqlen_k
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        ws = torch.empty(max(16, bwd_ws_bytes(wl)), dtype=torch.uint8, device="cuda:0")
+
+        def step():
+            A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk, wl.softmax_scale,
+                              wl.causal, out=out, lse=lse)
+            A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
+                              mq, mk, wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        per = {}
+        for _ in range(rounds):
+            A.attn_varlen_profile_enable(True)
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            A.attn_varlen_profile_enable(False)
+            got = {}
+            for name, ms in A.attn_varlen_profile_records():
+                got.setdefault(name, []).append(ms)
+            for name, v in got.items():
+                per.setdefault(name, []).append(sum(v) / len(v))
+        rows[wl.name] = {k: statistics.median(v) for k, v in per.items()}
+        del d, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"library": os.path.basename(L.LIB_PATH), "kernels_ms": rows}), flush=True)
+    return 0
+
+
 def fwd_table():
     """Steady-state forward time (with and without the LSE) of one workload per
     head dim, for comparing builds of the library (ATTN_VARLEN_LIBRARY selects a
@@ -845,6 +894,9 @@ def main(argv=None):
     ap.add_argument("--bwd-paths", action="store_true",
                     help="only time the step with dS stored for dQ against the recomputing dQ on workloads of "
                          "every head dim <= 128 (one JSON line each) and exit")
+    ap.add_argument("--kernel-times", action="store_true",
+                    help="only time each kernel of eager forward+backward steps on one workload per head dim for the "
+                         "loaded library build (one JSON line) and exit")
     ap.add_argument("--fwd-table", action="store_true",
                     help="only time the forward (with and without the LSE) of one workload per head dim for the "
                          "loaded library build (one JSON line) and exit")
@@ -872,6 +924,9 @@ def main(argv=None):
     if a.fwd_table:
         warm_gpu()
         return fwd_table()
+    if a.kernel_times:
+        warm_gpu()
+        return kernel_times()
     if a.bwd_paths:
         warm_gpu()
         for wl in (W.packed_16k(), W.a100_shape(4096), W.single_16k_full(),
