@@ -460,25 +460,30 @@ def named_workload(name: str):
     return known[name]
 
 
-def eager_only(wl, steps: int, warmup: int):
+def eager_only(wl, steps: int, warmup: int, stored_ds: bool = False):
     """warmup + steps eager forward+backward steps (forward only for a
     forward-only workload), no graphs and no extra timing machinery: the command
-    profilers wrap."""
+    profilers wrap. stored_ds: the backward stores dS for dQ
+    (attn_varlen_bwd_stored_ds) instead of recomputing it."""
     import torch
 
     import exact_attention_varlen_amd as A
     import workloads as W
 
     d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+    ws = None
+    if wl.backward:
+        ws = torch.empty(max(16, bwd_ws_bytes(wl, stored_ds)), dtype=torch.uint8, device="cuda:0")
     for i in range(warmup + steps):
         out, lse = A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], wl.max_seqlen_q,
                                      wl.max_seqlen_k, wl.softmax_scale, wl.causal, return_lse=True)
         if not wl.backward:
             continue
         A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"],
-                          wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal)
+                          wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal, workspace=ws,
+                          stored_ds=stored_ds)
     torch.cuda.synchronize()
-    print(json.dumps({"workload": wl.name, "eager_steps": warmup + steps}), flush=True)
+    print(json.dumps({"workload": wl.name, "eager_steps": warmup + steps, "stored_ds": bool(stored_ds)}), flush=True)
     return 0
 
 
@@ -879,6 +884,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--stored-ds", action="store_true",
+                    help="with --eager-only: the backward stores dS for dQ instead of recomputing it")
     ap.add_argument("--eager-only", action="store_true",
                     help="only run warmup + steps eager fwd+bwd steps of the main workload (for profilers) and exit")
     ap.add_argument("--workload", default=None,
@@ -942,7 +949,8 @@ def main(argv=None):
         print(json.dumps(window_split_secondary()), flush=True)
         return 0
     if a.eager_only:
-        return eager_only(named_workload(a.workload) if a.workload else W.packed_16k(), a.steps, a.warmup)
+        return eager_only(named_workload(a.workload) if a.workload else W.packed_16k(), a.steps, a.warmup,
+                          stored_ds=a.stored_ds)
     primary = W.packed_16k()
     log(f"device {torch.cuda.get_device_name(0)}; warming up")
     warm_gpu()
