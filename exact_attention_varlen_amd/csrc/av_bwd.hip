@@ -140,16 +140,6 @@ __device__ __forceinline__ void issue_qdo(uint32_t stage, const i32x4& rq, const
   }
 }
 
-// waves 0 and 1 have F32_DMAS more copies per stage in flight than waves 2 and 3
-template <int D>
-__device__ __forceinline__ void wait_qdo_stage(int wave) {
-  using T = DkdvCfg<D>;
-  if (wave < 2)
-    wait_vmcnt<T::DMA_PER_WAVE + T::F32_DMAS>();
-  else
-    wait_vmcnt<T::DMA_PER_WAVE>();
-}
-
 // S / dP products of the dK / dV kernel, written as asm so that their
 // accumulators are VGPRs, which the VALU reads next, and the K / V operand is an
 // AGPR. (At one wave per SIMD the compiler gives every MFMA an AGPR result, and
@@ -188,8 +178,9 @@ constexpr int kSchedValu = 0x002;
 //   Y(b): C(b - 1) with B(b, k-step 0) between its MFMAs,
 // for b = 0 .. NB (the first and last phases run without partner work). Each
 // unit also issues the LDS reads one or two units ahead: the next k-steps of
-// the Q / dO rows, the transposed operands of C (a ring of RV), and the rows'
-// lse2 / Delta of the next B part.
+// the Q / dO rows and the transposed operands of C (a ring of RV). The rows'
+// lse2 / Delta of a B part are read at the start of the phase before the one
+// that uses them (their registers are free by then), a whole phase ahead.
 // STORE: the first two units of Y(b) also write dS of block b - 1 (16 bytes per
 // lane and k-step: this lane's key, 8 consecutive query rows) to the stored-dS
 // row `dsrow` (this lane's key, query row m0 + 8 half), for the dQ kernel.
@@ -269,12 +260,11 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
 
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) load_rows(0, kk);
-  load_rowvals(0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b <= NB; ++b) {
     // ---- X(b): A(b), B(b - 1, 1) ----
-    if (b >= 1) load_rowvals(b - 1, 1);  // lse2 / Delta of B(b - 1, 1)
+    if (b < NB) load_rowvals(b, 0);  // lse2 / Delta of B(b, 0), a phase ahead
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -288,15 +278,16 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
           mfma_score(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
       }
       if (b >= 1) b_share(b - 1, 1, u);
-      // warm the ring of C(b - 1) and the lse2 / Delta of B(b, 0) in the last units
+      // warm the ring of C(b - 1) in the last units
       if (b >= 1 && u >= NU - (RV - 1)) load_tr(b - 1, u - (NU - (RV - 1)));
-      if (b < NB && u == NU - 1) load_rowvals(b, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (b < NB) s_fence_scores(sacc[b & 1], dacc[b & 1]);
     if (b >= 1) b_tail(b - 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     // ---- Y(b): C(b - 1), B(b, 0) ----
+    if (b < NB) load_rowvals(b, 1);  // lse2 / Delta of B(b, 1), a phase ahead
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       if (STORE && b >= 1 && u < 2 && kvalid) {
@@ -413,14 +404,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // unmasked steps, masked steps (near its left edge), as separate loops so the
   // accumulators keep their registers from step to step. `it` counts steps over
   // all heads for the double-buffer and copy pipeline.
+  // One barrier per step: after it, stage it (whose copies are the only ones in
+  // flight) is in LDS for every wave, and every wave is done with step it - 1,
+  // whose buffer then takes the copies of stage it + 1.
   auto stage_in = [&](int it) {
-    if (it + 1 < total) {
-      issue(it + 1, lds0 + ((it + 1) & 1) * T::STAGE);
-      wait_qdo_stage<D>(wave);
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
+    if (it + 1 < total) issue(it + 1, lds0 + ((it + 1) & 1) * T::STAGE);
   };
   int it = 0;
   // stored dS: this lane's key row of query head g r (the group's first head),
@@ -439,7 +429,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     dkdv_step<D, decltype(masked)::value, LEFT, STORE>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0,
                                                       rlo, rhi, off, half,
                                                       STORE ? ds_key + hg * ds_plane + m0 : nullptr, kvalid);
-    lds_barrier();
     ++it;
   };
   for (int hg = 0; hg < (total > 0 ? r : 0); ++hg) {
@@ -516,10 +505,13 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
     dp = mfma32x32x16(as_bf16x8(fr[kk % (PF + 1)][1]), df[kk], dp);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // K^T operands of the first k-step of dQ are read before the exp work
-  bf16x8 ka[D / 32];
+  // K^T operands of both k-steps of dQ are read before the exp work
+  bf16x8 ka[2][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) ka[db] = tr_operand<D>(Ks, off, db);
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) ka[ks][db] = tr_operand<D>(Ks + 16 * ks * T::ROW, off, db);
+  }
   __builtin_amdgcn_sched_barrier(0);
   float dsv[16];
 #pragma unroll
@@ -535,12 +527,8 @@ __device__ __forceinline__ void dq_half(const lds_char* Ks, const lds_char* Vs, 
   for (int ks = 0; ks < 2; ++ks) {
     const bf16x8 sb = to_bf16x8(dsv[8 * ks + 0], dsv[8 * ks + 1], dsv[8 * ks + 2], dsv[8 * ks + 3], dsv[8 * ks + 4],
                                 dsv[8 * ks + 5], dsv[8 * ks + 6], dsv[8 * ks + 7]);
-    if (ks == 1) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) ka[db] = tr_operand<D>(Ks + 16 * T::ROW, off, db);
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(ka[db], sb, dq[db]);
+    for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(ka[ks][db], sb, dq[db]);
   }
 }
 
@@ -638,14 +626,12 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
 
   // masked head, full tiles, masked tail: separate loops so the accumulators
   // keep their registers across iterations
+  // one barrier per tile: stage n has landed for every wave, and every wave is
+  // done with tile n - 1, whose buffer then takes the copies of tile n + 1
   auto stage_in = [&](int n) {
-    if (n + 1 < t_hi) {
-      issue_kv_dq<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
-      wait_vmcnt<T::DMA_PER_WAVE>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
+    if (n + 1 < t_hi) issue_kv_dq<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
   };
   auto tile = [&](int n, auto masked) {
     stage_in(n);
@@ -654,7 +640,6 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
     for (int kb = 0; kb < 2; ++kb)
       dq_half<D, decltype(masked)::value, LEFT>(cur + kb * 32 * T::ROW, cur + T::TILE + kb * 32 * T::ROW, qf, df, dq, c,
                                           lse2, dlt, n * T::BN + kb * 32, klo, khi, off, half);
-    lds_barrier();
   };
   for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
   for (int n = f_lo; n < f_hi; ++n) tile(n, std::false_type());
@@ -827,21 +812,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq[db] = zero16();
 
+  // one barrier per tile, as in the dQ kernel
   auto stage_in = [&](int n) {
-    if (n + 1 < t_hi) {
-      issue_k_ds<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, pitch_k, rds, pitch_ds, (n + 1) * T::BN, wave, lane);
-      wait_vmcnt<T::DMA_PER_WAVE>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
+    if (n + 1 < t_hi)
+      issue_k_ds<D>(lds0 + ((n + 1) & 1) * T::STAGE, rk, pitch_k, rds, pitch_ds, (n + 1) * T::BN, wave, lane);
   };
   auto tile = [&](int n, auto masked) {
     stage_in(n);
     const lds_char* cur = lds + (n & 1) * T::STAGE;
     dq_ds_tile<D, decltype(masked)::value, LEFT>(cur, cur + T::KV::BYTES, dq, n * T::BN, klo, khi, off, ds0, ds1,
                                                 half);
-    lds_barrier();
   };
   for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
   for (int n = f_lo; n < f_hi; ++n) tile(n, std::false_type());

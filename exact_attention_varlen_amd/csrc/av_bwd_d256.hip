@@ -344,18 +344,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
   const int rlo = (BAND && p.wr >= 0) ? kj - (Lk - Lq) - p.wr : INT_MIN / 2;
   const int rhi = (BAND && p.wl >= 0) ? kj - (Lk - Lq) + p.wl : INT_MAX / 2;
 
-  // waves 0 and 1 have one more copy (lse2 / Delta) per stage in flight
+  // One barrier per step: after it, stage it (whose copies are the only ones in
+  // flight) is in LDS for every wave, and every wave is done with step it - 1,
+  // whose buffer then takes the copies of stage it + 1.
   auto stage_in = [&](int it) {
-    if (it + 1 < total) {
-      issue(it + 1, (it + 1) & 1);
-      if (wave < 2)
-        wait_vmcnt<T::DMA_PER_WAVE + 1>();
-      else
-        wait_vmcnt<T::DMA_PER_WAVE>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
+    if (it + 1 < total) issue(it + 1, (it + 1) & 1);
   };
   // Per query head of the split: masked steps, unmasked steps, masked steps
   // (separate loops, so the accumulators keep their registers). `it` counts
@@ -368,7 +363,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv256_kernel(BwdParams p) {
     const float* f32 = reinterpret_cast<const float*>(smem) + (T::F32 + (it & 1) * T::F32_STAGE) / 4;
     dkdv256_step<decltype(masked)::value, LEFT>(lds, stg, stg + T::TILE, f32, f32 + 64, kf, vrow, dk, dv, c, rlo - m0,
                                           rhi - m0, off, half);
-    lds_barrier();
     ++it;
   };
   for (int hg = 0; hg < (total > 0 ? hper : 0); ++hg) {
@@ -597,20 +591,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   acc_fence(dq);
   const float c = p.scale_log2;
 
+  // one barrier per tile: stage n has landed for every wave, and every wave is
+  // done with tile n - 1, whose buffer then takes the copies of tile n + 1
   auto stage_in = [&](int n) {
-    if (n + 1 < t_hi) {
-      issue_kv_dq256(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
-      wait_vmcnt<T::DMA_PER_WAVE>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_vmcnt<0>();
     lds_barrier();
+    if (n + 1 < t_hi) issue_kv_dq256(lds0 + ((n + 1) & 1) * T::STAGE, rk, rv, pitch, (n + 1) * T::BN, wave, lane);
   };
   auto tile = [&](int n, auto masked) {
     stage_in(n);
     const lds_char* cur = lds + (n & 1) * T::STAGE;
     dq256_tile<decltype(masked)::value, LEFT>(cur, cur + T::TILE, qf, df, dq, c, lse2, dlt, n * T::BN, klo, khi, off, half);
-    lds_barrier();
   };
   for (int n = t_lo; n < f_lo; ++n) tile(n, std::true_type());
   for (int n = f_lo; n < f_hi; ++n) tile(n, std::false_type());
