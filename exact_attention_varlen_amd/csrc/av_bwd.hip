@@ -176,7 +176,9 @@ constexpr int kSchedValu = 0x002;
 // units each:
 //   X(b): A(b)     with B(b - 1, k-step 1) between its MFMAs,
 //   Y(b): C(b - 1) with B(b, k-step 0) between its MFMAs,
-// for b = 0 .. NB (the first and last phases run without partner work). Each
+// for b = 0 .. NB. X(0) has no B part and X(NB) no A part, Y(0) no C part and
+// Y(NB) no B part; so that no phase is left with vector work alone, X(NB) also
+// runs the first units of C(NB - 1) and Y(0) the first units of A(1). Each
 // unit also issues the LDS reads one or two units ahead: the next k-steps of
 // the Q / dO rows and the transposed operands of C (a ring of RV). The rows'
 // lse2 / Delta of a B part are read at the start of the phase before the one
@@ -257,6 +259,36 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
       if (e * NU / 8 + 1 >= NU) b_finish(b, ks, e);
     }
   };
+  // unit w of C(b): dV (w even) or dK (w odd) of head-dim block (w / 2) % DB and
+  // k-step w / (2 DB), its transposed operand from the ring
+  auto c_unit = [&](int b, int w) {
+    const int ks = w / (2 * DB), db = (w / 2) % DB;
+    const uint32_t* wv = (w & 1) ? sw[b & 1][ks] : pw[b & 1][ks];
+    const bf16x8 bop = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
+    f32x16& acc = (w & 1) ? dk[db] : dv[db];
+    acc = mfma32x32x16(va[w % RV], bop, acc);
+  };
+  // X(NB) has no A MFMAs of its own: it runs the first CX units of C(NB - 1),
+  // which need only k-step 0's P / dS (formed in Y(NB - 1)), one every other
+  // unit from unit 2 on, between the vector work of B(NB - 1, 1); Y(NB) runs the
+  // rest. The ring of C(NB - 1) is warmed at the start of X(NB).
+  constexpr int CX = (NU / 2 - 1 < 2 * DB) ? NU / 2 - 1 : 2 * DB;
+  // unit v of A(b): S (v even) or dP (v odd) for k-step v / 2, fetching the
+  // Q / dO rows of k-step v / 2 + PF first
+  auto a_unit = [&](int b, int v) {
+    const int kk = v / 2, j = v & 1;
+    if (j == 0 && kk + PF < KK) load_rows(b, kk + PF);
+    f32x16& acc = j ? dacc[b & 1] : sacc[b & 1];
+    if (kk == 0)
+      mfma_score0(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
+    else
+      mfma_score(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
+  };
+  // Likewise Y(0) has no C MFMAs: it runs the first AY units of A(1), one every
+  // other unit from unit 2 on, and X(1) the rest (every other unit, and the last
+  // unit). Block 1's first rows are fetched at the end of X(0).
+  constexpr int AY = NU / 2 - 1;
+  static_assert(NB >= 2, "the head start of A(1) needs a second block");
 
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) load_rows(0, kk);
@@ -265,22 +297,31 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
   for (int b = 0; b <= NB; ++b) {
     // ---- X(b): A(b), B(b - 1, 1) ----
     if (b < NB) load_rowvals(b, 0);  // lse2 / Delta of B(b, 0), a phase ahead
+    if (b == NB) {
+#pragma unroll
+      for (int w = 0; w < RV - 1; ++w) load_tr(b - 1, w);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int kk = u / 2, j = u & 1;
-      if (b < NB) {
-        if (j == 0 && kk + PF < KK) load_rows(b, kk + PF);
-        f32x16& acc = j ? dacc[b & 1] : sacc[b & 1];
-        if (kk == 0)
-          mfma_score0(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
-        else
-          mfma_score(acc, as_bf16x8(fr[kk % (PF + 1)][j]), j ? vf[kk] : kf[kk]);
+      if (b < NB && b != 1) a_unit(b, u);
+      if (b == 1) {
+        const int v = (j == 0) ? AY + kk : (u == NU - 1 ? NU - 1 : -1);
+        if (v >= 0) a_unit(1, v);
+      }
+      if (b == NB && u >= 2 && j == 0 && kk - 1 < CX) {
+        if (kk - 1 + RV - 1 < NU) load_tr(b - 1, kk - 1 + RV - 1);
+        c_unit(b - 1, kk - 1);
       }
       if (b >= 1) b_share(b - 1, 1, u);
       // warm the ring of C(b - 1) in the last units
-      if (b >= 1 && u >= NU - (RV - 1)) load_tr(b - 1, u - (NU - (RV - 1)));
+      if (b >= 1 && b < NB && u >= NU - (RV - 1)) load_tr(b - 1, u - (NU - (RV - 1)));
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (b == 0) {
+#pragma unroll
+      for (int kk = 0; kk < PF; ++kk) load_rows(1, kk);
     }
     if (b < NB) s_fence_scores(sacc[b & 1], dacc[b & 1]);
     if (b >= 1) b_tail(b - 1, 1);
@@ -295,16 +336,16 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
         *reinterpret_cast<uint4*>(dsrow + 32 * (b - 1) + 16 * u) = make_uint4(w[0], w[1], w[2], w[3]);
       }
       if (b >= 1) {
-        if (u + RV - 1 < NU) load_tr(b - 1, u + RV - 1);
-        const int ks = u / (2 * DB), db = (u / 2) % DB;
-        const uint32_t* wv = (u & 1) ? sw[(b - 1) & 1][ks] : pw[(b - 1) & 1][ks];
-        const bf16x8 bop = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
-        f32x16& acc = (u & 1) ? dk[db] : dv[db];
-        acc = mfma32x32x16(va[u % RV], bop, acc);
+        const int w = (b == NB) ? u + CX : u;  // C(NB - 1)'s first CX units ran in X(NB)
+        if (w < NU) {
+          if (w + RV - 1 < NU) load_tr(b - 1, w + RV - 1);
+          c_unit(b - 1, w);
+        }
       }
+      if (b == 0 && u >= 2 && (u & 1) == 0 && u / 2 - 1 < AY) a_unit(1, u / 2 - 1);
       if (b < NB) b_share(b, 0, u);
-      // the first Q / dO row k-steps of the next block
-      if (b + 1 < NB && u >= NU - PF) load_rows(b + 1, u - (NU - PF));
+      // the first Q / dO row k-steps of the next block (block 1's: end of X(0))
+      if (b >= 1 && b + 1 < NB && u >= NU - PF) load_rows(b + 1, u - (NU - PF));
       __builtin_amdgcn_sched_barrier(0);
     }
     if (b < NB) b_tail(b, 0);
