@@ -186,11 +186,13 @@ constexpr int kSchedValu = 0x002;
 // STORE: the first two units of Y(b) also write dS of block b - 1 (16 bytes per
 // lane and k-step: this lane's key, 8 consecutive query rows) to the stored-dS
 // row `dsrow` (this lane's key, query row m0 + 8 half), for the dQ kernel.
-template <int D, bool MASK, bool LEFT, bool STORE>
+// x0(u) runs in unit u of X(0), whose MFMAs have no vector work beside them:
+// the kernel issues the next stage's copies there.
+template <int D, bool MASK, bool LEFT, bool STORE, class X0>
 __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dOs, const float* lse2_s,
                                           const float* dlt_s, const bf16x8* kf, const bf16x8* vf, f32x16* dk,
                                           f32x16* dv, float c, int m0, int rlo, int rhi, const OperandOffsets<D>& off,
-                                          int half, uint16_t* dsrow, bool kvalid) {
+                                          int half, uint16_t* dsrow, bool kvalid, const X0& x0) {
   using T = DkdvCfg<D>;
   constexpr int KK = D / 16, DB = D / 32, NB = T::BMQ / 32, PF = 2, RV = 3;
   constexpr int NU = 2 * KK;  // MFMA units per phase
@@ -306,6 +308,7 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
     for (int u = 0; u < NU; ++u) {
       const int kk = u / 2, j = u & 1;
       if (b < NB && b != 1) a_unit(b, u);
+      if (b == 0) x0(u);  // the caller's work for unit u of X(0) (the next stage's copies)
       if (b == 1) {
         const int v = (j == 0) ? AY + kk : (u == NU - 1 ? NU - 1 : -1);
         if (v >= 0) a_unit(1, v);
@@ -451,7 +454,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto stage_in = [&](int it) {
     wait_vmcnt<0>();
     lds_barrier();
-    if (it + 1 < total) issue(it + 1, lds0 + ((it + 1) & 1) * T::STAGE);
   };
   int it = 0;
   // stored dS: this lane's key row of query head g r (the group's first head),
@@ -467,9 +469,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int m0 = (sfirst + st) * T::BMQ;
     const lds_char* stg = lds + (it & 1) * T::STAGE;
     const float* f32 = reinterpret_cast<const float*>(smem) + ((it & 1) * T::STAGE + T::F32) / 4;
+    // the copies of stage it + 1, one or two per unit of the step's first phase
+    static_assert(T::DMA_PER_WAVE <= D / 8 && T::F32_DMAS <= D / 8, "copies fit the units of X(0)");
+    const bool next = it + 1 < total;
+    const int h1 = g * r + (it + 1) / nsteps;
+    const int m1 = (sfirst + (it + 1) % nsteps) * T::BMQ;
+    const int64_t qoff1 = ((int64_t)cq * p.Hq + h1) * D;
+    const int64_t roff1 = (int64_t)h1 * p.total_q + cq;
+    const uint32_t stage1 = lds0 + ((it + 1) & 1) * T::STAGE;
+    auto x0 = [&](int u) {
+      if (!next) return;
+      if (u < T::DMA_PER_WAVE) {
+        const int qd = wave * T::DMA_PER_WAVE + u;
+        const bool is_do = qd >= T::QT::DMAS;
+        const i32x4 rs = head_rows_rsrc<D>((is_do ? p.dout : p.q) + qoff1, Lq, pitch);
+        tile_dma<D, T::BMQ>(stage1 + (is_do ? T::TILE : 0), rs, pitch, m1, is_do ? qd - T::QT::DMAS : qd, lane);
+      }
+      if (u < T::F32_DMAS && wave < 2) {  // lse2 rows on wave 0, Delta rows on wave 1
+        const i32x4 rs = make_rsrc((wave == 0 ? p.lse2 : p.delta) + roff1, (uint32_t)Lq * 4u);
+        rows64_f32_dma(stage1 + T::F32 + (wave == 0 ? 0 : 4 * T::BMQ) + 256 * u, rs, m1 + 64 * u, lane);
+      }
+    };
     dkdv_step<D, decltype(masked)::value, LEFT, STORE>(stg, stg + T::TILE, f32, f32 + T::BMQ, kf, vf, dk, dv, c, m0,
                                                       rlo, rhi, off, half,
-                                                      STORE ? ds_key + hg * ds_plane + m0 : nullptr, kvalid);
+                                                      STORE ? ds_key + hg * ds_plane + m0 : nullptr, kvalid, x0);
     ++it;
   };
   for (int hg = 0; hg < (total > 0 ? r : 0); ++hg) {
