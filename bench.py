@@ -156,6 +156,36 @@ def time_graph(fn, steps: int, warmup: int):
     return time_steps(g.replay, steps, warmup)
 
 
+def time_graph_steps(fn, steps: int, warmup: int):
+    """Capture `steps` back-to-back calls of fn in one HIP graph (after eager
+    warm-up, and one untimed replay), then time one replay of it bracketed by
+    synchronizations. Returns (wall ms per call, event ms per call): the steps
+    run back to back as in a training loop, without the per-replay dispatch gap
+    of a one-step graph."""
+    import torch
+
+    for _ in range(max(3, warmup)):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / max(1, steps)
+    return wall, s.elapsed_time(e) / max(1, steps)
+
+
 def time_graph_steady(fn, reps: int = 10, rounds: int = 5):
     """Per-call ms of `reps` back-to-back calls captured in one HIP graph (median
     over rounds): the steady-state rate without per-launch dispatch gaps."""
@@ -372,7 +402,9 @@ def run_workload(wl, steps, warmup, profile=True, stored_ds=False):
         recs = A.attn_varlen_profile_records()
     # 2) the same work replayed from HIP graphs: no host launch overhead
     fwd_ms, fwd_per = time_graph(fwd, steps, warmup)
-    step_ms, step_per = time_graph(step, steps, warmup)
+    step_single_ms, step_per = time_graph(step, steps, warmup)
+    # the step figure: all timed steps back to back in one graph
+    step_ms, step_event_ms = time_graph_steps(step, steps, warmup)
     # the forward figure: event-timed, ten forwards back to back in one graph
     # (per call, median of five rounds), free of the per-launch dispatch gap
     # that a single-kernel graph replay adds
@@ -383,7 +415,9 @@ def run_workload(wl, steps, warmup, profile=True, stored_ds=False):
     res["fwd_ms_single_replay_median"] = statistics.median(fwd_per)
     res["fwd_tflops_single_replay"] = fwd_flop / (fwd_ms * 1e-3) / 1e12
     res["step_ms"] = step_ms
-    res["step_ms_median"] = statistics.median(step_per)
+    res["step_ms_event"] = step_event_ms
+    res["step_ms_single_replay"] = step_single_ms
+    res["step_ms_single_replay_median"] = statistics.median(step_per)
     res["fwdbwd_tflops"] = 3.5 * fwd_flop / (step_ms * 1e-3) / 1e12
     res["eager_step_ms"] = eager_step_ms
     # per-kernel averages over the timed eager steps (the session also saw the
@@ -1030,12 +1064,16 @@ def main(argv=None):
         # chip held (power-limited) while running the step
         "frac_of_peak_fwdbwd_at_sclk": (res["fwdbwd_tflops"] / (PEAK_BF16_TFLOPS * clocks["sclk_mhz_mean"] / 2400.0)
                                         if "sclk_mhz_mean" in clocks else None),
-        "step_ms_median": res["step_ms_median"],
+        "step_ms_event": res["step_ms_event"],
+        "step_ms_single_replay": res["step_ms_single_replay"],
+        "step_ms_single_replay_median": res["step_ms_single_replay_median"],
         "fwd_ms_single_replay_median": res["fwd_ms_single_replay_median"],
         "eager_step_ms": res["eager_step_ms"],
-        "timing": ("value: HIP graph replays of one step (forward with LSE, then backward), host wall clock over "
-                   "the timed replays bracketed by synchronizations; per-kernel times from eager steps with "
-                   "library events on the launch stream"),
+        "timing": ("value / ms_per_step: the K timed steps (forward with LSE, then backward) captured back to "
+                   "back in one HIP graph, host wall clock over one replay of it bracketed by synchronizations "
+                   "(step_ms_event: HIP events around the same replay). step_ms_single_replay: a graph of one "
+                   "step replayed K times, which adds the per-replay dispatch gap. Per-kernel times from eager "
+                   "steps with library events on the launch stream"),
         "kernels": kern,
         "roofline": roofline,
         "gemm_reference": gemm,
