@@ -23,6 +23,7 @@ guide's Public API.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -83,6 +84,22 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _on_input_device(fn):
+    """Run fn with its first device tensor argument's device current: the library
+    launches on the current HIP device, and its stream argument is that device's
+    current stream."""
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        for a in args:
+            if isinstance(a, torch.Tensor) and a.is_cuda:
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+
+    return wrapped
+
+
 def _check_bf16(name: str, t: torch.Tensor, dev: torch.device):
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
@@ -99,6 +116,7 @@ SEQLEN_BITS = {1: "a first cu_seqlens entry is not 0", 2: "cu_seqlens decreases"
                8: "a sequence is longer than its max_seqlen"}
 
 
+@_on_input_device
 def attn_varlen_validate_seqlens(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, total_q: int, total_k: int,
                                  max_seqlen_q: int, max_seqlen_k: int) -> int:
     """Check the packing arrays on the device (waits for the result): returns 0 when valid, else the
@@ -140,6 +158,7 @@ def _check_inputs(q, k, v, cu_q, cu_k):
     return dev
 
 
+@_on_input_device
 def attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                     softmax_scale: Optional[float] = None, causal: bool = False, return_lse: bool = False,
@@ -276,6 +295,7 @@ def bwd_workspace_bytes(num_seqs: int, total_q: int, total_k: int, max_seqlen_q:
     return attn_varlen_bwd_workspace_size(num_seqs, total_q, total_k, n_q_heads, n_kv_heads, head_dim)
 
 
+@_on_input_device
 def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                     lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                     max_seqlen_k: int, softmax_scale: Optional[float] = None, causal: bool = False,
@@ -343,6 +363,7 @@ def attn_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: tor
 NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_VARLEN_NOALLOC_SCRATCH_BYTES
 
 
+@_on_input_device
 def attn_varlen_bwd_noalloc(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             out: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
                             cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
@@ -414,6 +435,7 @@ def attn_varlen_tile_plan_host(kind: int, head_dim: int, seqlen_q: int, seqlen_k
     return dict(zip(keys, list(plan)))
 
 
+@_on_input_device
 def attn_varlen_schedule_device(cu_seqlens_q: torch.Tensor, max_seqlen_q: int, block_m: int, count: int):
     """Device ranking of the first ``count`` ranks (the decode the kernels run)."""
     dev = cu_seqlens_q.device

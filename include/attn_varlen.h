@@ -44,8 +44,9 @@
  * when its size is 0. The cu_seqlens arrays are never NULL.
  *
  * Execution: calls are asynchronous on `stream` (a hipStream_t, passed as void*;
- * NULL is the default stream) and never synchronise the host. They are
- * re-entrant and stateless. Identical inputs give bit-identical outputs (no
+ * NULL is the default stream) and never synchronise the host. They run on the
+ * calling thread's current HIP device: `stream` and every buffer must belong to
+ * it. They are re-entrant and stateless. Identical inputs give bit-identical outputs (no
  * atomics; every reduction runs in a fixed order).
  *
  * Errors: 0 on success, a negative ATTN_VARLEN_ERR_* code otherwise. Every
