@@ -419,6 +419,7 @@ def attn_varlen_schedule_host(cu_seqlens_q, block_m: int):
 
 
 PLAN_FWD, PLAN_DQ, PLAN_DKDV = 0, 1, 2  # ATTN_VARLEN_PLAN_*
+PLAN_GROUP2, PLAN_GROUP4 = 0x10, 0x20  # or-ed into FWD / DQ: blocks of 2 / 4 heads x 64 / 32 rows
 
 
 def attn_varlen_tile_plan_host(kind: int, head_dim: int, seqlen_q: int, seqlen_k: int, causal: bool,

@@ -364,8 +364,14 @@ int attn_varlen_tile_plan_host(int32_t kind, int32_t head_dim, int32_t seqlen_q,
   const int wr = causal ? 0 : wr0;
   const bool band = wl >= 0 || wr >= 0;
   for (int i = 0; i < 8; ++i) plan[i] = 0;
+  const int group = kind & (ATTN_VARLEN_PLAN_GROUP2 | ATTN_VARLEN_PLAN_GROUP4);
+  kind &= ~(ATTN_VARLEN_PLAN_GROUP2 | ATTN_VARLEN_PLAN_GROUP4);
+  if (group == (ATTN_VARLEN_PLAN_GROUP2 | ATTN_VARLEN_PLAN_GROUP4)) return ATTN_VARLEN_ERR_BAD_FLAG;
+  if (group != 0 && kind != ATTN_VARLEN_PLAN_FWD && kind != ATTN_VARLEN_PLAN_DQ) return ATTN_VARLEN_ERR_BAD_FLAG;
   if (kind == ATTN_VARLEN_PLAN_FWD || kind == ATTN_VARLEN_PLAN_DQ) {
-    const int bm = av::kQueryBlock, bn = av::key_tile(head_dim);
+    // the kernels' block: block_heads(r) heads of kQueryBlock / block_heads(r) rows
+    const int heads = group == ATTN_VARLEN_PLAN_GROUP4 ? 4 : group == ATTN_VARLEN_PLAN_GROUP2 ? 2 : 1;
+    const int bm = av::kQueryBlock / heads, bn = av::key_tile(head_dim);
     if (block < 0 || block >= av::ceil_div(Lq, bm)) return ATTN_VARLEN_ERR_BAD_SEQLEN;
     const int q0 = block * bm - av::query_lead(Lq, bm, bn);
     // the kernels' ranges: plain attention visits every key tile and masks the

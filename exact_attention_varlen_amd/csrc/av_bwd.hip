@@ -19,9 +19,10 @@
 //                         dV += P^T dO, dK += dS^T Q.
 //                       The sum over the group's query heads happens in fp32
 //                       registers in a fixed order: no atomics, no scratch.
-//  3. bwd_dq_kernel     query-stationary: a workgroup owns 128 query rows of one
-//                       head and loops over the visible 64-key tiles in
-//                       ascending order: dQ += dS K.
+//  3. bwd_dq_kernel     query-stationary: a workgroup owns 32 query rows per
+//                       wave, of hw = block_heads(group size) query heads of one
+//                       KV group (128 / hw rows of each), and loops over the
+//                       visible 64-key tiles in ascending order: dQ += dS K.
 // dQ and dK are scaled by softmax_scale at the end. Head dim 256 uses the
 // main kernels of av_bwd_d256.hip after the same preprocess.
 //
@@ -519,7 +520,7 @@ template <int D>
 struct DqCfg {
   using KV = RowTile<D, 64>;
   static constexpr int NT = 256;
-  static constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+  static constexpr int BM = 128;  // query rows x heads per workgroup (32 rows per wave)
   static constexpr int BN = 64;   // keys per tile
   static constexpr int ROW = KV::ROW;
   static constexpr int TILE = KV::BYTES;
@@ -605,13 +606,16 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   extern __shared__ __align__(16) uint16_t smem[];
   lds_char* lds = (lds_char*)smem;
 
+  // the workgroup covers hw heads of one KV group, bm rows of each (as the forward)
   const int r = p.Hq / p.Hkv;
-  const int64_t L = xcd_logical(blockIdx.x, r);
-  const int rank = (int)(L / p.Hq);
-  const int h = (int)(L % p.Hq);
+  const int hw = block_heads(r), hwl = log2_small(hw), bm = T::BM / hw;
+  const int64_t L = xcd_logical(blockIdx.x, r >> hwl);
+  const int heads = p.Hq >> hwl;
+  const int rank = (int)(L / heads);
+  const int hs = (int)(L % heads);
   Item item;
-  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, T::BM, p.levels, rank, item)) return;
-  const int g = h / r;
+  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, bm, p.levels, rank, item)) return;
+  const int g = (hs << hwl) / r;
   const int mblk = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
 
   const int tid = threadIdx.x;
@@ -619,9 +623,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int h = (hs << hwl) + (wave & (hw - 1));
   // query blocks aligned toward the end of the sequence, as in the forward
-  const int q0 = mblk * T::BM - query_lead(Lq, T::BM, T::BN);
-  const int qi = q0 + wave * 32 + col;
+  const int q0 = mblk * bm - query_lead(Lq, bm, T::BN);
+  const int qi = q0 + (wave >> hwl) * 32 + col;
   const bool qvalid = qi >= 0 && qi < Lq;
   const int qa = qvalid ? qi : 0;  // a valid row for address arithmetic
 
@@ -629,7 +634,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::WAVES_PER_SIMD) void bwd_dq_kernel(B
   // ones (the band's left edge before, its right edge and the sequence end after)
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + bm, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
     t_lo = ts.lo;
     t_hi = ts.hi;
     f_lo = ts.full_lo;
@@ -972,12 +977,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
     }
     return e;
   };
-  auto run_dq = [&](auto kern, size_t lds_bytes, std::atomic<uint64_t>& lds_set, const char* name) -> hipError_t {
+  // hw: query heads per workgroup (the recomputing dQ kernel groups a KV
+  // group's heads as the forward does; the stored-dS one takes one head)
+  auto run_dq = [&](auto kern, size_t lds_bytes, std::atomic<uint64_t>& lds_set, const char* name,
+                    int hw) -> hipError_t {
     hipError_t e = lds_limit_once(kern, lds_bytes, lds_set);
     if (e != hipSuccess) return e;
     BwdParams pq = p;
-    pq.levels = ceil_div(f.max_q, kQueryBlock);
-    const int64_t grid = grid_for(f.total_q, f.num_seqs, kQueryBlock, f.Hq, f.Hq / f.Hkv);
+    const int bm = kQueryBlock / hw, hwl = log2_small(hw);
+    pq.levels = ceil_div(f.max_q, bm);
+    const int64_t grid = grid_for(f.total_q, f.num_seqs, bm, f.Hq >> hwl, (f.Hq / f.Hkv) >> hwl);
     if (grid > 0 && pq.levels > 0) {
       prof_begin(name, stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, stream, pq);
@@ -994,14 +1003,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
     if (e == hipSuccess) e = run_dkdv(std::true_type());
     static std::atomic<uint64_t> lds_set{0};
     if (e == hipSuccess)
-      e = run_dq(bwd_dq_ds_kernel<D, BAND, LEFT>, DqDsCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq_ds");
+      e = run_dq(bwd_dq_ds_kernel<D, BAND, LEFT>, DqDsCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq_ds", 1);
     return e;
   }
   // recomputing dQ: the dQ kernel first, which also writes the Delta / lse2 rows
   // that dK / dV reads
   if (f.total_q > 0) {
     static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = run_dq(bwd_dq_kernel<D, BAND, LEFT>, DqCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq");
+    const hipError_t e =
+        run_dq(bwd_dq_kernel<D, BAND, LEFT>, DqCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq", block_heads(f.Hq / f.Hkv));
     if (e != hipSuccess) return e;
   }
   if (f.total_k > 0) return run_dkdv(std::false_type());

@@ -20,7 +20,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   }
   FwdParams p = fwd_params(a, T::BM);
   const int r = a.Hq / a.Hkv;
-  const int64_t grid = grid_for(a.total_q, a.num_seqs, T::BM, a.Hq, r);
+  const int64_t grid = grid_for(a.total_q, a.num_seqs, p.bm, a.Hq >> p.hw_log2, r >> p.hw_log2);
   if (grid == 0 || p.levels == 0) return hipSuccess;
   hipStream_t stream = (hipStream_t)a.stream;
   prof_begin("attn_fwd", stream);

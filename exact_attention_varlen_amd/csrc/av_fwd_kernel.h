@@ -9,8 +9,9 @@
 // Abstractions (online softmax; causal block ranges; varlen offsets). The
 // result is the exact softmax(QK^T * scale + mask) V of each packed sequence.
 //
-// gfx950 design (one workgroup = BM / 32 waves = one query block of BM rows of
-// one query head; each wave owns 32 query rows):
+// gfx950 design (one workgroup = BM / 32 waves sharing every K / V tile; each
+// wave owns 32 query rows of one query head; the waves cover hw heads of one
+// KV group and BM / hw rows of each, hw = block_heads(group size)):
 //  * Q^T stays in VGPRs for the whole item as the B operand of S^T = K Q^T.
 //  * K and V tiles of 64 keys go HBM -> LDS with buffer_load ... lds (no VGPR
 //    staging, out-of-range rows read as zero) into separate double buffers.
@@ -111,7 +112,12 @@ struct FwdParams {
   int total_q;
   int Hq;
   int Hkv;
-  int levels;        // ceil(max_seqlen_q / BM)
+  // A workgroup's waves cover hw query heads of one KV group (hw divides both
+  // the group size and the wave count) and, for each, bm = 32 waves / hw query
+  // rows; hw_log2 = log2(hw). With hw > 1 the causal diagonal of a block
+  // crosses fewer key tiles.
+  int hw, hw_log2, bm;
+  int levels;        // ceil(max_seqlen_q / bm)
   float scale_log2;  // |softmax_scale| * log2(e), at least FLT_MIN
   int neg_scale;     // softmax_scale < 0: Q is negated so the scale is positive
   int wl, wr;        // visible band of a row (keys i + Lk - Lq - wl .. + wr; < 0: unbounded)
@@ -498,21 +504,22 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   constexpr int NA = T::NA;
 
   const int r = p.Hq / p.Hkv;
-  const int h = (int)(L % p.Hq);
+  const int heads = p.Hq >> p.hw_log2;  // head sets of hw heads
+  const int hs = (int)(L % heads);
   int rank, split = 0;
   if (SPLIT) {
-    const int64_t unit = L / p.Hq;
+    const int64_t unit = L / heads;
     split = (int)(unit % p.splits);
     rank = (int)(unit / p.splits);
   } else {
-    rank = (int)(L / p.Hq);
+    rank = (int)(L / heads);
   }
   Item item;
-  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, T::BM, p.levels, rank, item)) {
+  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, p.bm, p.levels, rank, item)) {
     hook();
     return;
   }
-  const int g = h / r;
+  const int g = (hs << p.hw_log2) / r;
   const int mblk = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
 
   FwdCtx<D, BM, BN, MODE> x;
@@ -530,13 +537,16 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   x.half = lane >> 5;
+  // this wave's query head and 32-row part of the block
+  const int h = (hs << p.hw_log2) + (x.wave & (p.hw - 1));
+  const int wrow = (x.wave >> p.hw_log2) * 32;
   // query blocks are aligned toward the end of the sequence: the first block
   // starts `lead` rows before row 0 (the padding of the last block rounded
   // down to whole key tiles), so that a partial block is mostly the first one,
   // which under a causal mask sees the fewest keys, while block starts stay on
   // the key-tile grid (a block's causal diagonal then crosses BM / BN tiles)
-  const int q0 = mblk * T::BM - query_lead(Lq, T::BM, T::BN);
-  const int qi = q0 + x.wave * 32 + (lane & 31);  // this lane's query row (sequence-relative)
+  const int q0 = mblk * p.bm - query_lead(Lq, p.bm, T::BN);
+  const int qi = q0 + wrow + (lane & 31);  // this lane's query row (sequence-relative)
   const bool qvalid = qi >= 0 && qi < Lq;
 
   // key tiles of this block, [t_lo, t_hi), and the unmasked ones among them,
@@ -544,7 +554,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int64_t L, uint16_t
   constexpr bool BAND = MODE > 0;
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + p.bm, Lq) - 1, T::BN, Lq, Lk, MODE == 2 ? p.wl : -1, p.wr);
     t_lo = ts.lo;
     t_hi = ts.hi;
     f_lo = ts.full_lo;
@@ -738,7 +748,7 @@ template <int D, int BM, int BN, int MODE, bool WRITE_LSE, bool SPLIT = false>
 __global__ __launch_bounds__((FwdCfg<D, BM, BN>::NT), (FwdCfg<D, BM, BN>::MIN_BLOCKS_PER_CU)) void fwd_kernel(
     FwdParams p) {
   extern __shared__ __align__(16) uint16_t smem[];
-  fwd_item<D, BM, BN, MODE, WRITE_LSE, SPLIT>(p, xcd_logical(blockIdx.x, p.Hq / p.Hkv), smem);
+  fwd_item<D, BM, BN, MODE, WRITE_LSE, SPLIT>(p, xcd_logical(blockIdx.x, (p.Hq / p.Hkv) >> p.hw_log2), smem);
 }
 
 // Persistent scheduling (FlashAttention repository guide, Core Abstractions:
@@ -764,7 +774,7 @@ fwd_kernel_persistent(FwdParams p, unsigned int n_items) {
   // then thread 0's count of queues found empty so far
   // (plain LDS accesses: the barriers order them)
   int* slot = reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + T::LDS_BYTES);
-  const unsigned int r = (unsigned int)(p.Hq / p.Hkv);
+  const unsigned int r = (unsigned int)((p.Hq / p.Hkv) >> p.hw_log2);  // items per KV group and block
   const unsigned int per_queue = n_items / kNumXcd;  // items per queue (whole groups)
   // thread 0, tested without keeping the thread index live across the loop
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -835,7 +845,11 @@ inline FwdParams fwd_params(const FwdArgs& a, int bm) {
   p.total_q = (int)a.total_q;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
-  p.levels = ceil_div(a.max_q, bm);
+  static_assert(FwdCfg<128, kQueryBlock, 64>::WAVES == 4, "block_heads assumes four waves");
+  p.hw = (bm == kQueryBlock) ? block_heads(a.Hq / a.Hkv) : 1;
+  p.hw_log2 = log2_small(p.hw);
+  p.bm = bm / p.hw;
+  p.levels = ceil_div(a.max_q, p.bm);
   // a zero (or tiny) scale becomes the smallest normal float: the scores then
   // all map to exp2(~0) = 1 as for scale 0, while masked scores (-inf) stay -inf
   p.scale_log2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);

@@ -175,6 +175,13 @@ AV_HD inline void left_edge_tiles(int t_lo, int t_hi, int f_lo, int f_hi, int wl
 // keys against query steps of query_step(D) rows.
 constexpr int kQueryBlock = 128;
 constexpr int kKeyBlock = 128;
+// Query heads per forward / dQ workgroup: the workgroup's four 32-row waves
+// cover block_heads(r) heads of one KV group (r heads) and kQueryBlock /
+// block_heads(r) rows of each. Grouping heads keeps the block's rows few, so a
+// causal diagonal crosses fewer key tiles, while the waves still share every
+// K / V tile.
+AV_HD constexpr int block_heads(int r) { return r % 4 == 0 ? 4 : r % 2 == 0 ? 2 : 1; }
+AV_HD constexpr int log2_small(int x) { return x >= 4 ? 2 : x >= 2 ? 1 : 0; }
 AV_HD constexpr int key_tile(int D) { return D <= 128 ? 64 : 32; }
 AV_HD constexpr int query_step(int D) { return D <= 128 ? 128 : 32; }
 

@@ -390,6 +390,13 @@ int attn_varlen_schedule_device(const int32_t* cu_seqlens_q, int32_t num_seqs, i
  *   kind        ATTN_VARLEN_PLAN_FWD  query block `block` of the forward kernel
  *               ATTN_VARLEN_PLAN_DQ   query block `block` of the dQ kernel
  *               ATTN_VARLEN_PLAN_DKDV key block `block` of the dK / dV kernel
+ *               FWD or DQ may be or-ed with ATTN_VARLEN_PLAN_GROUP2 or
+ *               ATTN_VARLEN_PLAN_GROUP4: the blocks these kernels take when the
+ *               KV group size (n_q_heads / n_kv_heads) is a multiple of 2 but
+ *               not of 4, or a multiple of 4. A workgroup then covers 2 or 4
+ *               query heads of one KV group and 64 or 32 rows of each; without
+ *               a flag it covers one head and 128 rows. (The dQ kernel that
+ *               reads stored dS always takes one head and 128 rows.)
  *   head_dim    64, 128 or 256 (tile shapes depend on it)
  *   seqlen_q, seqlen_k, causal, window_left, window_right
  *               the sequence and its mask, as in attn_varlen_fwd_window
@@ -411,6 +418,8 @@ int attn_varlen_schedule_device(const int32_t* cu_seqlens_q, int32_t num_seqs, i
 #define ATTN_VARLEN_PLAN_FWD 0
 #define ATTN_VARLEN_PLAN_DQ 1
 #define ATTN_VARLEN_PLAN_DKDV 2
+#define ATTN_VARLEN_PLAN_GROUP2 0x10
+#define ATTN_VARLEN_PLAN_GROUP4 0x20
 int attn_varlen_tile_plan_host(int32_t kind, int32_t head_dim, int32_t seqlen_q, int32_t seqlen_k, int32_t causal,
                                int32_t window_left, int32_t window_right, int32_t block, int32_t* plan);
 

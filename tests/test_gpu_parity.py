@@ -431,24 +431,39 @@ def test_varlen_equals_separate_calls(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_gqa_equals_mha_with_repeated_kv(causal):
-    Hq, Hkv = 8, 2
+@pytest.mark.parametrize("Hkv", [2, 4])
+def test_gqa_equals_mha_with_repeated_kv(causal, Hkv):
+    """Grouped-query attention is attention of each query head against its
+    group's KV head, which equals plain multi-head attention with every KV head
+    repeated over its group. The LSE agrees bit for bit: each row visits its key
+    tiles in the same order with the same fp32 row sums. The kernels put a KV
+    group's heads in one workgroup (4 heads of 32 rows each for the groups of 4
+    here, 2 of 64 for the groups of 2, 1 of 128 for MHA), so the layouts split a sequence's
+    rows into different blocks, and a tile near a block's diagonal may take the
+    masked path, whose P enters the PV product split into two bf16 parts, in one
+    layout and not the other: O and the gradients agree to bf16 rounding."""
+    Hq = 8
     wl = W.Workload("gqa", [400, 250], Hq, Hkv, 64, causal)
     d = to_dev(W.make_inputs(wl))
-    announce(f"gqa vs mha causal={causal}")
+    announce(f"gqa vs mha causal={causal} Hkv={Hkv}")
     out, lse, dq, dk, dv = _run_all(wl, d)
     wm = W.Workload("mha", [400, 250], Hq, Hq, 64, causal)
     dm = dict(d)
     dm["k"] = d["k"].repeat_interleave(Hq // Hkv, dim=1).contiguous()
     dm["v"] = d["v"].repeat_interleave(Hq // Hkv, dim=1).contiguous()
     om, lm, qm, km, vm = _run_all(wm, dm)
-    assert torch.equal(out, om)
     assert torch.equal(lse, lm)
-    assert torch.equal(dq, qm)
+
+    def rel(x, y):
+        return float((x.float() - y.float()).norm() / y.float().norm())
+
+    assert float((out.float() - om.float()).abs().max()) <= 1e-2
+    assert rel(out, om) <= 5e-3
+    assert rel(dq, qm) <= 1e-2
     km = km.float().reshape(km.shape[0], Hkv, Hq // Hkv, -1).sum(2)
     vm = vm.float().reshape(vm.shape[0], Hkv, Hq // Hkv, -1).sum(2)
-    assert float((dk.float() - km).norm() / km.norm()) < 1e-2
-    assert float((dv.float() - vm).norm() / vm.norm()) < 1e-2
+    assert rel(dk, km) < 1e-2
+    assert rel(dv, vm) < 1e-2
 
 
 def test_no_writes_outside_outputs():

@@ -49,7 +49,8 @@ def _check_query_blocks(kind, D, Lq, Lk, causal, window):
     vis = O.visible(Lq, Lk, causal, None, window) if Lq and Lk else np.zeros((Lq, Lk), dtype=bool)
     right_ok = _right_ok(Lq, Lk, causal, window)
     nvis = vis.sum(axis=1)
-    nblocks = -(-Lq // 128)
+    heads = 4 if kind & A.PLAN_GROUP4 else 2 if kind & A.PLAN_GROUP2 else 1
+    nblocks = -(-Lq // (128 // heads))
     covered = np.zeros(Lq, dtype=int)
     for m in range(nblocks):
         p = A.attn_varlen_tile_plan_host(kind, D, Lq, Lk, causal, window[0], window[1], m)
@@ -71,8 +72,9 @@ def _check_query_blocks(kind, D, Lq, Lk, causal, window):
             assert rows[:, k0:k1].all(), tag
         # forward left-edge tiles: no row's right edge or key end inside; rows
         # that reach them see at least a tile of keys
+        assert bm == 128 // heads, tag
         if p["left_edge"]:
-            assert kind == A.PLAN_FWD and window[0] >= 0, tag
+            assert kind & 0xF == A.PLAN_FWD and window[0] >= 0, tag
             k0, k1 = p["lo"] * bn, (p["lo"] + p["left_edge"]) * bn
             assert k1 <= Lk and right_ok[r0:r1, k0:k1].all(), tag
             reach = rows[:, k0:k1].any(axis=1)
@@ -102,13 +104,15 @@ def _check_key_blocks(D, Lq, Lk, causal, window):
 
 
 CASES = [(D, c, w) for D in (64, 128, 256) for c in (False, True) for w in WINDOWS]
+# the forward and dQ blocks for KV groups of one head, of 2 and of 4 (or more)
+QUERY_KINDS = [k | g for k in (A.PLAN_FWD, A.PLAN_DQ) for g in (0, A.PLAN_GROUP2, A.PLAN_GROUP4)]
 
 
 @pytest.mark.parametrize("D,causal,window", CASES, ids=[f"d{D}-{'c' if c else 'f'}-w{w[0]}_{w[1]}"
                                                         for D, c, w in CASES])
 def test_tile_plans_cover_every_visible_pair(D, causal, window):
     for Lq, Lk in itertools.product(LENGTHS, LENGTHS):
-        for kind in (A.PLAN_FWD, A.PLAN_DQ):
+        for kind in QUERY_KINDS:
             _check_query_blocks(kind, D, Lq, Lk, causal, window)
         _check_key_blocks(D, Lq, Lk, causal, window)
 
@@ -122,7 +126,7 @@ def test_tile_plans_random_long():
         causal = bool(rng.integers(0, 2))
         window = tuple(int(rng.choice([-1, int(rng.integers(0, 4)) * 32, int(rng.integers(0, 700))]))
                        for _ in range(2))
-        for kind in (A.PLAN_FWD, A.PLAN_DQ):
+        for kind in QUERY_KINDS:
             _check_query_blocks(kind, D, Lq, Lk, causal, window)
         _check_key_blocks(D, Lq, Lk, causal, window)
 
@@ -139,6 +143,12 @@ def test_tile_plan_argument_errors():
         A.attn_varlen_tile_plan_host(7, 64, 10, 10, False, -1, -1, 0)
     with pytest.raises(E):
         A.attn_varlen_tile_plan_host(A.PLAN_DQ, 64, -1, 10, False, -1, -1, 0)
+    with pytest.raises(E):  # grouped heads apply to query blocks only
+        A.attn_varlen_tile_plan_host(A.PLAN_DKDV | A.PLAN_GROUP4, 64, 10, 10, False, -1, -1, 0)
+    with pytest.raises(E):
+        A.attn_varlen_tile_plan_host(A.PLAN_FWD | A.PLAN_GROUP2 | A.PLAN_GROUP4, 64, 10, 10, False, -1, -1, 0)
+    with pytest.raises(E):  # 32-row blocks: rows 0 .. 39 make two
+        A.attn_varlen_tile_plan_host(A.PLAN_FWD | A.PLAN_GROUP4, 64, 40, 40, False, -1, -1, 2)
 
 
 @pytest.mark.parametrize("field,delta", [("hi", -1), ("lo", 1), ("full_hi", 1), ("full_lo", -1), ("left_edge", 2)])
@@ -157,6 +167,6 @@ def test_checker_catches_a_plan_off_by_one_tile(monkeypatch, field, delta):
         for D, causal, window in [(128, True, (-1, -1)), (64, False, (100, 37)), (256, True, (200, -1)),
                                   (128, False, (130, -1))]:
             for Lq, Lk in itertools.product(LENGTHS, LENGTHS):
-                for kind in (A.PLAN_FWD, A.PLAN_DQ):
+                for kind in QUERY_KINDS:
                     _check_query_blocks(kind, D, Lq, Lk, causal, window)
                 _check_key_blocks(D, Lq, Lk, causal, window)
