@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __res
 
 struct Dq256 {
   static constexpr int NT = 256;
-  static constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+  static constexpr int BM = 128;  // query rows x heads per workgroup (32 rows per wave)
   static constexpr int BN = 32;   // keys per tile
   static_assert(BM == kQueryBlock && BN == key_tile(kD), "tile shapes of the host-side plan");
   using KV = RowTile<kD, BN>;
@@ -528,13 +528,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   extern __shared__ __align__(16) uint16_t smem[];
   lds_char* lds = (lds_char*)smem;
 
+  // the workgroup covers hw heads of one KV group, bm rows of each (as the forward)
   const int r = p.Hq / p.Hkv;
-  const int64_t L = xcd_logical(blockIdx.x, r);
-  const int rank = (int)(L / p.Hq);
-  const int h = (int)(L % p.Hq);
+  const int hw = block_heads(r), hwl = log2_small(hw), bm = T::BM / hw;
+  const int64_t L = xcd_logical(blockIdx.x, r >> hwl);
+  const int heads = p.Hq >> hwl;
+  const int rank = (int)(L / heads);
+  const int hs = (int)(L % heads);
   Item item;
-  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, T::BM, p.levels, rank, item)) return;
-  const int g = h / r;
+  if (!decode_item<false>(p.cu_q, p.cu_k, p.num_seqs, bm, p.levels, rank, item)) return;
+  const int g = (hs << hwl) / r;
   const int mblk = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
 
   const int tid = threadIdx.x;
@@ -542,16 +545,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq256_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int h = (hs << hwl) + (wave & (hw - 1));
   // query blocks aligned toward the end of the sequence, as in the forward
-  const int q0 = mblk * T::BM - query_lead(Lq, T::BM, T::BN);
-  const int qi = q0 + wave * 32 + col;
+  const int q0 = mblk * bm - query_lead(Lq, bm, T::BN);
+  const int qi = q0 + (wave >> hwl) * 32 + col;
   const bool qvalid = qi >= 0 && qi < Lq;
   const int qa = qvalid ? qi : 0;  // a valid row for address arithmetic
 
   // key tiles [t_lo, t_hi), the unmasked ones [f_lo, f_hi)
   int t_lo = 0, t_hi = ceil_div(Lk, T::BN), f_lo = 0, f_hi = Lk / T::BN;
   if (BAND) {
-    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + T::BM, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
+    const TileSpan ts = key_tiles(max(q0, 0), min(q0 + bm, Lq) - 1, T::BN, Lq, Lk, p.wl, p.wr);
     t_lo = ts.lo;
     t_hi = ts.hi;
     f_lo = ts.full_lo;
@@ -684,8 +688,9 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
     hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     BwdParams pq = p;
-    pq.levels = ceil_div(f.max_q, T::BM);
-    const int64_t grid = grid_for(f.total_q, f.num_seqs, T::BM, f.Hq, f.Hq / f.Hkv);
+    const int hw = block_heads(f.Hq / f.Hkv), hwl = log2_small(hw), bm = T::BM / hw;
+    pq.levels = ceil_div(f.max_q, bm);
+    const int64_t grid = grid_for(f.total_q, f.num_seqs, bm, f.Hq >> hwl, (f.Hq / f.Hkv) >> hwl);
     if (grid > 0 && pq.levels > 0) {
       prof_begin("attn_bwd_dq", stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pq);
