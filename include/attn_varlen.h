@@ -43,6 +43,15 @@
  * total_q = 0, and k, v, dk and dv when total_k = 0. A workspace may be NULL
  * when its size is 0. The cu_seqlens arrays are never NULL.
  *
+ * Size limits (ATTN_VARLEN_ERR_BAD_SEQLEN otherwise): total_q and total_k below
+ * 2^31; within one sequence rows are addressed with 32-bit byte offsets that
+ * stay below 2 GiB, tile overruns past the last row included, so
+ * (max_seqlen_q + 128) * n_q_heads * head_dim * 2 and (max_seqlen_k + 64) *
+ * n_kv_heads * head_dim * 2 must be below 2^31 (e.g. at most 262015 tokens in a
+ * sequence with 32 query heads of 128); and the largest launch, (total_q +
+ * total_k) / 64 + 2 * num_seqs blocks of 256 threads per query head, must stay
+ * below 2^32 threads.
+ *
  * Execution: calls are asynchronous on `stream` (a hipStream_t, passed as void*;
  * NULL is the default stream) and never synchronise the host. They run on the
  * calling thread's current HIP device: `stream` and every buffer must belong to

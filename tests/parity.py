@@ -182,3 +182,14 @@ def sample_rows(cu, per_seq: int = 6, extra: int = 64, seed: int = 0, tail_only:
             pick = rng.choice(total, size=min(extra, total), replace=False)
         rows.update(int(x) for x in pick)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def band_subsequence(L: int, s: int, n: int, left: int, right: int):
+    """Tokens [a, e) of a sequence of L queries and L keys that hold, for a band of
+    `left` keys before and `right` after each query's diagonal (right = 0 when
+    causal), every key that query rows [s, s + n) see, every query that sees keys
+    [s, s + n), and every key such a query sees. On that sub-sequence the oracle
+    gives the full problem's O, LSE and dQ of rows [s, s + n) and dK, dV of keys
+    [s, s + n) exactly: the queries and keys involved see the same sets."""
+    assert left >= 0 and right >= 0 and 0 <= s and s + n <= L
+    return max(0, s - left - right), min(L, s + n + left + right)

@@ -425,3 +425,24 @@ def test_stored_ds_call_argument_errors():
     assert need > A.attn_varlen_bwd_workspace_size(1, 64, 64, 4, 2, 128)
     assert l.attn_varlen_bwd_stored_ds(*args, 128, *tail, FAKE, need - 16, None) == E["ATTN_VARLEN_ERR_WORKSPACE"]
     assert l.attn_varlen_bwd_stored_ds(*args, 128, *tail, None, need, None) == E["ATTN_VARLEN_ERR_WORKSPACE"]
+
+
+def longest_sequence(heads: int, head_dim: int, overrun: int) -> int:
+    # one sequence's rows plus the kernels' tile overrun must span < 2 GiB (32-bit buffer offsets)
+    return ((1 << 31) - 1) // (heads * head_dim * 2) - overrun
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 1, 256), (16, 16, 64)])
+def test_sequence_length_limit(Hq, Hkv, D):
+    # tiles run up to 127 query rows (the dK / dV kernel's query steps) and 63 key rows past a sequence's end
+    lq, lk = longest_sequence(Hq, D, 128), longest_sequence(Hkv, D, 64)
+    assert (lq + 128) * Hq * D * 2 < (1 << 31) <= (lq + 129) * Hq * D * 2
+    assert (lk + 64) * Hkv * D * 2 < (1 << 31) <= (lk + 65) * Hkv * D * 2
+    sizes = dict(D=D, Hq=Hq, Hkv=Hkv, total_q=lq + 100, total_k=lk + 100)
+    # at the limit every size check passes: the call stops at the causal flag, checked after them
+    assert fwd_call(max_q=lq, max_k=lk, causal=2, **sizes) == E["ATTN_VARLEN_ERR_BAD_FLAG"]
+    assert bwd_call(max_q=lq, max_k=lk, causal=2, **sizes) == E["ATTN_VARLEN_ERR_BAD_FLAG"]
+    # one row more on either side is rejected
+    for mq, mk in ((lq + 1, lk), (lq, lk + 1)):
+        assert fwd_call(max_q=mq, max_k=mk, **sizes) == E["ATTN_VARLEN_ERR_BAD_SEQLEN"]
+        assert bwd_call(max_q=mq, max_k=mk, **sizes) == E["ATTN_VARLEN_ERR_BAD_SEQLEN"]

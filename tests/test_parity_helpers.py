@@ -60,3 +60,39 @@ def test_gradient_column_check_catches_a_few_bad_columns():
     with pytest.raises(AssertionError, match="exactly zero"):
         check_grad(np.full((3, 1, 64), 1e-3), np.zeros((3, 1, 64)), "zero tensor")
     check_grad(np.full((3, 1, 64), 1e-7), np.zeros((3, 1, 64)), "zero tensor, rounding only")
+
+
+@pytest.mark.parametrize("causal,window", [(True, (9, -1)), (False, (6, 11)), (True, (0, -1))])
+def test_band_subsequence_gives_the_full_problems_rows(causal, window):
+    # the oracle on the sub-sequence against the oracle on the whole sequence
+    import oracle.attention as O
+
+    from parity import band_subsequence
+
+    rng = np.random.default_rng(3)
+    L, Hq, Hkv, D, scale = 90, 4, 2, 8, 0.4
+    q, dout = rng.standard_normal((2, L, Hq, D))
+    k, v = rng.standard_normal((2, L, Hkv, D))
+    cu = [0, L]
+    o, lse = O.forward(q, k, v, cu, cu, scale, causal, window=window)
+    dq, dk, dv = O.backward(q, k, v, cu, cu, scale, causal, dout, window=window)
+    right = 0 if causal else window[1]
+    for s, n in [(0, 10), (37, 12), (80, 10), (0, 90)]:
+        a, e = band_subsequence(L, s, n, window[0], right)
+        cs = [0, e - a]
+        o2, lse2 = O.forward(q[a:e], k[a:e], v[a:e], cs, cs, scale, causal, window=window)
+        dq2, dk2, dv2 = O.backward(q[a:e], k[a:e], v[a:e], cs, cs, scale, causal, dout[a:e], window=window)
+        r = slice(s - a, s - a + n)
+        np.testing.assert_allclose(o2[r], o[s:s + n], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse2[:, r], lse[:, s:s + n], rtol=0, atol=1e-12)
+        for x2, x in ((dq2, dq), (dk2, dk), (dv2, dv)):
+            np.testing.assert_allclose(x2[r], x[s:s + n], rtol=0, atol=1e-12)
+        if n < L and a > 0:
+            # a narrower sub-sequence is not enough: the first compared rows lose keys
+            a3 = a + 1
+            cs3 = [0, e - a3]
+            o3, _ = O.forward(q[a3:e], k[a3:e], v[a3:e], cs3, cs3, scale, causal, window=window)
+            dq3, dk3, _ = O.backward(q[a3:e], k[a3:e], v[a3:e], cs3, cs3, scale, causal, dout[a3:e], window=window)
+            r3 = slice(s - a3, s - a3 + n)
+            assert (np.abs(o3[r3] - o[s:s + n]).max() > 1e-9 or np.abs(dk3[r3] - dk[s:s + n]).max() > 1e-9
+                    or np.abs(dq3[r3] - dq[s:s + n]).max() > 1e-9)
