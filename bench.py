@@ -821,6 +821,45 @@ def all_configs_table(include_long: bool):
     return 0
 
 
+def many_docs_table(total: int = 65536):
+    """Forward and forward+backward of batches of equal causal documents (32/8
+    heads, hd128) at a fixed token count, from 16 to 4096 documents: the cost of
+    the work decode as the number of sequences grows (one JSON line each)."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    for n in (16, 64, 65, 256, 1024, 4096):
+        L = total // n
+        wl = W.Workload(f"docs{n}x{L}-gqa32/8-d128-causal", [L] * n, 32, 8, 128, True)
+        log(f"many documents {wl.name}")
+        d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        ws = torch.empty(max(16, bwd_ws_bytes(wl)), dtype=torch.uint8, device="cuda:0")
+
+        def fwd():
+            A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], L, L, wl.softmax_scale,
+                              True, out=out, lse=lse)
+
+        def step():
+            fwd()
+            A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"], L, L,
+                              wl.softmax_scale, True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        fl = wl.accounted_fwd_flop()
+        f_ms = time_graph_steady(fwd, 10, 3)
+        s_ms = time_graph_steady(step, 5, 3)
+        print(json.dumps({"workload": wl.name, "documents": n, "tokens_each": L, "fwd_ms": f_ms,
+                          "fwd_tflops": fl / (f_ms * 1e-3) / 1e12, "fwdbwd_ms": s_ms,
+                          "fwdbwd_tflops": 3.5 * fl / (s_ms * 1e-3) / 1e12}), flush=True)
+        del d, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def kernel_times(rounds: int = 3, steps: int = 8):
     """Per-kernel times (library events, eager forward+backward steps) of one
     workload per head dim, for comparing builds of the library: one JSON line
@@ -941,6 +980,9 @@ def main(argv=None):
     ap.add_argument("--fwd-table", action="store_true",
                     help="only time the forward (with and without the LSE) of one workload per head dim for the "
                          "loaded library build (one JSON line) and exit")
+    ap.add_argument("--many-docs", action="store_true",
+                    help="only time forward and forward+backward of 16 to 4096 equal causal documents at 65536 "
+                         "tokens (one JSON line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
@@ -965,6 +1007,9 @@ def main(argv=None):
     if a.fwd_table:
         warm_gpu()
         return fwd_table()
+    if a.many_docs:
+        warm_gpu()
+        return many_docs_table()
     if a.kernel_times:
         warm_gpu()
         return kernel_times()

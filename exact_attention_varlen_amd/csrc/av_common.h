@@ -222,43 +222,31 @@ __device__ __forceinline__ int seq_blocks(const int32_t* cu, int b, int num_seqs
   return ceil_div(cu[b + 1] - cu[b], bm);
 }
 
-// C(k) = sum_b max(0, nb_b - k), per lane for the lane's own k.
-__device__ __forceinline__ int count_at_least(const int32_t* cu, int num_seqs, int bm, int nb_lane, int k) {
-  const int lane = threadIdx.x & (kWave - 1);
+// C(k) = sum_b max(0, nb_b - k), per lane for the lane's own k; up to 64
+// sequences, nb_lane the block count of sequence `lane`.
+__device__ __forceinline__ int count_at_least(int num_seqs, int nb_lane, int k) {
   int acc = 0;
-  if (num_seqs <= kWave) {
-    for (int bb = 0; bb < num_seqs; ++bb) {
-      const int nb = __builtin_amdgcn_readlane(nb_lane, bb);
-      acc += max(0, nb - k);
-    }
-  } else {
-    for (int base = 0; base < num_seqs; base += kWave) {
-      const int nbc = seq_blocks(cu, base + lane, num_seqs, bm);
-      const int n = min(kWave, num_seqs - base);
-      for (int bb = 0; bb < n; ++bb) {
-        const int nb = __builtin_amdgcn_readlane(nbc, bb);
-        acc += max(0, nb - k);
-      }
-    }
+  for (int bb = 0; bb < num_seqs; ++bb) {
+    const int nb = __builtin_amdgcn_readlane(nb_lane, bb);
+    acc += max(0, nb - k);
   }
   return acc;
 }
 
 __device__ __forceinline__ int highest_bit(uint64_t m) { return 63 - __builtin_clzll(m); }
 
-// Returns false when `rank` is past the last block. Must be called by all 64
-// lanes of a wave (the counts are evaluated with every lane active so that the
-// cross-lane reads see defined values). nb_lane is the block count of sequence
-// `lane` (of sequence `base + lane` for the first 64-sequence slice).
-__device__ inline bool decode_rank_nb(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int nb_lane,
-                                      int& b_out, int& m_out) {
+// Up to 64 sequences. Returns false when `rank` is past the last block. Must be
+// called by all 64 lanes of a wave (the counts are evaluated with every lane
+// active so that the cross-lane reads see defined values). nb_lane is the block
+// count of sequence `lane` (0 past the last sequence).
+__device__ inline bool decode_rank_nb(int num_seqs, int levels, int rank, int nb_lane, int& b_out, int& m_out) {
   const int lane = threadIdx.x & (kWave - 1);
   if (levels <= 0) return false;
   // C(k) falls as k grows; the level of `rank` is the largest k < levels with
   // C(k) > rank. Pass 1: lane t probes k = t * stride.
   int stride = ceil_div(levels, kWave);
   const int k1 = lane * stride;
-  const int c1 = count_at_least(cu, num_seqs, bm, nb_lane, k1);
+  const int c1 = count_at_least(num_seqs, nb_lane, k1);
   const uint64_t mask = __ballot((k1 < levels) && (c1 > rank));
   if (mask == 0) return false;
   int kstar = highest_bit(mask) * stride;
@@ -269,35 +257,131 @@ __device__ inline bool decode_rank_nb(const int32_t* cu, int num_seqs, int bm, i
   while (stride > 1) {
     const int sub = ceil_div(stride, kWave);
     const int k2 = kstar + lane * sub;
-    const int c2 = count_at_least(cu, num_seqs, bm, nb_lane, k2);
+    const int c2 = count_at_least(num_seqs, nb_lane, k2);
     const uint64_t mask2 = __ballot((lane * sub < stride) && (k2 < levels) && (c2 > rank));
     kstar += highest_bit(mask2) * sub;  // lane 0 probes kstar itself, so mask2 != 0
     stride = sub;
   }
   // rank within level kstar: subtract the number of blocks of higher index
-  const int above = count_at_least(cu, num_seqs, bm, nb_lane, kstar + 1);
+  const int above = count_at_least(num_seqs, nb_lane, kstar + 1);
   int j = rank - __builtin_amdgcn_readfirstlane(above);
-  for (int base = 0; base < num_seqs; base += kWave) {
-    const int nbc = base == 0 ? nb_lane : seq_blocks(cu, base + lane, num_seqs, bm);
-    const uint64_t sel = __ballot(nbc > kstar);
-    const int pc = __popcll(sel);
-    if (j < pc) {
-      // position of the (j+1)-th set bit
-      uint64_t s = sel;
-      for (int i = 0; i < j; ++i) s &= s - 1;
-      b_out = base + __builtin_ctzll(s);
-      m_out = kstar;
-      return true;
-    }
-    j -= pc;
-  }
-  return false;
+  const uint64_t sel = __ballot(nb_lane > kstar);
+  if (j >= __popcll(sel)) return false;
+  // position of the (j+1)-th set bit
+  uint64_t bits = sel;
+  for (int i = 0; i < j; ++i) bits &= bits - 1;
+  b_out = __builtin_ctzll(bits);
+  m_out = kstar;
+  return true;
 }
 
+// Sum over the wave's lanes, as a wave-uniform value (all 64 lanes active).
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Exclusive prefix sum over the wave's lanes in lane order (all lanes active).
+__device__ __forceinline__ int wave_excl_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  return inc - x;
+}
+
+// Block counts of sequences first .. first + N - 1, 0 for those at or past
+// `last` (last <= num_seqs). The loads are unconditional, their indices clamped
+// to the array, so no lane-dependent branch is needed.
+template <int N>
+__device__ __forceinline__ void chunk_blocks(const int32_t* cu, int num_seqs, int bm, int first, int last,
+                                             int (&nb)[N]) {
+  int c[N + 1];
+#pragma unroll
+  for (int i = 0; i <= N; ++i) c[i] = cu[min(first + i, num_seqs)];
+#pragma unroll
+  for (int i = 0; i < N; ++i) nb[i] = (first + i < last) ? ceil_div(c[i + 1] - c[i], bm) : 0;
+}
+
+// More than 64 sequences. Lane t owns the consecutive sequences
+// [t S, (t + 1) S), S = ceil(num_seqs / 64), and holds the block counts of the
+// first kDecodeChunk of them in registers (the rest are reloaded in rounds of
+// that size for each count). C(k) is a wave sum of the lanes' partial counts,
+// the level of `rank` is found by bisection over k, and the sequence by a prefix
+// count of each lane's sequences at that level: O(S log(levels)) per wave,
+// instead of O(num_seqs) per probe. Same ranking and contract as decode_rank_nb.
+constexpr int kDecodeChunk = 16;
+__device__ inline bool decode_rank_many(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int& b_out,
+                                        int& m_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (levels <= 0) return false;
+  const int S = ceil_div(num_seqs, kWave);
+  const int rounds = ceil_div(S, kDecodeChunk);
+  const int first = lane * S, last = min(first + S, num_seqs);
+  int held[kDecodeChunk];
+  chunk_blocks(cu, num_seqs, bm, first, last, held);
+  // sum of f(nb) over this lane's sequences
+  auto lane_sum = [&](auto f) {
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < kDecodeChunk; ++i) acc += f(held[i]);
+    for (int r = 1; r < rounds; ++r) {
+      int nb[kDecodeChunk];
+      chunk_blocks(cu, num_seqs, bm, first + r * kDecodeChunk, last, nb);
+#pragma unroll
+      for (int i = 0; i < kDecodeChunk; ++i) acc += f(nb[i]);
+    }
+    return acc;
+  };
+  auto C = [&](int k) { return wave_sum(lane_sum([k](int nb) { return max(0, nb - k); })); };
+  // the level: the largest k < levels with C(k) > rank (C falls as k grows)
+  if (C(0) <= rank) return false;
+  int lo = 0, hi = levels;  // C(lo) > rank; hi == levels or C(hi) <= rank
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (C(mid) > rank) lo = mid;
+    else hi = mid;
+  }
+  const int kstar = lo;
+  // rank within level kstar, then the (j+1)-th sequence with more than kstar blocks
+  const int j = rank - C(kstar + 1);
+  const int own = lane_sum([kstar](int nb) { return nb > kstar ? 1 : 0; });
+  const int before = wave_excl_scan(own);
+  const uint64_t owner_mask = __ballot(j >= before && j < before + own);
+  if (owner_mask == 0) return false;
+  const int owner = __builtin_ctzll(owner_mask);
+  // each lane picks the (j - before + 1)-th of its sequences at this level; only
+  // the owner's pick is taken
+  int want = j - before, b = -1;
+  auto pick = [&](const int (&nb)[kDecodeChunk], int base) {
+#pragma unroll
+    for (int i = 0; i < kDecodeChunk; ++i) {
+      const int hit = nb[i] > kstar ? 1 : 0;
+      b = (hit && want == 0) ? base + i : b;
+      want -= hit;
+    }
+  };
+  pick(held, first);
+  for (int r = 1; r < rounds; ++r) {
+    int nb[kDecodeChunk];
+    chunk_blocks(cu, num_seqs, bm, first + r * kDecodeChunk, last, nb);
+    pick(nb, first + r * kDecodeChunk);
+  }
+  b_out = __builtin_amdgcn_readlane(b, owner);
+  m_out = kstar;
+  return b_out >= 0;
+}
+
+// rank -> (sequence, block) for any number of sequences.
 __device__ inline bool decode_rank(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int& b_out,
                                    int& m_out) {
   const int lane = threadIdx.x & (kWave - 1);
-  return decode_rank_nb(cu, num_seqs, bm, levels, rank, seq_blocks(cu, lane, num_seqs, bm), b_out, m_out);
+  if (num_seqs > kWave) return decode_rank_many(cu, num_seqs, bm, levels, rank, b_out, m_out);
+  return decode_rank_nb(num_seqs, levels, rank, seq_blocks(cu, lane, num_seqs, bm), b_out, m_out);
 }
 
 // A decoded work item: sequence b, block m of its ranked rows, and the
@@ -324,7 +408,7 @@ __device__ inline bool decode_item(const int32_t* cu_q, const int32_t* cu_k, int
       k1 = cu_k[lane + 1];
     }
     const int nb = ceil_div(BY_KEYS ? k1 - k0 : q1 - q0, bm);
-    if (!decode_rank_nb(cu, num_seqs, bm, levels, rank, nb, it.b, it.m)) return false;
+    if (!decode_rank_nb(num_seqs, levels, rank, nb, it.b, it.m)) return false;
     const int b = __builtin_amdgcn_readfirstlane(it.b);
     it.cq = __builtin_amdgcn_readlane(q0, b);
     it.Lq = __builtin_amdgcn_readlane(q1, b) - it.cq;

@@ -79,10 +79,18 @@ def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
 
 
 def check_out(x: np.ndarray, ref: np.ndarray, what: str = "out"):
+    """O against the exact result: max-abs 1e-2 and rel-Frobenius 5e-3. Where
+    |ref| >= 4 half a bf16 spacing (2^-6 and up) already exceeds 1e-2, so no bf16
+    output can meet the absolute bound there; such elements (rows with one or two
+    visible keys hold single V values, and peaked rows come close to them) may
+    differ by 1e-2 beyond half a bf16 spacing. Every other element keeps the
+    plain 1e-2."""
     assert np.all(np.isfinite(x)), f"{what}: non-finite values"
-    mabs = float(np.abs(x - ref).max()) if x.size else 0.0
+    err = np.abs(x - ref)
+    allow = np.where(np.abs(ref) >= 4.0, bf16_half_ulp(ref), 0.0) if x.size else 0.0
+    mabs = float((err - allow).max()) if x.size else 0.0
     rf = rel_fro(x, ref)
-    assert mabs <= OUT_MAX_ABS, f"{what}: max-abs {mabs:.3e} > {OUT_MAX_ABS}"
+    assert mabs <= OUT_MAX_ABS, f"{what}: max-abs {mabs:.3e} > {OUT_MAX_ABS} (beyond bf16 rounding where |O| >= 4)"
     assert rf <= OUT_REL_FRO, f"{what}: rel-Frobenius {rf:.3e} > {OUT_REL_FRO}"
     return mabs, rf
 

@@ -84,6 +84,14 @@ for n, D, causal, seed in ((64, 128, True, 1), (65, 64, False, 2), (65, 128, Tru
                            (150, 128, False, 5)):
     lq, lk = _many_lengths(n, seed)
     MANY_SEQS.append(W.Workload(f"many{n}-d{D}-{'c' if causal else 'f'}", lq, 4, 2, D, causal, seqlens_k=lk))
+# Past 1024 sequences each lane of the decode owns more than 16 of them (block
+# counts reloaded in rounds); 4097 makes 65 per lane, the last lane's chunk short.
+for n, D, causal, seed, hi in ((1000, 128, True, 6, 90), (1500, 64, False, 7, 40), (4097, 64, True, 8, 24),
+                               (4097, 256, False, 9, 12)):
+    rng = np.random.default_rng(seed)
+    lq = [int(x) for x in rng.integers(0, hi, size=n)]
+    lk = lq if causal else [int(x) for x in rng.integers(0, hi, size=n)]
+    MANY_SEQS.append(W.Workload(f"many{n}-d{D}-{'c' if causal else 'f'}", lq, 4, 2, D, causal, seqlens_k=lk))
 
 
 @pytest.mark.parametrize("wl", MANY_SEQS, ids=[w.name for w in MANY_SEQS])
@@ -511,8 +519,16 @@ def test_no_writes_outside_outputs():
     ([9000, 100], 128, 600000),
     ([3, 0, 700000, 5], 64, 2000000),
     ([600000, 1, 4096], 32, None),
+    # more than 64 sequences: per-lane chunks of block counts, bisection over the levels
+    ([7] * 65, 64, None),
+    (list(np.random.default_rng(21).integers(0, 300, size=1000)), 64, None),
+    (list(np.random.default_rng(22).integers(0, 40, size=4097)), 32, None),
+    (list(np.random.default_rng(23).integers(0, 5, size=20000)), 128, None),
+    ([600000] + list(np.random.default_rng(24).integers(0, 700, size=300)), 32, None),
+    (list(np.random.default_rng(25).integers(0, 90, size=2000)), 64, 70000),
 ])
 def test_device_schedule_matches_host(lengths, bm, max_q):
+    lengths = [int(x) for x in lengths]
     cu = W.cu_from_lengths(lengths)
     host = A.attn_varlen_schedule_host(cu, bm)
     max_q = max(lengths) if max_q is None else max_q

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import OUT_MAX_ABS, bf16_half_ulp, check_out_rounded
+from parity import OUT_MAX_ABS, bf16_half_ulp, check_out, check_out_rounded
 
 
 def test_bf16_half_ulp_values():
@@ -96,3 +96,23 @@ def test_band_subsequence_gives_the_full_problems_rows(causal, window):
             r3 = slice(s - a3, s - a3 + n)
             assert (np.abs(o3[r3] - o[s:s + n]).max() > 1e-9 or np.abs(dk3[r3] - dk[s:s + n]).max() > 1e-9
                     or np.abs(dq3[r3] - dq[s:s + n]).max() > 1e-9)
+
+
+def test_check_out_allows_bf16_rounding_only_where_it_exceeds_the_bound():
+    rng = np.random.default_rng(4)
+    ref = rng.uniform(-3.5, 3.5, size=(32, 4, 8))
+    ref[1, 2, 3] = 4.0 + 2.0 ** -6 * 0.999  # rounds to 4: an error of almost 2^-6 > 1e-2
+    best = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    check_out(best, ref)  # the correctly rounded result passes
+    half = 2.0 ** -6  # half the bf16 spacing on [4, 8)
+    near = best.copy()
+    near[1, 2, 3] = ref[1, 2, 3] - (half + 0.009)  # within 1e-2 beyond the rounding where |O| >= 4
+    check_out(near, ref)
+    bad = best.copy()
+    bad[1, 2, 3] = ref[1, 2, 3] - (half + 0.012)  # beyond it
+    with pytest.raises(AssertionError):
+        check_out(bad, ref)
+    bad = best.copy()
+    bad[5, 1, 0] = ref[5, 1, 0] + 0.0105  # past 1e-2 where |O| < 4: no allowance there
+    with pytest.raises(AssertionError):
+        check_out(bad, ref)
