@@ -310,9 +310,10 @@ __device__ __forceinline__ void chunk_blocks(const int32_t* cu, int num_seqs, in
 // More than 64 sequences. Lane t owns the consecutive sequences
 // [t S, (t + 1) S), S = ceil(num_seqs / 64), and holds the block counts of the
 // first kDecodeChunk of them in registers (the rest are reloaded in rounds of
-// that size for each count). C(k) is a wave sum of the lanes' partial counts,
-// the level of `rank` is found by bisection over k, and the sequence by a prefix
-// count of each lane's sequences at that level: O(S log(levels)) per wave,
+// that size for each pass over them). C(k) is a wave sum of the lanes' partial
+// counts, the level of `rank` is found by bisection over k (one pass per step),
+// and the sequence by a prefix count of each lane's sequences at that level (one
+// pass that also forms C(level + 1), one that picks): O(S log(levels)) per wave,
 // instead of O(num_seqs) per probe. Same ranking and contract as decode_rank_nb.
 constexpr int kDecodeChunk = 16;
 __device__ inline bool decode_rank_many(const int32_t* cu, int num_seqs, int bm, int levels, int rank, int& b_out,
@@ -324,32 +325,37 @@ __device__ inline bool decode_rank_many(const int32_t* cu, int num_seqs, int bm,
   const int first = lane * S, last = min(first + S, num_seqs);
   int held[kDecodeChunk];
   chunk_blocks(cu, num_seqs, bm, first, last, held);
-  // sum of f(nb) over this lane's sequences
-  auto lane_sum = [&](auto f) {
-    int acc = 0;
+  // f(nb, acc) over this lane's sequences
+  auto lane_pass = [&](auto f) {
 #pragma unroll
-    for (int i = 0; i < kDecodeChunk; ++i) acc += f(held[i]);
+    for (int i = 0; i < kDecodeChunk; ++i) f(held[i]);
     for (int r = 1; r < rounds; ++r) {
       int nb[kDecodeChunk];
       chunk_blocks(cu, num_seqs, bm, first + r * kDecodeChunk, last, nb);
 #pragma unroll
-      for (int i = 0; i < kDecodeChunk; ++i) acc += f(nb[i]);
+      for (int i = 0; i < kDecodeChunk; ++i) f(nb[i]);
     }
-    return acc;
   };
-  auto C = [&](int k) { return wave_sum(lane_sum([k](int nb) { return max(0, nb - k); })); };
-  // the level: the largest k < levels with C(k) > rank (C falls as k grows)
-  if (C(0) <= rank) return false;
-  int lo = 0, hi = levels;  // C(lo) > rank; hi == levels or C(hi) <= rank
+  // The level: the largest k < levels with C(k) > rank (C falls as k grows),
+  // by bisection that keeps C(hi) <= rank or hi == levels. When rank is past the
+  // last block (C(0) <= rank) it ends at k = 0 with no sequence left to pick.
+  int lo = 0, hi = levels;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (C(mid) > rank) lo = mid;
+    int acc = 0;
+    lane_pass([&](int nb) { acc += max(0, nb - mid); });
+    if (wave_sum(acc) > rank) lo = mid;
     else hi = mid;
   }
   const int kstar = lo;
+  // one pass: C(kstar + 1), and this lane's sequences with more than kstar blocks
+  int above = 0, own = 0;
+  lane_pass([&](int nb) {
+    above += max(0, nb - kstar - 1);
+    own += nb > kstar ? 1 : 0;
+  });
   // rank within level kstar, then the (j+1)-th sequence with more than kstar blocks
-  const int j = rank - C(kstar + 1);
-  const int own = lane_sum([kstar](int nb) { return nb > kstar ? 1 : 0; });
+  const int j = rank - wave_sum(above);
   const int before = wave_excl_scan(own);
   const uint64_t owner_mask = __ballot(j >= before && j < before + own);
   if (owner_mask == 0) return false;
