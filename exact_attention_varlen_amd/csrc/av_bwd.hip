@@ -968,7 +968,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
     if (e != hipSuccess) return e;
     BwdParams pk = p;
     pk.levels = ceil_div(f.max_k, T::BNK);
-    const int64_t grid = grid_for(f.total_k, f.num_seqs, T::BNK, f.Hkv, 1);
+    const int64_t grid = grid_for(f.total_k, f.num_seqs, pk.levels, T::BNK, f.Hkv, 1);
     if (grid > 0 && pk.levels > 0) {
       prof_begin("attn_bwd_dkdv", stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
@@ -986,7 +986,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
     BwdParams pq = p;
     const int bm = kQueryBlock / hw, hwl = log2_small(hw);
     pq.levels = ceil_div(f.max_q, bm);
-    const int64_t grid = grid_for(f.total_q, f.num_seqs, bm, f.Hq >> hwl, (f.Hq / f.Hkv) >> hwl);
+    const int64_t grid = grid_for(f.total_q, f.num_seqs, pq.levels, bm, f.Hq >> hwl, (f.Hq / f.Hkv) >> hwl);
     if (grid > 0 && pq.levels > 0) {
       prof_begin(name, stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, stream, pq);

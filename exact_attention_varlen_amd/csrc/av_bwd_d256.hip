@@ -661,7 +661,7 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
     if (e != hipSuccess) return e;
     BwdParams pk = p;
     pk.levels = ceil_div(f.max_k, T::BNK);
-    const int64_t grid = grid_for(f.total_k, f.num_seqs, T::BNK, f.Hkv * splits, splits);
+    const int64_t grid = grid_for(f.total_k, f.num_seqs, pk.levels, T::BNK, f.Hkv * splits, splits);
     if (grid > 0 && pk.levels > 0) {
       prof_begin("attn_bwd_dkdv", stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
@@ -690,7 +690,7 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
     BwdParams pq = p;
     const int hw = block_heads(f.Hq / f.Hkv), hwl = log2_small(hw), bm = T::BM / hw;
     pq.levels = ceil_div(f.max_q, bm);
-    const int64_t grid = grid_for(f.total_q, f.num_seqs, bm, f.Hq >> hwl, (f.Hq / f.Hkv) >> hwl);
+    const int64_t grid = grid_for(f.total_q, f.num_seqs, pq.levels, bm, f.Hq >> hwl, (f.Hq / f.Hkv) >> hwl);
     if (grid > 0 && pq.levels > 0) {
       prof_begin("attn_bwd_dq", stream);
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pq);

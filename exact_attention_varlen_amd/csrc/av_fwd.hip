@@ -20,7 +20,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   }
   FwdParams p = fwd_params(a, T::BM);
   const int r = a.Hq / a.Hkv;
-  const int64_t grid = grid_for(a.total_q, a.num_seqs, p.bm, a.Hq >> p.hw_log2, r >> p.hw_log2);
+  const int64_t grid = grid_for(a.total_q, a.num_seqs, p.levels, p.bm, a.Hq >> p.hw_log2, r >> p.hw_log2);
   if (grid == 0 || p.levels == 0) return hipSuccess;
   hipStream_t stream = (hipStream_t)a.stream;
   prof_begin("attn_fwd", stream);
@@ -45,10 +45,6 @@ hipError_t launch_fwd(const FwdArgs& a) {
     case 256: return launch_fwd_d<256>(a);
     default: return hipErrorInvalidValue;
   }
-}
-
-int64_t fwd_grid_size(int64_t total_q, int num_seqs, int Hq, int Hkv) {
-  return grid_for(total_q, num_seqs, FwdBlock<128>::BM, Hq, Hq / Hkv);
 }
 
 }  // namespace av

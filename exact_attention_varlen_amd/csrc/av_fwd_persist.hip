@@ -23,7 +23,7 @@ static hipError_t launch_persist_t(const FwdArgs& a, unsigned int* sched) {
   FwdParams p = fwd_params(a, T::BM);
   p.sched = sched;
   const int r = a.Hq / a.Hkv;
-  const int64_t n_items = grid_for(a.total_q, a.num_seqs, p.bm, a.Hq >> p.hw_log2, r >> p.hw_log2);
+  const int64_t n_items = grid_for(a.total_q, a.num_seqs, p.levels, p.bm, a.Hq >> p.hw_log2, r >> p.hw_log2);
   if (n_items == 0 || p.levels == 0) return hipSuccess;
   const int64_t slots = (int64_t)kNumCu * T::MIN_BLOCKS_PER_CU;
   const int64_t grid = n_items < slots ? n_items : slots;

@@ -92,7 +92,7 @@ static hipError_t launch_split_t(const FwdArgs& a, int splits, float* part_o, fl
   p.part_l = part_l;
   p.splits = splits;
   const int r = a.Hq / a.Hkv;
-  const int64_t grid = grid_for(a.total_q, a.num_seqs, p.bm, (a.Hq >> p.hw_log2) * splits, r >> p.hw_log2);
+  const int64_t grid = grid_for(a.total_q, a.num_seqs, p.levels, p.bm, (a.Hq >> p.hw_log2) * splits, r >> p.hw_log2);
   if (grid == 0 || p.levels == 0) return hipSuccess;
   hipStream_t stream = (hipStream_t)a.stream;
   prof_begin("attn_fwd_split", stream);

@@ -121,7 +121,6 @@ int prof_enable(int enable);
 int prof_count();
 int prof_get(int i, char* name, int cap, float* ms);
 
-int64_t fwd_grid_size(int64_t total_q, int num_seqs, int Hq, int Hkv);
 size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D);
 // Workspace of the stored-dS backward (bwd_workspace_bytes plus the dS buffer),
 // 0 when that path does not apply; and the dS buffer's row pitch (elements).

@@ -43,10 +43,16 @@ AV_HD inline int64_t xcd_logical(int64_t hw, int r) {
 }
 
 // Grid size of a kernel whose work is (query block rank) x (heads): an upper
-// bound on the number of blocks, sum_b ceil(Lq_b / bm) <= total_q / bm + num_seqs,
-// times the heads, rounded up to a multiple of 8*r.
-AV_HD inline int64_t grid_for(int64_t total_q, int num_seqs, int bm, int heads, int r) {
-  const int64_t blocks = total_q / bm + num_seqs;
+// bound on the number of blocks, sum_b ceil(Lq_b / bm), times the heads, rounded
+// up to a multiple of 8*r. Two bounds hold, the smaller is taken:
+// total_q / bm + num_seqs (a partial block per sequence at most) and
+// num_seqs * levels, levels = ceil(max_seqlen / bm) (the first is tight for a few
+// long sequences, the second for many short ones). Workgroups past the last
+// block find no work, but each still decodes its rank first.
+AV_HD inline int64_t grid_for(int64_t total_q, int num_seqs, int levels, int bm, int heads, int r) {
+  const int64_t by_tokens = total_q / bm + num_seqs;
+  const int64_t by_lengths = (int64_t)num_seqs * levels;
+  const int64_t blocks = by_tokens < by_lengths ? by_tokens : by_lengths;
   const int64_t n = blocks * heads;
   const int64_t group = (int64_t)kNumXcd * r;
   return ((n + group - 1) / group) * group;
