@@ -645,6 +645,15 @@ EDGE = [
     (W.Workload("edge-decode1-d256-f", [1, 1, 1], 8, 1, 256, False, seqlens_k=[1, 2000, 33]), 16),
     (W.Workload("edge-onekey-d128-c", [5, 1], 4, 4, 128, True, seqlens_k=[1, 1]), 2),
 ]
+# more than 64 sequences through the split-KV chunks and the persistent queues
+# (the decode's per-lane chunks): decode-like few queries against longer keys,
+# and many short causal documents
+_rng = np.random.default_rng(31)
+EDGE += [
+    (W.Workload("edge-many700-decode-d128-f", [int(x) for x in _rng.integers(1, 5, size=700)], 8, 2, 128, False,
+                seqlens_k=[int(x) for x in _rng.integers(0, 600, size=700)]), 3),
+    (W.Workload("edge-many1200-d64-c", [int(x) for x in _rng.integers(0, 70, size=1200)], 4, 2, 64, True), 5),
+]
 
 
 @pytest.mark.parametrize("wl,splits", EDGE, ids=[w.name for w, _ in EDGE])
