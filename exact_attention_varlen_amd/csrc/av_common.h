@@ -325,7 +325,7 @@ __device__ inline bool decode_rank_many(const int32_t* cu, int num_seqs, int bm,
   const int first = lane * S, last = min(first + S, num_seqs);
   int held[kDecodeChunk];
   chunk_blocks(cu, num_seqs, bm, first, last, held);
-  // f(nb, acc) over this lane's sequences
+  // f(nb) for each of this lane's sequences (nb = 0 past the end of its chunk)
   auto lane_pass = [&](auto f) {
 #pragma unroll
     for (int i = 0; i < kDecodeChunk; ++i) f(held[i]);
