@@ -860,6 +860,47 @@ def many_docs_table(total: int = 65536):
     return 0
 
 
+def few_kv_heads_table():
+    """Forward and backward of short sequences with few KV heads (MQA / narrow
+    GQA), where the head dim 64 / 128 dK / dV work splits a group's query heads
+    over several work items (one JSON line each)."""
+    import torch
+
+    import exact_attention_varlen_amd as A
+    import workloads as W
+
+    for wl in (W.Workload("4096-gqa32/8-d128-full", [4096], 32, 8, 128, False),
+               W.Workload("4096-mqa32-d128-full", [4096], 32, 1, 128, False),
+               W.Workload("4096-mqa32-d128-causal", [4096], 32, 1, 128, True),
+               W.Workload("2x2048-mqa16-d64-causal", [2048, 2048], 16, 1, 64, True),
+               W.Workload("8192-gqa64/2-d128-causal", [8192], 64, 2, 128, True)):
+        log(f"few KV heads {wl.name}")
+        d = {k: v.to("cuda:0") for k, v in W.make_inputs(wl).items()}
+        out = torch.empty_like(d["q"])
+        lse = torch.empty((wl.n_q_heads, wl.total_q), dtype=torch.float32, device="cuda:0")
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        ws = torch.empty(max(16, bwd_ws_bytes(wl)), dtype=torch.uint8, device="cuda:0")
+        mq, mk = wl.max_seqlen_q, wl.max_seqlen_k
+
+        def fwd():
+            A.attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], mq, mk, wl.softmax_scale,
+                              wl.causal, out=out, lse=lse)
+
+        def bwd():
+            A.attn_varlen_bwd(d["dout"], d["q"], d["k"], d["v"], out, lse, d["cu_seqlens_q"], d["cu_seqlens_k"], mq,
+                              mk, wl.softmax_scale, wl.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        fwd()
+        fl = wl.accounted_fwd_flop()
+        f_ms = time_graph_steady(fwd, 10, 3)
+        b_ms = time_graph_steady(bwd, 5, 3)
+        print(json.dumps({"workload": wl.name, "fwd_ms": f_ms, "fwd_tflops": fl / (f_ms * 1e-3) / 1e12,
+                          "bwd_ms": b_ms, "bwd_tflops": 2.5 * fl / (b_ms * 1e-3) / 1e12}), flush=True)
+        del d, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def kernel_times(rounds: int = 3, steps: int = 8):
     """Per-kernel times (library events, eager forward+backward steps) of one
     workload per head dim, for comparing builds of the library: one JSON line
@@ -983,6 +1024,9 @@ def main(argv=None):
     ap.add_argument("--many-docs", action="store_true",
                     help="only time forward and forward+backward of 16 to 4096 equal causal documents at 65536 "
                          "tokens (one JSON line each) and exit")
+    ap.add_argument("--few-kv-heads", action="store_true",
+                    help="only time forward and backward of short sequences with 1 or 2 KV heads (one JSON line "
+                         "each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale profiler byte counters) and exit")
     a = ap.parse_args(argv)
@@ -1010,6 +1054,9 @@ def main(argv=None):
     if a.many_docs:
         warm_gpu()
         return many_docs_table()
+    if a.few_kv_heads:
+        warm_gpu()
+        return few_kv_heads_table()
     if a.kernel_times:
         warm_gpu()
         return kernel_times()

@@ -110,7 +110,11 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
     }
   }
   if (static_scratch) {
-    if (need > av::noalloc_scratch_bytes()) return ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL;
+    // the scratch must hold the workspace without dK / dV head splits; the
+    // backward then runs with as many splits as it holds
+    if (av::bwd_min_workspace_bytes(total_q, total_k, n_q_heads, n_kv_heads, head_dim) >
+        av::noalloc_scratch_bytes())
+      return ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL;
   } else {
     if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_VARLEN_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return ATTN_VARLEN_ERR_MISALIGNED;
@@ -131,6 +135,7 @@ int bwd_checked(const void* q, const void* k, const void* v, const int32_t* cu_s
   a.delta = static_cast<float*>(workspace);
   a.ds = stored_ds ? static_cast<char*>(workspace) + need : nullptr;
   a.ds_pitch = stored_ds ? av::bwd_ds_pitch(max_seqlen_q) : 0;
+  a.ws_bytes = static_scratch ? av::noalloc_scratch_bytes() : workspace_bytes;
   return av::launch_bwd(a) == hipSuccess ? ATTN_VARLEN_OK : ATTN_VARLEN_ERR_HIP;
 }
 

@@ -59,16 +59,26 @@ __device__ __forceinline__ void rows64_f32_dma(uint32_t dst, const i32x4& rsrc, 
 inline size_t ws_pad(size_t b) { return (b + 255) / 256 * 256; }
 inline size_t ws_plane_bytes(int64_t total_q, int Hq) { return ws_pad((size_t)total_q * (size_t)Hq * sizeof(float)); }
 
-// Query-head splits of the head dim 256 dK / dV work: the smallest divisor s of
-// the group size r with (key blocks x KV heads x s) >= 2048 work items (8 per
-// compute unit, so longest-first ordering can balance causal work), else r.
+// Query-head splits of the dK / dV work (head_dim 256 and, with few work items,
+// 64 / 128). The kernels are key-stationary: a work item is a key block of one KV
+// head and sums the group's r query heads in registers. With few key blocks x KV
+// heads (short sequences, few KV heads) that leaves most compute units idle, so
+// the group's heads are split over s items, each writing fp32 partial sums that
+// bwd_dkdv_reduce_kernel adds in split order (deterministic, no atomics).
+// head_dim 256 (one workgroup per CU, long items): the smallest divisor s of r
+// with (key blocks x KV heads x s) >= 2048 work items (8 per compute unit, so
+// longest-first ordering can balance causal work), else r. head_dim 64 / 128:
+// no split while there are at least 256 items (one per compute unit); below
+// that the smallest divisor s of r giving >= 1024 items, else r.
 // Key blocks are counted as total_k / 128, a lower bound of sum_b ceil(Lk_b / 128).
 inline int dkdv_splits(int64_t total_k, int Hq, int Hkv, int D) {
-  if (D != 256 || Hkv <= 0) return 1;
+  if (Hkv <= 0) return 1;
   const int r = Hq / Hkv;
   const int64_t base = (total_k / 128 > 0 ? total_k / 128 : 1) * (int64_t)Hkv;
+  if (D != 256 && base >= 256) return 1;
+  const int64_t want = D == 256 ? 2048 : 1024;
   for (int s = 1; s <= r; ++s) {
-    if (r % s == 0 && base * s >= 2048) return s;
+    if (r % s == 0 && base * s >= want) return s;
   }
   return r > 0 ? r : 1;
 }
@@ -95,6 +105,23 @@ inline size_t ds_buffer_bytes(int64_t total_q, int64_t total_k, int max_q, int m
 
 inline size_t ws_part_bytes(int64_t total_k, int Hkv, int D, int splits) {
   return splits > 1 ? ws_pad((size_t)splits * (size_t)total_k * (size_t)Hkv * (size_t)D * sizeof(float)) : 0;
+}
+
+// Backward workspace: Delta and lse2 planes, then the partial dK / dV sums.
+inline size_t bwd_ws_bytes_for(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D, int splits) {
+  return 2 * ws_plane_bytes(total_q, Hq) + 2 * ws_part_bytes(total_k, Hkv, D, splits);
+}
+
+// The split count a backward runs with: dkdv_splits, lowered to the largest
+// divisor of r whose workspace fits in `limit` bytes (the allocation-free entry
+// point's fixed scratch); 1 always fits where the call was accepted.
+inline int dkdv_splits_within(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D, size_t limit) {
+  const int want = dkdv_splits(total_k, Hq, Hkv, D);
+  const int r = Hkv > 0 ? Hq / Hkv : 1;
+  for (int s = want; s > 1; --s) {
+    if (r % s == 0 && bwd_ws_bytes_for(total_q, total_k, Hq, Hkv, D, s) <= limit) return s;
+  }
+  return 1;
 }
 
 }  // namespace av

@@ -46,10 +46,15 @@ namespace av {
 
 hipError_t launch_bwd_main_d256(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv,
                                 int splits);  // av_bwd_d256.hip
+hipError_t launch_dkdv_reduce(const float* part_dk, const float* part_dv, uint16_t* dk, uint16_t* dv, int64_t n8,
+                              int splits, float scale, hipStream_t stream);  // av_bwd_d256.hip
 
 size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D) {
-  const int splits = dkdv_splits(total_k, Hq, Hkv, D);
-  return 2 * ws_plane_bytes(total_q, Hq) + 2 * ws_part_bytes(total_k, Hkv, D, splits);
+  return bwd_ws_bytes_for(total_q, total_k, Hq, Hkv, D, dkdv_splits(total_k, Hq, Hkv, D));
+}
+
+size_t bwd_min_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D) {
+  return bwd_ws_bytes_for(total_q, total_k, Hq, Hkv, D, 1);
 }
 
 size_t bwd_ds_workspace_bytes(int64_t total_q, int64_t total_k, int max_q, int max_k, int Hq, int Hkv, int D) {
@@ -361,18 +366,33 @@ __device__ __forceinline__ void dkdv_step(const lds_char* Qs, const lds_char* dO
 // LEFT: the band has a left bound (window_left >= 0). Without one, every row
 // past a key's first visible row sees it, and masked steps test that bound only.
 // STORE: also write dS to the stored-dS buffer p.ds (bwd_dq_ds_kernel reads it).
-template <int D, bool BAND, bool LEFT, bool STORE>
+// SPLIT: the item covers r / p.splits query heads of the group (split `split`)
+// and writes fp32 partial dK / dV sums (p.part_dk / part_dv, plane `split`), which
+// bwd_dkdv_reduce_kernel adds in split order.
+template <int D, bool BAND, bool LEFT, bool STORE, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+  static_assert(!(SPLIT && STORE), "the stored-dS path runs without splits");
   using T = DkdvCfg<D>;
   extern __shared__ __align__(16) uint16_t smem[];
   lds_char* lds = (lds_char*)smem;
 
-  // work item: (sequence, key block) ranked by descending work, x KV heads.
-  // The rank's level counts key blocks from the end of the sequence, so the
-  // blocks seen by the most query rows come first.
-  const int64_t L = xcd_logical(blockIdx.x, 1);
-  const int rank = (int)(L / p.Hkv);
-  const int g = (int)(L % p.Hkv);
+  // work item: (sequence, key block) ranked by descending work, x KV heads (x
+  // query-head splits, innermost, as in the head_dim 256 kernel). The rank's
+  // level counts key blocks from the end of the sequence, so the blocks seen by
+  // the most query rows come first.
+  int rank, g, split = 0;
+  if constexpr (SPLIT) {
+    const int64_t L = blockIdx.x;
+    const int64_t per = (int64_t)p.Hkv * p.splits;
+    rank = (int)(L / per);
+    const int rem = (int)(L % per);
+    g = rem / p.splits;
+    split = rem % p.splits;
+  } else {
+    const int64_t L = xcd_logical(blockIdx.x, 1);
+    rank = (int)(L / p.Hkv);
+    g = (int)(L % p.Hkv);
+  }
   Item item;
   if (!decode_item<true>(p.cu_q, p.cu_k, p.num_seqs, T::BNK, p.levels, rank, item)) return;
   const int lvl = item.m, cq = item.cq, Lq = item.Lq, ck = item.ck, Lk = item.Lk;
@@ -386,6 +406,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int kj = n0 + wave * 32 + col;  // this lane's key (sequence-relative)
   const bool kvalid = kj < Lk;
   const int r = p.Hq / p.Hkv;
+  const int nh = SPLIT ? r / p.splits : r;             // query heads of this item
+  const int h0 = SPLIT ? g * r + split * nh : g * r;   // the first of them
 
   // query steps [sfirst, sfirst + nsteps) whose rows see a key of this block,
   // and among them the unmasked ones [s_full_lo, s_full_hi): every row sees
@@ -398,12 +420,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     s_full_lo = ts.full_lo - sfirst;
     s_full_hi = ts.full_hi - sfirst;
   }
-  const int total = (nsteps > 0) ? nsteps * r : 0;
+  const int total = (nsteps > 0) ? nsteps * nh : 0;
 
   const uint32_t pitch = (uint32_t)p.Hq * D * 2;
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int it, uint32_t stage) {
-    const int h = g * r + it / nsteps;
+    const int h = h0 + it / nsteps;
     const int m0 = (sfirst + it % nsteps) * T::BMQ;
     const int64_t qoff = ((int64_t)cq * p.Hq + h) * D;
     const i32x4 rq = head_rows_rsrc<D>(p.q + qoff, Lq, pitch);
@@ -473,7 +495,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     // the copies of stage it + 1, one or two per unit of the step's first phase
     static_assert(T::DMA_PER_WAVE <= D / 8 && T::F32_DMAS <= D / 8, "copies fit the units of X(0)");
     const bool next = it + 1 < total;
-    const int h1 = g * r + (it + 1) / nsteps;
+    const int h1 = h0 + (it + 1) / nsteps;
     const int m1 = (sfirst + (it + 1) % nsteps) * T::BMQ;
     const int64_t qoff1 = ((int64_t)cq * p.Hq + h1) * D;
     const int64_t roff1 = (int64_t)h1 * p.total_q + cq;
@@ -496,7 +518,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
                                                       STORE ? ds_key + hg * ds_plane + m0 : nullptr, kvalid, x0);
     ++it;
   };
-  for (int hg = 0; hg < (total > 0 ? r : 0); ++hg) {
+  for (int hg = 0; hg < (total > 0 ? nh : 0); ++hg) {
     for (int st = 0; st < s_full_lo; ++st) step(hg, st, std::true_type());
     for (int st = s_full_lo; st < s_full_hi; ++st) step(hg, st, std::false_type());
     for (int st = s_full_hi; st < nsteps; ++st) step(hg, st, std::true_type());
@@ -504,10 +526,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   if (kvalid) {
     const int64_t base = ((int64_t)(ck + kj) * p.Hkv + g) * D + 4 * half;
+    if constexpr (SPLIT) {
+      const int64_t part = (int64_t)split * p.total_k * p.Hkv * D + base;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      store_acc_row(p.dk + base + db * 32, dk[db], p.scale);
-      store_acc_row(p.dv + base + db * 32, dv[db], 1.f);
+      for (int db = 0; db < D / 32; ++db) {
+        store_acc_row_f32(p.part_dk + part + db * 32, dk[db]);
+        store_acc_row_f32(p.part_dv + part + db * 32, dv[db]);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        store_acc_row(p.dk + base + db * 32, dk[db], p.scale);
+        store_acc_row(p.dv + base + db * 32, dv[db], 1.f);
+      }
     }
   }
 }
@@ -926,7 +957,7 @@ static hipError_t launch_prep(const BwdArgs& a, float* delta, float* lse2) {
 }
 
 template <int D, bool BAND, bool LEFT>
-static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
+static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
   const FwdArgs& f = a.f;
   hipStream_t stream = (hipStream_t)f.stream;
   BwdParams p;
@@ -977,6 +1008,28 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
     }
     return e;
   };
+  // the group's query heads split over `splits` items per key block, fp32
+  // partial sums, then their ordered reduce (recomputing-dQ path only)
+  auto run_dkdv_split = [&]() -> hipError_t {
+    using T = DkdvCfg<D>;
+    auto kern = bwd_dkdv_kernel<D, BAND, LEFT, false, true>;
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_limit_once(kern, T::LDS_BYTES, lds_set);
+    if (e != hipSuccess) return e;
+    BwdParams pk = p;
+    pk.levels = ceil_div(f.max_k, T::BNK);
+    pk.part_dk = part_dk;
+    pk.part_dv = part_dv;
+    pk.splits = splits;
+    const int64_t grid = grid_for(f.total_k, f.num_seqs, pk.levels, T::BNK, f.Hkv * splits, splits);
+    if (grid == 0 || pk.levels == 0) return hipSuccess;
+    prof_begin("attn_bwd_dkdv", stream);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T::NT), T::LDS_BYTES, stream, pk);
+    prof_end(stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_dkdv_reduce(part_dk, part_dv, p.dk, p.dv, f.total_k * f.Hkv * D / 8, splits, f.scale, stream);
+  };
   // hw: query heads per workgroup (the recomputing dQ kernel groups a KV
   // group's heads as the forward does; the stored-dS one takes one head)
   auto run_dq = [&](auto kern, size_t lds_bytes, std::atomic<uint64_t>& lds_set, const char* name,
@@ -1014,7 +1067,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, float* lse2) {
         run_dq(bwd_dq_kernel<D, BAND, LEFT>, DqCfg<D>::LDS_BYTES, lds_set, "attn_bwd_dq", block_heads(f.Hq / f.Hkv));
     if (e != hipSuccess) return e;
   }
-  if (f.total_k > 0) return run_dkdv(std::false_type());
+  if (f.total_k > 0) return splits > 1 ? run_dkdv_split() : run_dkdv(std::false_type());
   return hipSuccess;
 }
 
@@ -1026,16 +1079,21 @@ static hipError_t launch_bwd_d(const BwdArgs& a) {
     const hipError_t e = launch_prep<D>(a, a.delta, lse2);
     if (e != hipSuccess) return e;
   }
+  // dK / dV query-head splits (the stored-dS path runs without them), as many as
+  // the workspace holds
+  const int splits =
+      a.ds ? 1 : dkdv_splits_within(a.f.total_q, a.f.total_k, a.f.Hq, a.f.Hkv, D, a.ws_bytes);
+  char* part = reinterpret_cast<char*>(a.delta) + 2 * ws_plane_bytes(a.f.total_q, a.f.Hq);
+  const size_t pb = ws_part_bytes(a.f.total_k, a.f.Hkv, D, splits);
+  float* part_dk = splits > 1 ? reinterpret_cast<float*>(part) : nullptr;
+  float* part_dv = splits > 1 ? reinterpret_cast<float*>(part + pb) : nullptr;
   if constexpr (D == 256) {
-    const int splits = dkdv_splits(a.f.total_k, a.f.Hq, a.f.Hkv, D);
-    char* part = reinterpret_cast<char*>(a.delta) + 2 * ws_plane_bytes(a.f.total_q, a.f.Hq);
-    const size_t pb = ws_part_bytes(a.f.total_k, a.f.Hkv, D, splits);
-    return launch_bwd_main_d256(a, lse2, splits > 1 ? reinterpret_cast<float*>(part) : nullptr,
-                                splits > 1 ? reinterpret_cast<float*>(part + pb) : nullptr, splits);
+    return launch_bwd_main_d256(a, lse2, part_dk, part_dv, splits);
   } else {
     const Band bd = band_of(a.f);
-    if (!bd.band) return launch_bwd_t<D, false, false>(a, lse2);
-    return bd.wl >= 0 ? launch_bwd_t<D, true, true>(a, lse2) : launch_bwd_t<D, true, false>(a, lse2);
+    if (!bd.band) return launch_bwd_t<D, false, false>(a, lse2, part_dk, part_dv, splits);
+    return bd.wl >= 0 ? launch_bwd_t<D, true, true>(a, lse2, part_dk, part_dv, splits)
+                      : launch_bwd_t<D, true, false>(a, lse2, part_dk, part_dv, splits);
   }
 }
 

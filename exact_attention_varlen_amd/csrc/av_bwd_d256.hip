@@ -43,6 +43,9 @@
 
 namespace av {
 
+hipError_t launch_dkdv_reduce(const float* part_dk, const float* part_dv, uint16_t* dk, uint16_t* dv, int64_t n8,
+                              int splits, float scale, hipStream_t stream);
+
 namespace {
 
 constexpr int kD = 256;
@@ -424,6 +427,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __res
   }
 }
 
+
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
@@ -670,14 +674,7 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
       if (e != hipSuccess) return e;
     }
     if (splits > 1) {
-      const int64_t n8 = f.total_k * f.Hkv * kD / 8;
-      int64_t rgrid = (n8 + 255) / 256;
-      if (rgrid > 8192) rgrid = 8192;
-      prof_begin("attn_bwd_dkdv_reduce", stream);
-      hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)rgrid), dim3(256), 0, stream, part_dk, part_dv,
-                         p.dk, p.dv, n8, splits, f.scale);
-      prof_end(stream);
-      e = hipGetLastError();
+      e = launch_dkdv_reduce(part_dk, part_dv, p.dk, p.dv, f.total_k * f.Hkv * kD / 8, splits, f.scale, stream);
       if (e != hipSuccess) return e;
     }
   }
@@ -703,6 +700,19 @@ hipError_t launch_main_t(const BwdArgs& a, float* lse2, float* part_dk, float* p
 }
 
 }  // namespace
+
+// The ordered reduce of split partial sums, for any head dim (n8: elements / 8).
+hipError_t launch_dkdv_reduce(const float* part_dk, const float* part_dv, uint16_t* dk, uint16_t* dv, int64_t n8,
+                              int splits, float scale, hipStream_t stream) {
+  if (n8 <= 0) return hipSuccess;
+  int64_t rgrid = (n8 + 255) / 256;
+  if (rgrid > 8192) rgrid = 8192;
+  prof_begin("attn_bwd_dkdv_reduce", stream);
+  hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)rgrid), dim3(256), 0, stream, part_dk, part_dv, dk, dv,
+                     n8, splits, scale);
+  prof_end(stream);
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_main_d256(const BwdArgs& a, float* lse2, float* part_dk, float* part_dv, int splits) {
   const Band bd = band_of(a.f);

@@ -75,6 +75,7 @@ struct BwdArgs {
   float* delta;  // workspace (Delta, lse2, partial dK / dV): see av_bwd.h
   void* ds;      // stored-dS buffer in the workspace (head dims 64 / 128), or null: dQ recomputes dS
   int ds_pitch;  // its elements per key row
+  size_t ws_bytes;  // bytes the workspace holds (bounds the dK / dV split count)
 };
 
 // Packing-array check (av_validate.hip): bits of the result word.
@@ -122,6 +123,8 @@ int prof_count();
 int prof_get(int i, char* name, int cap, float* ms);
 
 size_t bwd_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D);
+// the workspace without dK / dV head splits (the least a backward can run with)
+size_t bwd_min_workspace_bytes(int64_t total_q, int64_t total_k, int Hq, int Hkv, int D);
 // Workspace of the stored-dS backward (bwd_workspace_bytes plus the dS buffer),
 // 0 when that path does not apply; and the dS buffer's row pitch (elements).
 size_t bwd_ds_workspace_bytes(int64_t total_q, int64_t total_k, int max_q, int max_k, int Hq, int Hkv, int D);

@@ -86,7 +86,7 @@ enum {
   ATTN_VARLEN_ERR_BAD_FLAG = -8,          /* causal not 0 or 1 */
   ATTN_VARLEN_ERR_HIP = -9,               /* the HIP runtime reported an error at launch */
   ATTN_VARLEN_ERR_BAD_SPLITS = -10,       /* num_splits outside [1, ATTN_VARLEN_MAX_SPLITS] */
-  ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL = -11 /* attn_varlen_bwd_noalloc: the problem's workspace exceeds
+  ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL = -11 /* attn_varlen_bwd_noalloc: the problem's row terms exceed
                                              ATTN_VARLEN_NOALLOC_SCRATCH_BYTES */
 };
 
@@ -332,17 +332,20 @@ int attn_varlen_bwd_stored_ds(const void* q, const void* k, const void* v,
  * Allocation-free backward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc). The same computation, arguments and results as attn_varlen_bwd
- * (bit-identical: the same kernels), without the workspace arguments: the
+ * (the same kernels; bit-identical whenever the scratch holds the workspace
+ * attn_varlen_bwd_workspace_size gives), without the workspace arguments: the
  * workspace lives in a device array inside the library,
  * ATTN_VARLEN_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which each GPU the
  * library runs on holds until the process ends. The call allocates nothing and
  * frees nothing; the caller still passes every input and output.
- *   Limit: problems whose workspace (attn_varlen_bwd_workspace_size) exceeds
- *   the scratch are rejected with ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL before any
- *   HIP call. The row terms take 8 bytes per (query row, query head), so up to
- *   4M query row-heads (e.g. 32 heads x 128K tokens) fit at head_dim 64 / 128;
- *   at head_dim 256 the partial dK / dV sums of problems with few key blocks per
- *   KV head also count.
+ *   Limit: the row terms take 8 bytes per (query row, query head); problems
+ *   whose row terms exceed the scratch (more than 4M query row-heads, e.g. 32
+ *   heads x 128K tokens) are rejected with ATTN_VARLEN_ERR_SCRATCH_TOO_SMALL
+ *   before any HIP call. With few key blocks per KV head the dK / dV work splits
+ *   a group's query heads and keeps fp32 partial sums in the workspace; here it
+ *   uses as many splits as the scratch holds, and where that is fewer than
+ *   attn_varlen_bwd uses, dK and dV differ from its by fp32 summation order
+ *   (the result stays deterministic).
  *   Sharing: every call on one GPU uses that GPU's one scratch array, which keeps
  *   the last call's contents (nothing in it needs to start at zero). Calls on
  *   one GPU must therefore not overlap: calls on different streams, or from

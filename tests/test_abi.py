@@ -155,16 +155,23 @@ def _pad(b):
 
 
 @pytest.mark.parametrize("total, hq, hkv, d, splits", [
-    (1000, 32, 8, 128, 1),        # head dims 64 / 128 never split the dK / dV work
     (32768, 8, 1, 256, 8),        # 256 key blocks x 1 KV head: 8 splits reach 2048 items
     (131072, 8, 1, 256, 2),       # 1024 key blocks: 2 splits
     (16384, 16, 2, 256, 8),       # 128 blocks x 2 heads = 256 items: 8 of the 8 heads
     (300000, 8, 1, 256, 1),       # >= 2048 key blocks: no split
     (1000, 6, 1, 256, 6),         # too few items for any divisor: all 6 heads
+    # head dims 64 / 128: no split from 256 items (key blocks x KV heads) on,
+    # below that the smallest divisor reaching 1024 items
+    (16384, 32, 8, 128, 1),       # 128 blocks x 8 heads = 1024 items
+    (4096, 32, 8, 128, 1),        # 32 x 8 = 256 items
+    (4096, 32, 1, 128, 32),       # 32 items: 32 splits reach 1024
+    (8192, 16, 2, 64, 8),         # 64 x 2 = 128 items: 8 splits
+    (1000, 32, 8, 128, 4),        # 7 x 8 = 56 items, no divisor of 4 reaches 1024: all 4
+    (65536, 16, 16, 64, 1),       # MHA: nothing to split
 ])
 def test_bwd_workspace_size_splits(total, hq, hkv, d, splits):
-    """Two fp32 row planes [Hq][total_q], plus (head dim 256) two fp32 partial
-    dK / dV blocks of [splits][total_k][Hkv][D] when the split count exceeds 1."""
+    """Two fp32 row planes [Hq][total_q], plus two fp32 partial dK / dV blocks of
+    [splits][total_k][Hkv][D] when the split count exceeds 1."""
     planes = 2 * _pad(total * hq * 4)
     parts = 2 * _pad(splits * total * hkv * d * 4) if splits > 1 else 0
     assert A.attn_varlen_bwd_workspace_size(1, total, total, hq, hkv, d) == planes + parts
@@ -374,13 +381,16 @@ def test_noalloc_scratch_constant_matches_header():
 @pytest.mark.parametrize("Hq,total,D,ok", [
     (32, 131072, 128, True),     # row terms 2 x 32 x 131072 x 4 B = 32 MiB: fits exactly
     (32, 131073, 128, False),    # one row more does not
-    (8, 32768, 256, False),      # head_dim 256 with few key blocks: partial dK / dV sums too
+    (8, 32768, 256, True),       # head_dim 256, few key blocks: its 8-split partial sums (512 MiB) do
+                                 # not fit, so the allocation-free call runs with fewer splits
+    (16, 262145, 64, False),     # head_dim 64: row terms 2 x 16 x 262145 x 4 B, beyond the scratch
 ])
 def test_noalloc_rejects_problems_beyond_the_scratch(Hq, total, D, ok):
-    """The allocation-free backward checks its workspace need against the static
-    scratch before any HIP call (no GPU needed to see the rejection)."""
+    """The allocation-free backward checks the workspace it needs without dK / dV
+    head splits (the row terms) against the static scratch before any HIP call
+    (no GPU needed to see the rejection); with splits it uses as many as fit."""
     l = _lib.lib()
-    need = A.attn_varlen_bwd_workspace_size(1, total, total, Hq, 1 if D == 256 else 8, D)
+    need = 2 * _pad(total * Hq * 4)  # Delta and lse2 planes
     assert (need <= A.NOALLOC_SCRATCH_BYTES) == ok
     if ok:
         return  # a fitting problem would launch kernels

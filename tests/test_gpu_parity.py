@@ -99,6 +99,34 @@ def test_parity_many_sequences(wl):
     full_parity(wl)
 
 
+# Few KV heads and few key blocks: the head dim 64 / 128 dK / dV work splits a
+# group's query heads over several items (fp32 partial sums, ordered reduce).
+SPLIT_DKDV = [
+    (W.Workload("mqa16-d128-c", [1500, 700], 16, 1, 128, True), 16),
+    (W.Workload("mqa8-d64-f-band", [900, 600], 8, 1, 64, False, window=(100, 50)), 8),
+    (W.Workload("gqa32/2-d128-f", [2048], 32, 2, 128, False), 16),
+    (W.Workload("gqa8/2-d64-c-ragged", [300, 0, 77, 513], 8, 2, 64, True, seqlens_k=[300, 5, 77, 700]), 4),
+]
+
+
+@pytest.mark.parametrize("wl,splits", SPLIT_DKDV, ids=[w.name for w, _ in SPLIT_DKDV])
+def test_parity_split_dkdv(wl, splits):
+    need = A.attn_varlen_bwd_workspace_size(len(wl.seqlens_q), wl.total_q, wl.total_k, wl.n_q_heads,
+                                            wl.n_kv_heads, wl.head_dim)
+    planes = 2 * (-(-wl.total_q * wl.n_q_heads * 4 // 256) * 256)
+    part = -(-splits * wl.total_k * wl.n_kv_heads * wl.head_dim * 4 // 256) * 256
+    assert need == planes + 2 * part  # the split count this case is for
+    full_parity(wl)
+    d = to_dev(W.make_inputs(wl))
+    out, lse = gpu_fwd(wl, d)
+    announce(f"split dK/dV determinism {wl.name}")
+    a = gpu_bwd(wl, d, out, lse)
+    b = gpu_bwd(wl, d, out, lse)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # local (sliding-window) attention: band (left, right) around the bottom-right
 # diagonal; causal fixes right = 0. Windows narrower than a tile, wider than a
 # sequence, zero-width, one-sided, and bands that leave rows without a key.
@@ -393,8 +421,9 @@ def test_stored_ds_matches_recompute(D):
     one only adds the dS stores): bit-identical. dK and dQ depend on the row
     term Delta, which the two paths sum in different orders (the row-term
     kernel against the recomputing dQ kernel), so they agree to rounding; each
-    is checked against the oracle elsewhere."""
-    wl = W.Workload("paths", [700, 33, 1200, 0, 257], 8, 2, D, True)
+    is checked against the oracle elsewhere. MHA, so that the recomputing path
+    does not split the query heads of a group (the stored-dS path never does)."""
+    wl = W.Workload("paths", [700, 33, 1200, 0, 257], 8, 8, D, True)
     d = to_dev(W.make_inputs(wl))
     announce(f"stored vs recomputed dS, D={D}")
     out, lse = gpu_fwd(wl, d)
